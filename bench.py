@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the EAGLE tree-verification step on one MI355X.
+
+One step = eagle_tree_build + eagle_tree_verify + eagle_accept_commit over one batch of
+synthetic trees (the whole verification hot path), on the seeded random-init workload
+of the chosen configuration (default: the Llama-3-8B-shaped layer, 60-node static
+tree, 2048-token prefix, batch 1).  Prints one JSON line:
+  value        = tree-verify nodes/s (nodes verified per second of step time)
+  accepted_tok_s = accepted tokens (L + 1 per sequence) per second, measured
+  roofline     = the dominant kernel (LM head + fused argmax): algorithmic bytes per
+                 launch / its mean launch time from HIP events recorded in the timed
+                 region, against 8 TB/s
+  cpu_baseline = the fp64 CPU oracle on one full step of the same workload.
+Inputs are resident in HBM before timing starts; the KV cache grows by the committed
+tokens as a real decode loop does.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-nodes", type=int, default=0, help="0: one full step")
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="also run a 1 GiB torch copy so counter runs can scale FETCH/WRITE_SIZE")
+    ap.add_argument("--no-timer", action="store_true", help="time without per-kernel events")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def lm_head_bytes(dims, M):
+    # weights once, the fp32 feature rows once, one packed key per row out
+    es = 2 if dims.dtype == "bf16" else 4
+    return dims.vocab * dims.hidden * es + M * dims.hidden * 4 + M * 8
+
+
+def step_roofline_bytes_flops(dims, wl):
+    """Algorithmic bytes and flops of one verification step (every weight once, KV prefix once,
+    tree K/V written once and read once, activations in and out once)."""
+    es = 2 if dims.dtype == "bf16" else 4
+    H, Hq, Hkv, D, F, V = dims.hidden, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.ffn, dims.vocab
+    M = wl.n_nodes
+    w = (Hq + 2 * Hkv) * D * H + H * Hq * D + 3 * F * H + V * H
+    kv = sum(int(p) for p in wl.prefix_len) * Hkv * D * 2 * es
+    act = M * H * es * 2 + M * (Hq + 2 * Hkv) * D * es * 2 + M * H * 4 * 2
+    byts = w * es + kv + act
+    flops = 2 * M * w
+    for b, par in enumerate(wl.parents):
+        d = np.zeros(len(par), dtype=np.int64)
+        for i in range(1, len(par)):
+            d[i] = d[par[i]] + 1
+        flops += int(np.sum(4 * Hq * D * (int(wl.prefix_len[b]) + d + 1)))
+    return byts, flops
+
+
+def cpu_baseline(wl, sample_nodes):
+    """The fp64 oracle (as it is) on one step of the workload, on this host's cores."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    parents = wl.parents
+    x = wl.x
+    tokens = wl.tokens
+    if sample_nodes:
+        parents = [parents[0][:sample_nodes]]
+        x = x[:sample_nodes]
+        tokens = tokens[:sample_nodes]
+    n = sum(len(p) for p in parents)
+    t0 = time.perf_counter()
+    out = oracle.verify_forward(wl.dims, wl.weights, x, parents, wl.prefix_len[:len(parents)], wl.k_cache,
+                                wl.v_cache, want_logits=False)
+    res = oracle.accept_batch(parents, tokens, out["argmax"], out["encs"])
+    kc = wl.k_cache.copy()
+    vc = wl.v_cache.copy()
+    off = 0
+    for b, (L, path, *_rest) in enumerate(res):
+        oracle.commit_sequence(kc[b], vc[b], out["k_tree"][off:off + len(parents[b])],
+                               out["v_tree"][off:off + len(parents[b])], path, int(wl.prefix_len[b]))
+        off += len(parents[b])
+    dt = time.perf_counter() - t0
+    acc = sum(r[0] + 1 for r in res)
+    return dict(value=n / dt, unit="nodes/s", cores=threads, kind="oracle",
+                sample=f"one full verification step ({n} nodes: tree encode, fp64 layer forward, LM head argmax, "
+                       f"accept, commit) of the same workload",
+                seconds=dt, accepted_tok_s=acc / dt)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the verification step runs on one MI355X; "
+              f"no cross-GPU path is built); got --gpus {args.gpus}", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import tree_attention_verification_06_amd as E
+    from tree_attention_verification_06_amd.runner import TreeVerifier
+    from workloads import make_workload, trees as T
+    from workloads.device import upload
+
+    E.lib()  # fail loudly if the HIP library is not built
+    cfg = args.config
+    extra = args.warmup + args.steps + 8
+    t0 = time.perf_counter()
+    wl = make_workload(cfg, seed=args.seed, cache_slack=extra * 10)
+    dims = wl.dims
+    log(f"workload {wl.name}: {wl.n_nodes} nodes, batch {wl.batch}, generated in {time.perf_counter() - t0:.1f}s")
+    t = upload(wl)
+    torch.cuda.synchronize()
+    M = wl.n_nodes
+    max_nodes = max(len(p) for p in wl.parents)
+    cap = wl.cache_cap
+    v = TreeVerifier(dims, t["weights"], t["k_cache"], t["v_cache"], batch=wl.batch, max_total_nodes=M,
+                     max_nodes=max_nodes, max_prefix=cap)
+    prefix0 = t["prefix_len"].clone()
+
+    def step(timer=None):
+        v.step(t["tree_off"], t["parent"], t["tokens"], t["prefix_len"], M, x=t.get("x"), timer=timer)
+
+    # warmup
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t["prefix_len"].copy_(prefix0)
+    torch.cuda.synchronize()
+
+    timer = None if args.no_timer else E.Timer(capacity=16 * (args.steps + 1))
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step(timer)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / args.steps
+    stages = timer.collect() if timer else {}
+    if timer:
+        timer.close()
+    st = int(v.status.item())
+    if st != 0:
+        raise RuntimeError(f"device status {st} ({E.status_str(st)})")
+
+    # accepted tokens per step: the same steps again, reading accept_len after each (untimed)
+    t["prefix_len"].copy_(prefix0)
+    accepted = []
+    for _ in range(min(args.steps, 10)):
+        step()
+        accepted.append(int((v.accept_len + 1).sum().item()))
+    acc_per_step = float(np.mean(accepted))
+
+    # planted variant: tokens along one depth-3 root path set to the target's greedy choice
+    # (node inputs are given hidden states, so tokens do not change the target's argmax)
+    g = v.argmax.cpu().numpy()
+    tokens = wl.tokens.copy()
+    for b, par in enumerate(wl.parents):
+        o = int(wl.tree_off[b])
+        d = T.depths(par)
+        cands = [i for i in range(len(par)) if d[i] == 3] or [max(range(len(par)), key=lambda i: d[i])]
+        j = cands[0]
+        path = []
+        while j != -1:
+            path.append(j)
+            j = par[j]
+        for node in path[::-1][1:]:
+            tokens[o + node] = g[o + par[node]]
+    t_tokens = torch.from_numpy(tokens).cuda()
+    t["prefix_len"].copy_(prefix0)
+    v.step(t["tree_off"], t["parent"], t_tokens, t["prefix_len"], M, x=t.get("x"))
+    planted = int((v.accept_len + 1).sum().item())
+
+    nodes_per_s = M / (ms_per_step * 1e-3)
+    byts, flops = step_roofline_bytes_flops(dims, wl)
+    t_roof_ms = max(byts / (HBM_PEAK_GBS * 1e9), 0) * 1e3  # step is HBM-bound at these shapes
+    lm_ms, lm_n = stages.get("lm_head", (0.0, 0))
+    roof = None
+    if lm_n:
+        lm_avg = lm_ms / lm_n
+        ach = lm_head_bytes(dims, M) / (lm_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gemm_bf16_kernel (LM head + fused row argmax)" if dims.dtype == "bf16" else
+                "gemm_f32_kernel (LM head + fused row argmax)",
+                "kernel_ms": round(lm_avg, 4), "bytes_per_launch": lm_head_bytes(dims, M)}
+
+    out = {
+        "metric": "tree-verify nodes/sec + accepted tok/s at 1 GPU; % of HBM/MFMA roofline",
+        "value": round(nodes_per_s, 1),
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dims.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded random-init weights N(0,0.02), KV prefix and node states N(0,1), uniform tokens",
+        "config": {"workload": wl.name, "batch": wl.batch, "tree_nodes": M, "max_tree_nodes": max_nodes,
+                   "prefix": int(wl.prefix_len.max()), "hidden": dims.hidden, "q_heads": dims.n_q_heads,
+                   "kv_heads": dims.n_kv_heads, "head_dim": dims.head_dim, "ffn": dims.ffn, "vocab": dims.vocab,
+                   "step": "tree_build + tree_verify + accept_commit"},
+        "accepted_tok_s": round(acc_per_step / (ms_per_step * 1e-3), 1),
+        "accepted_per_step": acc_per_step,
+        "accepted_tok_s_planted_depth3": round(planted / (ms_per_step * 1e-3), 1),
+        "step_roofline": {"bound": "hbm", "algorithmic_bytes": byts, "algorithmic_flops": flops,
+                          "t_roof_ms": round(t_roof_ms, 5), "frac": round(t_roof_ms / ms_per_step, 4)},
+        "roofline": roof,
+        "stage_ms_per_step": {k: round(ms / max(args.steps, 1), 5) for k, (ms, n) in stages.items()},
+    }
+    if args.pmc_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(2):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        out["pmc_calibration_copy_bytes"] = 1 << 30
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host ...")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_nodes)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

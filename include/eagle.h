@@ -1,0 +1,258 @@
+/*
+ * eagle.h - C ABI of an MI355X (gfx950) library for the hot path of EAGLE
+ * feature-level speculative decoding: the tree-verification step and the
+ * draft head's tree expansion.
+ *
+ * Method sources (web pages; cited by page title and section):
+ *  - "Speculative decoding with EAGLE" (aiunderstanding.org), Deep dive and
+ *    Technical insight: a cheap drafter proposes candidate tokens; the target
+ *    checks all of them in a single parallel pass and keeps the longest
+ *    correct prefix; accepted tokens must equal the target's own (argmax)
+ *    choice, so the output equals what the target produces alone; the drafter
+ *    predicts hidden features, is fed the true embedding of the previous
+ *    token, and reuses the target's LM head.
+ *  - "LLM parallel decoding EAGLE" (jisaku.com glossary), How EAGLE works:
+ *    one-layer decoder draft head over the final hidden features; several
+ *    candidate tokens per predicted feature expanded into a tree; tree
+ *    attention verifies every node in one forward pass and the longest valid
+ *    path is accepted.  EAGLE vs EAGLE-2 table: a fixed 60-node topology
+ *    (EAGLE-1) or confidence-adaptive trees of 40..120 nodes (EAGLE-2).
+ *    FAQ Q3: pruning at a confidence threshold of 0.3.
+ *
+ * Conventions shared by every call
+ *  - All pointers are DEVICE pointers unless a parameter says "host".  All
+ *    device buffers are allocated and freed by the caller; the library never
+ *    allocates device memory and keeps no pointer after a call returns.
+ *  - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *    default stream) and never synchronises.  Buffers must stay valid until
+ *    the stream has executed the work.
+ *  - Weights are row-major [out][in] (each output row contiguous over the
+ *    input dimension).  bf16 tensors are IEEE bfloat16; f32 tensors are IEEE
+ *    binary32.  The element type of weights, activations given as `void*`,
+ *    KV caches and tree K/V is `eagle_dims.dtype`.
+ *  - Trees of a batch are concatenated: tree b owns nodes
+ *    tree_off[b] .. tree_off[b+1]-1 of every per-node array.  Parent indices
+ *    are local to their tree; node 0 of each tree is the root (parent -1) and
+ *    0 <= parent[i] < i for every other node.  The root is the last committed
+ *    token (the previous step's bonus token), whose K/V is not in the cache
+ *    yet, so it is verified and committed together with the accepted nodes.
+ *  - KV caches are [B][Hkv][capacity][D] with the strides given in
+ *    eagle_cache_layout (elements; d is contiguous).  Slots 0..prefix_len[b]-1
+ *    of sequence b hold its committed keys (already rotated) and values.
+ *  - Return value: EAGLE_OK or a negative eagle_status for argument errors
+ *    detectable on the host; nothing is enqueued in that case.  Errors that
+ *    depend on device data (a malformed parent array, cache overflow) are
+ *    written to `dev_status` (first error wins; the caller zeroes it) and the
+ *    affected sequence's outputs are left as documented per call.
+ *  - Workspace: a caller-owned device buffer of at least
+ *    eagle_workspace_size() bytes, 256-byte aligned, zero-filled once after
+ *    allocation (eagle_workspace_init).  Every call leaves the synchronisation
+ *    counters it uses back at zero, so the same workspace can be reused
+ *    without clearing.  Calls that share one workspace must not overlap.
+ */
+#ifndef EAGLE_H_
+#define EAGLE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EAGLE_ABI_VERSION 1
+
+typedef enum {
+  EAGLE_OK = 0,
+  EAGLE_ERR_ARG = -1,         /* null pointer, bad size, misaligned buffer */
+  EAGLE_ERR_TREE = -2,        /* malformed parent array (device-side)       */
+  EAGLE_ERR_CAPACITY = -3,    /* tree or accepted path exceeds a capacity   */
+  EAGLE_ERR_UNSUPPORTED = -4, /* dims outside what the kernels implement    */
+  EAGLE_ERR_HIP = -5,         /* a HIP launch or runtime call failed        */
+  EAGLE_ERR_WORKSPACE = -6    /* workspace too small                        */
+} eagle_status;
+
+typedef enum { EAGLE_BF16 = 0, EAGLE_F32 = 1 } eagle_dtype;
+
+/* Shape of one decoder layer and its LM head.
+ *  ffn == 0 and rms_eps == 0 select the attention-only layer:
+ *    y = x + W_o attn(x),  logits = W_lm y   (no norms, no MLP).
+ *  Otherwise the Llama-style pre-norm layer:
+ *    y = x + W_o attn(RMSNorm(x)),  h = y + W_down(SiLU(W_gate y') * W_up y'),
+ *    y' = RMSNorm(y),  logits = W_lm RMSNorm(h).
+ *  rope_theta == 0 disables the rotary embedding; otherwise q and k are rotated
+ *  in the rotate-half pairing (j, j + D/2) with angle pos * theta^(-2j/D).
+ *  Supported: bf16 with head_dim 128; f32 with head_dim 64 or 128;
+ *  n_q_heads a multiple of n_kv_heads; hidden a multiple of 64. */
+typedef struct {
+  int32_t hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+  float rope_theta, rms_eps;
+  int32_t dtype; /* eagle_dtype */
+} eagle_dims;
+
+/* Weights of one decoder layer (element type dims.dtype). */
+typedef struct {
+  const void* ln_attn; /* [H] RMSNorm gain before attention (NULL if rms_eps == 0) */
+  const void* w_qkv;   /* [(Hq + 2 Hkv) D][H]: q rows (head-major), then k rows, then v rows */
+  const void* w_o;     /* [H][Hq D] */
+  const void* ln_mlp;  /* [H] RMSNorm gain before the MLP (NULL if ffn == 0) */
+  const void* w_gate;  /* [F][H] */
+  const void* w_up;    /* [F][H] */
+  const void* w_down;  /* [H][F] */
+} eagle_layer_w;
+
+/* KV cache geometry, in elements: element (b, h, t, d) is at
+ * b*batch_stride + h*head_stride + t*token_stride + d. */
+typedef struct {
+  int64_t batch_stride, head_stride, token_stride;
+  int32_t capacity; /* slots per (b, h) */
+} eagle_cache_layout;
+
+/* Draft expansion parameters (readings of the pages' EAGLE-2 description). */
+typedef struct {
+  int32_t depth;        /* expansion levels (1..16)                                   */
+  int32_t top_k;        /* children per expanded node (1..16)                         */
+  int32_t frontier;     /* nodes expanded per level after the first (1..16)           */
+  int32_t max_nodes;    /* final tree size per sequence, root included (2..128)       */
+  float conf_threshold; /* a child is expandable iff its probability >= this, [0, 1]  */
+} eagle_draft_params;
+
+/* ---- tree encode -------------------------------------------------------
+ * Method: "LLM parallel decoding EAGLE", How EAGLE works (tree attention: a
+ * node sees the prefix and its own root path).  For every node i of tree b:
+ *   depth[i] = depth[parent[i]] + 1 (root 0);
+ *   anc[i][w] bit j set iff node 64w+j of the same tree is i or an ancestor of i;
+ *   pos[i] = prefix_len[b] + depth[i].
+ * tree_off [B+1], parent [total_nodes], prefix_len [B] are inputs;
+ * anc [total_nodes][mask_words] (uint64), depth and pos [total_nodes] outputs.
+ * Host: total_nodes = tree_off[B], max_nodes >= every tree size, both host ints.
+ * Errors: mask_words*64 < max_nodes -> EAGLE_ERR_CAPACITY (host).  A tree with
+ * parent[0] != -1 or parent[i] outside [0, i) sets *dev_status = EAGLE_ERR_TREE
+ * and its anc words are all zero (depth/pos then undefined). */
+int eagle_tree_build(int32_t batch, const int32_t* tree_off, int32_t total_nodes, int32_t max_nodes,
+                     const int32_t* parent, const int32_t* prefix_len, int32_t mask_words,
+                     uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* dev_status, void* stream);
+
+/* ---- tree verification --------------------------------------------------
+ * Method: "Speculative decoding with EAGLE", Deep dive (all drafted tokens
+ * checked in one parallel pass) and "LLM parallel decoding EAGLE", How EAGLE
+ * works (tree attention).  One decoder layer over every node of every tree:
+ *   x = x_in (or embed[tokens] when x_in is NULL), node positions pos;
+ *   attention of node i: softmax(q_i k_j / sqrt(D)) over every prefix slot of
+ *   its sequence and over the tree nodes set in anc[i] (GQA: query head h uses
+ *   KV head h / (Hq/Hkv));
+ *   h_out = layer output (the next draft feature), argmax[i] = first index of
+ *   the maximum of logits_i = W_lm RMSNorm(h_i), maxlogit[i] = that maximum.
+ *   The [total_nodes][vocab] logits are never written (unless dbg_logits).
+ * Inputs: x_in [total_nodes][H] (dtype) or NULL; embed [V][H] or NULL; tokens
+ * [total_nodes]; anc [total_nodes][mask_words]; pos [total_nodes]; prefix_len
+ * [B]; k_cache/v_cache (read only).  Host ints: total_nodes, max_nodes,
+ * max_prefix >= every prefix_len[b] (bounds the work grid).
+ * Outputs: k_tree, v_tree [total_nodes][Hkv][D] (dtype; post-rotary keys),
+ * h_out [total_nodes][H] f32, argmax [total_nodes] i32, maxlogit [total_nodes] f32.
+ * Optional outputs (NULL to skip): dbg_attn [total_nodes][Hq D] f32 attention
+ * output, dbg_logits [total_nodes][V] f32 full logits.
+ * The cache is not modified, so verification can be repeated freely.
+ * timer: optional (NULL), records per-kernel HIP events (eagle_timer_*). */
+typedef struct eagle_timer eagle_timer;
+
+int eagle_tree_verify(const eagle_dims* dims, const eagle_layer_w* layer, const void* final_ln,
+                      const void* w_lm, int32_t batch, const int32_t* tree_off, int32_t total_nodes,
+                      int32_t max_nodes, const void* x_in, const void* embed, const int32_t* tokens,
+                      const uint64_t* anc, int32_t mask_words, const int32_t* pos, const int32_t* prefix_len,
+                      int32_t max_prefix, const void* k_cache, const void* v_cache,
+                      const eagle_cache_layout* cache, void* k_tree, void* v_tree, float* h_out,
+                      int32_t* argmax, float* maxlogit, float* dbg_attn, float* dbg_logits,
+                      void* workspace, size_t ws_bytes, eagle_timer* timer, void* stream);
+
+/* ---- acceptance and KV commit -------------------------------------------
+ * Method: "Speculative decoding with EAGLE", Deep dive and FAQ (keep the
+ * longest correct prefix; accepted tokens equal the target's choice, hence
+ * lossless); "LLM parallel decoding EAGLE", How EAGLE works (the longest valid
+ * path is accepted).  Greedy rule per tree b:
+ *   match(j) = tokens[j] == argmax[parent(j)] for non-root j;
+ *   a node is consistent iff every non-root node on its root path matches;
+ *   leaf = deepest consistent node (ties: lowest index), L = depth[leaf];
+ *   path[b][0..L] = root .. leaf, out_tokens[b][0..L] = tokens of path[1..L]
+ *   followed by the bonus token argmax[leaf]; next_token[b] = argmax[leaf];
+ *   accept_len[b] = L.
+ * Commit: cache slot prefix_len[b] + d <- (k_tree, v_tree) of path[d] for
+ * d = 0..L, then prefix_len[b] += L + 1; next_feature[b] = h_nodes[leaf].
+ * The copies read k_tree/v_tree, never the cache, so there is no in-place hazard.
+ * Inputs: tree_off, parent, tokens, argmax, anc, depth, k_tree, v_tree, h_nodes
+ * [total_nodes][hidden] f32.  In/out: k_cache, v_cache, prefix_len.
+ * Outputs: accept_len [B], path and out_tokens [B][max_accept + 1] (entries
+ * past L are -1), next_token [B], next_feature [B][hidden] f32 (NULL to skip).
+ * Device errors: L > max_accept or prefix_len + L + 1 > capacity set
+ * *dev_status = EAGLE_ERR_CAPACITY; that sequence gets accept_len -1 and no
+ * commit. */
+int eagle_accept_commit(int32_t batch, const int32_t* tree_off, int32_t max_nodes, const int32_t* parent,
+                        const int32_t* tokens, const int32_t* argmax, const uint64_t* anc, int32_t mask_words,
+                        const int32_t* depth, const void* k_tree, const void* v_tree, void* k_cache,
+                        void* v_cache, const eagle_cache_layout* cache, int32_t n_kv_heads, int32_t head_dim,
+                        int32_t dtype, int32_t* prefix_len, const float* h_nodes, int32_t hidden,
+                        float* next_feature, int32_t max_accept, int32_t* accept_len, int32_t* path,
+                        int32_t* out_tokens, int32_t* next_token, int32_t* dev_status, void* stream);
+
+/* ---- draft-head tree expansion -------------------------------------------
+ * Method: "Speculative decoding with EAGLE", Technical insight (feature-level
+ * draft head fed the true previous-token embedding; reuses the target LM
+ * head); "LLM parallel decoding EAGLE", How EAGLE works (one-layer decoder head,
+ * candidates expanded into a tree), EAGLE vs EAGLE-2 table and FAQ Q3
+ * (confidence-adaptive trees, pruning threshold).  Level-synchronous, per
+ * sequence b, starting from the root (root_token[b], feature root_feature[b]):
+ *   draft row of node n = W_fc [f_parent(n) ; embed[token n]] -> the draft
+ *   decoder layer at position prefix_len[b] + depth(n), attending to the draft
+ *   KV prefix and the expanded draft nodes on n's root path -> feature f_hat(n);
+ *   log p = log_softmax(W_lm RMSNorm(f_hat(n))) over the vocabulary; the top_k
+ *   tokens (ties: lower id) become children with
+ *   cum = cum(n) + min(0, log p) (cum(root) = 0);
+ *   children with p >= conf_threshold are expandable; the next level expands
+ *   the `frontier` best expandable children by (cum desc, depth asc, generation
+ *   order asc), generation order = (level, parent rank, child rank).
+ * After `depth` levels the tree is the root plus the best max_nodes-1 generated
+ * nodes by the same key, re-indexed by (depth asc, cum desc, generation order).
+ * Inputs: root_feature [B][H] f32, root_token [B], dk_cache/dv_cache (the draft
+ * layer's own KV prefix, read only), prefix_len [B]; host int max_prefix.
+ * Outputs: tree_off [B+1]; parent, tokens [B*max_nodes] i32 and cum_logp
+ * [B*max_nodes] f32, tree b stored at tree_off[b] (trees are compacted; a tree
+ * is smaller than max_nodes only when pruning leaves fewer nodes).
+ * Supported: dtype bf16. */
+int eagle_draft_expand(const eagle_dims* dims, const eagle_draft_params* params, const void* w_fc,
+                       const eagle_layer_w* draft_layer, const void* final_ln, const void* w_lm,
+                       const void* embed, int32_t batch, const float* root_feature, const int32_t* root_token,
+                       const void* dk_cache, const void* dv_cache, const eagle_cache_layout* cache,
+                       const int32_t* prefix_len, int32_t max_prefix, int32_t* tree_off, int32_t* parent,
+                       int32_t* tokens, float* cum_logp, void* workspace, size_t ws_bytes,
+                       eagle_timer* timer, int32_t* dev_status, void* stream);
+
+/* ---- workspace -------------------------------------------------------------
+ * Bytes of workspace a call needs.  which: 0 = eagle_tree_verify, 1 =
+ * eagle_draft_expand.  params is used only for which == 1.  Returns 0 for
+ * unsupported arguments. */
+size_t eagle_workspace_size(int32_t which, const eagle_dims* dims, int32_t batch, int32_t total_nodes,
+                            int32_t max_nodes, int32_t max_prefix, const eagle_draft_params* params);
+
+/* Zero-fill a workspace (once, after allocating it); enqueued on stream. */
+int eagle_workspace_init(void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- per-kernel timing --------------------------------------------------------
+ * A timer owns HIP events; calls given a timer record an event pair around each
+ * kernel they launch, tagged by stage.  Stages: 0 tree_build, 1 qkv, 2 attention,
+ * 3 attention_merge, 4 o_proj, 5 gate_up, 6 down, 7 lm_head, 8 accept_commit,
+ * 9 draft_fc, 10 draft_topk, 11 draft_select, 12 other.  capacity = event pairs
+ * recorded before the timer must be read. */
+eagle_timer* eagle_timer_create(int32_t capacity);
+void eagle_timer_destroy(eagle_timer* t);
+/* Synchronises on the recorded events, adds elapsed ms per stage into
+ * ms[EAGLE_N_STAGES] and launch counts into count[EAGLE_N_STAGES], and resets. */
+int eagle_timer_collect(eagle_timer* t, double* ms, int32_t* count);
+#define EAGLE_N_STAGES 13
+
+const char* eagle_status_str(int status);
+int eagle_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE_H_ */

@@ -1,0 +1,109 @@
+"""The C ABI library loads, exports every function include/eagle.h declares, and rejects bad
+arguments on the host with the documented status (no GPU needed: nothing is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_attention_verification_06_amd as E
+from tree_attention_verification_06_amd import _abi as A
+from workloads.configs import LLAMA8B, TINY
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "eagle.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(eagle_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 10
+    L = ctypes.CDLL(A.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    # and the binding covers exactly those names
+    assert set(A.PROTOTYPES) == set(names)
+
+
+def test_version_and_status_strings():
+    assert E.lib().eagle_abi_version() == 1
+    assert E.status_str(0) == "ok"
+    assert "workspace" in E.status_str(A.EAGLE_ERR_WORKSPACE)
+
+
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: every case below fails argument checks first
+
+
+def _tree_build(**kw):
+    a = dict(batch=1, tree_off=FAKE, total=5, maxn=5, parent=FAKE, prefix=FAKE, mw=1, anc=FAKE, depth=FAKE,
+             pos=FAKE)
+    a.update(kw)
+    return E.lib().eagle_tree_build(a["batch"], a["tree_off"], a["total"], a["maxn"], a["parent"], a["prefix"],
+                                    a["mw"], a["anc"], a["depth"], a["pos"], None, None)
+
+
+def test_tree_build_host_errors():
+    assert _tree_build(batch=0) == A.EAGLE_ERR_ARG
+    assert _tree_build(parent=None) == A.EAGLE_ERR_ARG
+    assert _tree_build(mw=3) == A.EAGLE_ERR_UNSUPPORTED
+    assert _tree_build(maxn=65, mw=1) == A.EAGLE_ERR_CAPACITY
+
+
+def _verify(dims, ws_bytes=1 << 40, **kw):
+    d = A.dims_struct(dims)
+    lw = A.EagleLayerW(4096, 4096, 4096, 4096, 4096, 4096, 4096)
+    cl = A.EagleCacheLayout(1 << 20, 1 << 16, 128, 4096)
+    a = dict(B=1, total=60, maxn=60, mw=1, max_prefix=2048, ws=ctypes.c_void_p(1 << 20))
+    a.update(kw)
+    return E.lib().eagle_tree_verify(ctypes.byref(d), ctypes.byref(lw), FAKE, FAKE, a["B"], FAKE, a["total"],
+                                     a["maxn"], FAKE, None, None, FAKE, a["mw"], FAKE, FAKE, a["max_prefix"], FAKE,
+                                     FAKE, ctypes.byref(cl), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, a["ws"],
+                                     ws_bytes, None, None)
+
+
+def test_verify_host_errors():
+    from dataclasses import replace
+    assert _verify(LLAMA8B, ws_bytes=16) == A.EAGLE_ERR_WORKSPACE
+    assert _verify(replace(LLAMA8B, head_dim=96)) == A.EAGLE_ERR_UNSUPPORTED
+    assert _verify(replace(LLAMA8B, n_kv_heads=7)) == A.EAGLE_ERR_UNSUPPORTED
+    assert _verify(replace(LLAMA8B, hidden=4000)) == A.EAGLE_ERR_UNSUPPORTED
+    assert _verify(LLAMA8B, maxn=65, mw=1) == A.EAGLE_ERR_ARG
+    assert _verify(LLAMA8B, B=0) == A.EAGLE_ERR_ARG
+    assert _verify(LLAMA8B, ws=ctypes.c_void_p((1 << 20) + 16)) == A.EAGLE_ERR_ARG  # misaligned workspace
+    assert _verify(replace(TINY, head_dim=32)) == A.EAGLE_ERR_UNSUPPORTED
+
+
+def test_workspace_size_query():
+    assert E.eagle_workspace_size(0, LLAMA8B, 1, 60, 60, 2048) > 0
+    from dataclasses import replace
+    assert E.eagle_workspace_size(0, replace(LLAMA8B, head_dim=96), 1, 60, 60, 2048) == 0
+    assert E.eagle_workspace_size(7, LLAMA8B, 1, 60, 60, 2048) == 0
+
+
+def test_accept_host_errors():
+    cl = A.EagleCacheLayout(1 << 20, 1 << 16, 128, 4096)
+    f = E.lib().eagle_accept_commit
+
+    def call(**kw):
+        a = dict(B=1, maxn=60, mw=1, hkv=8, hd=128, dtype=0, max_accept=16, tree_off=FAKE)
+        a.update(kw)
+        return f(a["B"], a["tree_off"], a["maxn"], FAKE, FAKE, FAKE, FAKE, a["mw"], FAKE, FAKE, FAKE, FAKE, FAKE,
+                 ctypes.byref(cl), a["hkv"], a["hd"], a["dtype"], FAKE, None, 4096, None, a["max_accept"], FAKE,
+                 FAKE, FAKE, FAKE, None, None)
+    assert call(B=0) == A.EAGLE_ERR_ARG
+    assert call(tree_off=None) == A.EAGLE_ERR_ARG
+    assert call(maxn=130, mw=2) == A.EAGLE_ERR_CAPACITY
+    assert call(dtype=5) == A.EAGLE_ERR_UNSUPPORTED
+    assert call(max_accept=500) == A.EAGLE_ERR_ARG
+    assert call(hd=4) == A.EAGLE_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(A, "_lib", None)
+    monkeypatch.setattr(A, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        A.lib()

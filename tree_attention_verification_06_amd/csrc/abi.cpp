@@ -1,0 +1,491 @@
+// C entry points: argument checks, workspace layout and the launch sequence of each call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "attn.h"
+#include "common.h"
+#include "draft.h"
+#include "gemm.h"
+#include "tree.h"
+
+struct eagle_timer {
+  int cap = 0;
+  int n = 0;
+  bool open = false;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> stage;
+};
+
+namespace eagle {
+
+void timer_begin(eagle_timer* t, int stage, hipStream_t s) {
+  if (!t || t->n >= t->cap) return;
+  hipEventRecord(t->ev[2 * t->n], s);
+  t->stage[t->n] = stage;
+  t->open = true;
+}
+void timer_end(eagle_timer* t, hipStream_t s) {
+  if (!t || !t->open) return;
+  hipEventRecord(t->ev[2 * t->n + 1], s);
+  t->n++;
+  t->open = false;
+}
+
+namespace {
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline int elem_size(int dtype) { return dtype == EAGLE_BF16 ? 2 : 4; }
+
+int check_dims(const eagle_dims* d) {
+  if (!d) return EAGLE_ERR_ARG;
+  if (d->hidden <= 0 || d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->head_dim <= 0 || d->vocab <= 0 || d->ffn < 0)
+    return EAGLE_ERR_ARG;
+  if (d->n_q_heads % d->n_kv_heads) return EAGLE_ERR_UNSUPPORTED;
+  if (d->hidden % 64 || d->ffn % 64) return EAGLE_ERR_UNSUPPORTED;
+  if (d->dtype == EAGLE_BF16) {
+    if (d->head_dim != 128) return EAGLE_ERR_UNSUPPORTED;
+  } else if (d->dtype == EAGLE_F32) {
+    if (d->head_dim != 64 && d->head_dim != 128) return EAGLE_ERR_UNSUPPORTED;
+  } else {
+    return EAGLE_ERR_UNSUPPORTED;
+  }
+  if ((d->ffn == 0) != (d->rms_eps == 0.f)) return EAGLE_ERR_UNSUPPORTED;
+  if (d->rms_eps < 0.f || d->rope_theta < 0.f) return EAGLE_ERR_ARG;
+  return EAGLE_OK;
+}
+
+struct VerifyLayout {
+  size_t q, attn, y, act, attn_part, gemm_part, gemm_ssq, counters, keys, done, total;
+  GemmPlan p_qkv, p_o, p_gu, p_down, p_lm;
+  AttnPlan pa;
+};
+
+VerifyLayout plan_verify(const eagle_dims* d, int B, int total_nodes, int max_nodes, int max_prefix) {
+  VerifyLayout L{};
+  const int es = elem_size(d->dtype);
+  const int M = total_nodes;
+  const int H = d->hidden, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim, F = d->ffn, V = d->vocab;
+  L.p_qkv = plan_gemm(d->dtype, (Hq + 2 * Hkv) * D, H, M, 0, EPI_QKV, D);
+  L.p_o = plan_gemm(d->dtype, H, Hq * D, M, 0, EPI_RESID, D);
+  if (F > 0) {
+    L.p_gu = plan_gemm(d->dtype, F, H, M, 1, EPI_SILU, D);
+    L.p_down = plan_gemm(d->dtype, H, F, M, 0, EPI_RESID, D);
+  }
+  L.p_lm = plan_gemm(d->dtype, V, H, M, 0, EPI_ARGMAX, D);
+  L.pa = plan_attn(d->dtype, B, Hq, Hkv, D, max_nodes, max_prefix);
+  size_t pf = 0, sf = 0, ci = 0;
+  for (const GemmPlan* p : {&L.p_qkv, &L.p_o, &L.p_gu, &L.p_down, &L.p_lm}) {
+    if (p->n_tiles == 0) continue;
+    size_t a, b, c;
+    gemm_workspace(*p, &a, &b, &c);
+    pf = std::max(pf, a);
+    sf = std::max(sf, b);
+    ci = std::max(ci, c);
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(std::max<size_t>(bytes, 1));
+    return o;
+  };
+  L.q = take((size_t)M * Hq * D * es);
+  L.attn = take((size_t)M * Hq * D * es);
+  L.y = take((size_t)M * H * 4);
+  L.act = take((size_t)M * std::max(F, 1) * es);
+  L.attn_part = take(attn_workspace_floats(L.pa, B, Hkv, D) * 4);
+  L.gemm_part = take(pf * 4);
+  L.gemm_ssq = take(sf * 4);
+  L.counters = take(ci * 4);
+  L.keys = take((size_t)M * 8);
+  L.done = take(4);
+  L.total = off;
+  return L;
+}
+
+GemmDesc base_desc(const eagle_dims* d) {
+  GemmDesc g{};
+  g.dtype = d->dtype;
+  return g;
+}
+
+XSeg seg(const void* p, int dtype, int64_t ld, const int32_t* idx = nullptr) {
+  XSeg s;
+  s.ptr = p;
+  s.dtype = dtype;
+  s.ld = ld;
+  s.idx = idx;
+  return s;
+}
+
+}  // namespace
+
+// Verification of every node of every tree: one decoder layer + LM head with a fused argmax.
+int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_ln, const void* w_lm, int B,
+                const int32_t* tree_off, int total_nodes, int max_nodes, const void* x_in, const void* embed,
+                const int32_t* tokens, const uint64_t* anc, int mw, const int32_t* pos, const int32_t* prefix_len,
+                int max_prefix, const void* k_cache, const void* v_cache, const eagle_cache_layout* cache,
+                void* k_tree, void* v_tree, float* h_out, int32_t* argmax, float* maxlogit, float* dbg_attn,
+                float* dbg_logits, void* ws, size_t ws_bytes, eagle_timer* timer, hipStream_t s) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!lw || !w_lm || !tree_off || !anc || !pos || !prefix_len || !k_cache || !v_cache || !cache || !k_tree ||
+      !v_tree || !h_out || !argmax || !ws)
+    return EAGLE_ERR_ARG;
+  if (B < 1 || total_nodes < 1 || max_nodes < 1 || max_nodes > 64 * mw || mw < 1 || mw > 2 || max_prefix < 0)
+    return EAGLE_ERR_ARG;
+  if (!x_in && (!embed || !tokens)) return EAGLE_ERR_ARG;
+  const bool norm = d->rms_eps > 0.f;
+  if (!lw->w_qkv || !lw->w_o) return EAGLE_ERR_ARG;
+  if (norm && (!lw->ln_attn || !lw->ln_mlp || !lw->w_gate || !lw->w_up || !lw->w_down || !final_ln))
+    return EAGLE_ERR_ARG;
+  if (((uintptr_t)ws) & 255) return EAGLE_ERR_ARG;
+  if (cache->token_stride % 8 || cache->head_stride % 8 || cache->batch_stride % 8 || cache->capacity < 0)
+    return EAGLE_ERR_ARG;
+  const VerifyLayout L = plan_verify(d, B, total_nodes, max_nodes, max_prefix);
+  if (ws_bytes < L.total) return EAGLE_ERR_WORKSPACE;
+  char* w = (char*)ws;
+  const int dt = d->dtype;
+  const int H = d->hidden, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim, F = d->ffn, V = d->vocab;
+  const int M = total_nodes;
+  void* q = w + L.q;
+  void* attn = w + L.attn;
+  float* y = (float*)(w + L.y);
+  void* act = w + L.act;
+  float* gpart = (float*)(w + L.gemm_part);
+  float* gssq = (float*)(w + L.gemm_ssq);
+  int* counters = (int*)(w + L.counters);
+  unsigned long long* keys = (unsigned long long*)(w + L.keys);
+  int* done = (int*)(w + L.done);
+
+  // x: the given node states, or the token embeddings
+  const XSeg xseg = x_in ? seg(x_in, dt, H) : seg(embed, dt, H, tokens);
+
+  // 1. RMSNorm -> QKV projection -> rotary at pos -> q (workspace), k_tree, v_tree
+  {
+    GemmDesc g = base_desc(d);
+    g.w0 = lw->w_qkv;
+    g.n = (Hq + 2 * Hkv) * D;
+    g.k = H;
+    g.ldw = H;
+    g.m = M;
+    g.x.a = xseg;
+    g.x.b = xseg;
+    g.x.ka = H;
+    g.x.norm = norm;
+    g.x.gain = norm ? lw->ln_attn : nullptr;
+    g.x.gain_dtype = dt;
+    g.x.eps = d->rms_eps;
+    g.epi.kind = EPI_QKV;
+    g.epi.q_out = q;
+    g.epi.k_out = k_tree;
+    g.epi.v_out = v_tree;
+    g.epi.out_dtype = dt;
+    g.epi.pos = pos;
+    g.epi.hq = Hq;
+    g.epi.hkv = Hkv;
+    g.epi.hd = D;
+    g.epi.theta = d->rope_theta;
+    g.partials = gpart;
+    g.sumsq_part = gssq;
+    g.counters = counters;
+    timer_begin(timer, ST_QKV, s);
+    rc = launch_gemm(g, L.p_qkv, s);
+    timer_end(timer, s);
+    if (rc) return rc;
+  }
+  // 2. tree-masked attention -> attn (workspace)
+  {
+    AttnArgs a{};
+    a.dtype = dt;
+    a.batch = B;
+    a.hq = Hq;
+    a.hkv = Hkv;
+    a.hd = D;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.cb = cache->batch_stride;
+    a.ch = cache->head_stride;
+    a.ct = cache->token_stride;
+    a.cap = cache->capacity;
+    a.k_tree = k_tree;
+    a.v_tree = v_tree;
+    a.anc = anc;
+    a.mw = mw;
+    a.tree_off = tree_off;
+    a.prefix_len = prefix_len;
+    a.max_nodes = max_nodes;
+    a.max_prefix = max_prefix;
+    a.out = attn;
+    a.dbg = dbg_attn;
+    a.part_o = (float*)(w + L.attn_part);
+    a.part_ml = a.part_o + (size_t)B * Hkv * L.pa.n_chunks * L.pa.rmax * D;
+    rc = dt == EAGLE_F32 ? launch_attn_f32(a, M, timer, s) : launch_attn(a, L.pa, timer, s);
+    if (rc) return rc;
+  }
+  // 3. O projection + residual -> y (or h_out for the attention-only layer)
+  float* yout = F > 0 ? y : h_out;
+  {
+    GemmDesc g = base_desc(d);
+    g.w0 = lw->w_o;
+    g.n = H;
+    g.k = Hq * D;
+    g.ldw = Hq * D;
+    g.m = M;
+    g.x.a = seg(attn, dt, Hq * D);
+    g.x.b = g.x.a;
+    g.x.ka = Hq * D;
+    g.epi.kind = EPI_RESID;
+    g.epi.out = yout;
+    g.epi.ld_out = H;
+    // residual = x: the given rows, or the embedding rows of the node tokens
+    g.epi.resid = x_in ? x_in : embed;
+    g.epi.resid_idx = x_in ? nullptr : tokens;
+    g.epi.resid_dtype = dt;
+    g.epi.ld_resid = H;
+    g.partials = gpart;
+    g.sumsq_part = gssq;
+    g.counters = counters;
+    timer_begin(timer, ST_O, s);
+    rc = launch_gemm(g, L.p_o, s);
+    timer_end(timer, s);
+    if (rc) return rc;
+  }
+  if (F > 0) {
+    // 4. RMSNorm -> gate/up -> SiLU(gate) * up -> act (workspace)
+    GemmDesc g = base_desc(d);
+    g.w0 = lw->w_gate;
+    g.w1 = lw->w_up;
+    g.dual = 1;
+    g.n = F;
+    g.k = H;
+    g.ldw = H;
+    g.m = M;
+    g.x.a = seg(y, EAGLE_F32, H);
+    g.x.b = g.x.a;
+    g.x.ka = H;
+    g.x.norm = 1;
+    g.x.gain = lw->ln_mlp;
+    g.x.gain_dtype = dt;
+    g.x.eps = d->rms_eps;
+    g.epi.kind = EPI_SILU;
+    g.epi.act = act;
+    g.epi.act_dtype = dt;
+    g.epi.ld_act = F;
+    g.partials = gpart;
+    g.sumsq_part = gssq;
+    g.counters = counters;
+    timer_begin(timer, ST_GATE_UP, s);
+    rc = launch_gemm(g, L.p_gu, s);
+    timer_end(timer, s);
+    if (rc) return rc;
+    // 5. down projection + residual -> h_out
+    GemmDesc g2 = base_desc(d);
+    g2.w0 = lw->w_down;
+    g2.n = H;
+    g2.k = F;
+    g2.ldw = F;
+    g2.m = M;
+    g2.x.a = seg(act, dt, F);
+    g2.x.b = g2.x.a;
+    g2.x.ka = F;
+    g2.epi.kind = EPI_RESID;
+    g2.epi.out = h_out;
+    g2.epi.ld_out = H;
+    g2.epi.resid = y;
+    g2.epi.resid_dtype = EAGLE_F32;
+    g2.epi.ld_resid = H;
+    g2.partials = gpart;
+    g2.sumsq_part = gssq;
+    g2.counters = counters;
+    timer_begin(timer, ST_DOWN, s);
+    rc = launch_gemm(g2, L.p_down, s);
+    timer_end(timer, s);
+    if (rc) return rc;
+  }
+  // 6. final RMSNorm -> LM head with fused row argmax
+  {
+    GemmDesc g = base_desc(d);
+    g.w0 = w_lm;
+    g.n = V;
+    g.k = H;
+    g.ldw = H;
+    g.m = M;
+    g.x.a = seg(h_out, EAGLE_F32, H);
+    g.x.b = g.x.a;
+    g.x.ka = H;
+    g.x.norm = norm;
+    g.x.gain = norm ? final_ln : nullptr;
+    g.x.gain_dtype = dt;
+    g.x.eps = d->rms_eps;
+    g.epi.kind = EPI_ARGMAX;
+    g.epi.keys = keys;
+    g.epi.dbg_logits = dbg_logits;
+    g.epi.ld_logits = V;
+    g.epi.argmax_out = argmax;
+    g.epi.max_out = maxlogit;
+    g.epi.done = done;
+    g.partials = gpart;
+    g.sumsq_part = gssq;
+    g.counters = counters;
+    timer_begin(timer, ST_LM_HEAD, s);
+    rc = launch_gemm(g, L.p_lm, s);
+    timer_end(timer, s);
+    if (rc) return rc;
+  }
+  return EAGLE_OK;
+}
+
+size_t verify_workspace(const eagle_dims* d, int B, int total_nodes, int max_nodes, int max_prefix) {
+  if (check_dims(d) || B < 1 || total_nodes < 1 || max_nodes < 1) return 0;
+  return plan_verify(d, B, total_nodes, max_nodes, max_prefix).total;
+}
+
+}  // namespace eagle
+
+using namespace eagle;
+
+extern "C" {
+
+int eagle_abi_version(void) { return EAGLE_ABI_VERSION; }
+
+const char* eagle_status_str(int st) {
+  switch (st) {
+    case EAGLE_OK: return "ok";
+    case EAGLE_ERR_ARG: return "invalid argument";
+    case EAGLE_ERR_TREE: return "malformed parent array";
+    case EAGLE_ERR_CAPACITY: return "capacity exceeded";
+    case EAGLE_ERR_UNSUPPORTED: return "unsupported dimensions";
+    case EAGLE_ERR_HIP: return "HIP error";
+    case EAGLE_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+int eagle_tree_build(int32_t batch, const int32_t* tree_off, int32_t total_nodes, int32_t max_nodes,
+                     const int32_t* parent, const int32_t* prefix_len, int32_t mask_words, uint64_t* anc,
+                     int32_t* depth, int32_t* pos, int32_t* dev_status, void* stream) {
+  if (batch < 1 || total_nodes < 1 || max_nodes < 1) return EAGLE_ERR_ARG;
+  if (!tree_off || !parent || !prefix_len || !anc || !depth || !pos) return EAGLE_ERR_ARG;
+  if (mask_words < 1 || mask_words > 2) return EAGLE_ERR_UNSUPPORTED;
+  if (max_nodes > 64 * mask_words) return EAGLE_ERR_CAPACITY;
+  hipStream_t s = (hipStream_t)stream;
+  return launch_tree_build(batch, tree_off, parent, prefix_len, mask_words, anc, depth, pos, dev_status, s);
+}
+
+int eagle_tree_verify(const eagle_dims* dims, const eagle_layer_w* layer, const void* final_ln, const void* w_lm,
+                      int32_t batch, const int32_t* tree_off, int32_t total_nodes, int32_t max_nodes,
+                      const void* x_in, const void* embed, const int32_t* tokens, const uint64_t* anc,
+                      int32_t mask_words, const int32_t* pos, const int32_t* prefix_len, int32_t max_prefix,
+                      const void* k_cache, const void* v_cache, const eagle_cache_layout* cache, void* k_tree,
+                      void* v_tree, float* h_out, int32_t* argmax, float* maxlogit, float* dbg_attn,
+                      float* dbg_logits, void* workspace, size_t ws_bytes, eagle_timer* timer, void* stream) {
+  return verify_impl(dims, layer, final_ln, w_lm, batch, tree_off, total_nodes, max_nodes, x_in, embed, tokens, anc,
+                     mask_words, pos, prefix_len, max_prefix, k_cache, v_cache, cache, k_tree, v_tree, h_out,
+                     argmax, maxlogit, dbg_attn, dbg_logits, workspace, ws_bytes, timer, (hipStream_t)stream);
+}
+
+int eagle_accept_commit(int32_t batch, const int32_t* tree_off, int32_t max_nodes, const int32_t* parent,
+                        const int32_t* tokens, const int32_t* argmax, const uint64_t* anc, int32_t mask_words,
+                        const int32_t* depth, const void* k_tree, const void* v_tree, void* k_cache, void* v_cache,
+                        const eagle_cache_layout* cache, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                        int32_t* prefix_len, const float* h_nodes, int32_t hidden, float* next_feature,
+                        int32_t max_accept, int32_t* accept_len, int32_t* path, int32_t* out_tokens,
+                        int32_t* next_token, int32_t* dev_status, void* stream) {
+  if (batch < 1 || max_nodes < 1 || !tree_off || !parent || !tokens || !argmax || !anc || !depth || !k_tree ||
+      !v_tree || !k_cache || !v_cache || !cache || !prefix_len || !accept_len || !path || !out_tokens || !next_token)
+    return EAGLE_ERR_ARG;
+  if (mask_words < 1 || mask_words > 2 || max_nodes > 64 * mask_words) return EAGLE_ERR_CAPACITY;
+  if (max_accept < 0 || max_accept > 127) return EAGLE_ERR_ARG;
+  if (dtype != EAGLE_BF16 && dtype != EAGLE_F32) return EAGLE_ERR_UNSUPPORTED;
+  const int es = elem_size(dtype);
+  if (n_kv_heads < 1 || head_dim < 1 || (head_dim * es) % 16) return EAGLE_ERR_UNSUPPORTED;
+  if ((cache->token_stride * es) % 16 || (cache->head_stride * es) % 16 || (cache->batch_stride * es) % 16)
+    return EAGLE_ERR_ARG;
+  if (next_feature && (!h_nodes || hidden < 1)) return EAGLE_ERR_ARG;
+  AcceptArgs a{};
+  a.tree_off = tree_off;
+  a.parent = parent;
+  a.tokens = tokens;
+  a.argmax = argmax;
+  a.anc = anc;
+  a.mw = mask_words;
+  a.depth = depth;
+  a.k_tree = k_tree;
+  a.v_tree = v_tree;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cb = cache->batch_stride;
+  a.ch = cache->head_stride;
+  a.ct = cache->token_stride;
+  a.capacity = cache->capacity;
+  a.hkv = n_kv_heads;
+  a.hd = head_dim;
+  a.elem = es;
+  a.prefix_len = prefix_len;
+  a.h_nodes = h_nodes;
+  a.hidden = hidden;
+  a.next_feature = next_feature;
+  a.max_accept = max_accept;
+  a.accept_len = accept_len;
+  a.path = path;
+  a.out_tokens = out_tokens;
+  a.next_token = next_token;
+  a.status = dev_status;
+  return launch_accept_commit(a, batch, (hipStream_t)stream);
+}
+
+size_t eagle_workspace_size(int32_t which, const eagle_dims* dims, int32_t batch, int32_t total_nodes,
+                            int32_t max_nodes, int32_t max_prefix, const eagle_draft_params* params) {
+  if (which == 0) return verify_workspace(dims, batch, total_nodes, max_nodes, max_prefix);
+  if (which == 1) return draft_workspace(dims, params, batch, max_prefix);
+  return 0;
+}
+
+int eagle_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+  if (!workspace) return EAGLE_ERR_ARG;
+  return launch_fill_zero(workspace, ws_bytes, (hipStream_t)stream);
+}
+
+eagle_timer* eagle_timer_create(int32_t capacity) {
+  if (capacity < 1) return nullptr;
+  eagle_timer* t = new eagle_timer();
+  t->cap = capacity;
+  t->ev.resize(2 * capacity);
+  t->stage.resize(capacity);
+  for (auto& e : t->ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      delete t;
+      return nullptr;
+    }
+  }
+  return t;
+}
+
+void eagle_timer_destroy(eagle_timer* t) {
+  if (!t) return;
+  for (auto& e : t->ev) hipEventDestroy(e);
+  delete t;
+}
+
+int eagle_timer_collect(eagle_timer* t, double* ms, int32_t* count) {
+  if (!t || !ms || !count) return EAGLE_ERR_ARG;
+  for (int i = 0; i < t->n; ++i) {
+    if (hipEventSynchronize(t->ev[2 * i + 1]) != hipSuccess) return EAGLE_ERR_HIP;
+    float e = 0.f;
+    if (hipEventElapsedTime(&e, t->ev[2 * i], t->ev[2 * i + 1]) != hipSuccess) return EAGLE_ERR_HIP;
+    const int st = t->stage[i];
+    if (st >= 0 && st < EAGLE_N_STAGES) {
+      ms[st] += e;
+      count[st] += 1;
+    }
+  }
+  t->n = 0;
+  t->open = false;
+  return EAGLE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Internal interface of the tree-masked GQA attention kernels.
+#pragma once
+
+#include "common.h"
+
+namespace eagle {
+
+struct AttnArgs {
+  int dtype;  // EAGLE_BF16 (MFMA path, head_dim 128) or EAGLE_F32 (VALU path)
+  int batch, hq, hkv, hd;
+  const void* q;         // [sum N][hq][hd]
+  const void* k_cache;   // cache layout below
+  const void* v_cache;
+  int64_t cb, ch, ct;    // cache strides (elements)
+  int cap;               // cache slots per (b, h); prefix lengths are clamped to it
+  const void* k_tree;    // [sum N][hkv][hd]
+  const void* v_tree;
+  const uint64_t* anc;   // [sum N][mw]
+  int mw;
+  const int32_t* tree_off;
+  const int32_t* prefix_len;
+  int max_nodes, max_prefix;
+  void* out;             // [sum N][hq * hd] (dtype)
+  float* dbg;            // optional [sum N][hq * hd] f32
+  // split-KV plan and partials (bf16 path)
+  int kch, n_chunks;     // prefix chunk length; chunks including the tree chunk
+  int row_groups;        // groups of 128 query rows per (b, kv head)
+  float* part_o;         // [B][hkv][n_chunks][rmax][hd]
+  float* part_ml;        // [B][hkv][n_chunks][rmax][2]
+};
+
+struct AttnPlan {
+  int kch, n_chunks, row_groups, rmax;
+};
+
+AttnPlan plan_attn(int dtype, int batch, int hq, int hkv, int hd, int max_nodes, int max_prefix);
+size_t attn_workspace_floats(const AttnPlan& p, int batch, int hkv, int hd);
+int launch_attn(AttnArgs& a, const AttnPlan& p, eagle_timer* timer, hipStream_t s);
+int launch_attn_f32(AttnArgs& a, int total_nodes, eagle_timer* timer, hipStream_t s);
+
+}  // namespace eagle

@@ -1,0 +1,411 @@
+// Tree-masked GQA attention over [KV prefix ; tree nodes] (gfx950).
+//
+// Every drafted node attends to the whole committed prefix of its sequence and to
+// the tree nodes on its own root path (ancestor bitmask, self included), so all nodes
+// of a tree are verified in one pass.
+//
+// bf16 path (head_dim 128): for one (sequence, KV head) the query rows are the g query
+// heads of every node (row = node * g + head-in-group), so a K/V tile is loaded once
+// and used by all of them (GQA).  Split-KV: workgroup (b, kv head, chunk, row group)
+// handles up to 128 query rows against one chunk of prefix keys, or against the tree
+// keys (the last chunk), and writes fp32 partials (running max, sum, unnormalised o);
+// a merge kernel combines the chunks in fixed order (deterministic).
+//  * K and V tiles (64 keys) are read with 16-byte coalesced loads and staged in LDS;
+//    V is written transposed so that the PV product reads 8-byte runs of keys.
+//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 d from LDS, B = Q held
+//    in registers); each lane then owns 4 consecutive keys of one query row, so the
+//    row max needs only two cross-lane swaps and the softmax rescale of the output is
+//    lane-local.
+//  * O^T += V^T P^T with the same MFMA (A = V^T from LDS, B = P packed to bf16 in
+//    registers, exactly the lane layout the score MFMA produced).
+//  * tree keys are masked with the node's ancestor words: key j is visible iff bit j.
+// fp32 path: a plain VALU kernel, one wave per (node, query head).
+#include "attn.h"
+
+#include <algorithm>
+
+namespace eagle {
+
+namespace {
+
+constexpr int kXcds = 8;
+constexpr int NWA = 4;                  // waves per workgroup
+constexpr int RBW = 2;                  // 16-row query blocks per wave
+constexpr int ROWS_WG = NWA * RBW * 16; // query rows per workgroup
+constexpr int KT = 64;                  // keys per LDS tile
+constexpr int HD = 128;
+constexpr int KS = HD + 8;              // LDS row stride of the K tile (bf16)
+constexpr int VS = KT + 8;              // LDS row stride of the transposed V tile (bf16)
+
+__device__ __forceinline__ int remap_xcd(int b, int total) {
+  const int per = (total + kXcds - 1) / kXcds;
+  return (b % kXcds) * per + b / kXcds;
+}
+
+__global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, int grid_real) {
+  __shared__ __align__(16) bf16 ks[KT * KS];
+  __shared__ __align__(16) bf16 vt[HD * VS];
+
+  const int bid = remap_xcd(blockIdx.x, gridDim.x);
+  if (bid >= grid_real) return;
+  int t = bid;
+  const int rg = t % a.row_groups;
+  t /= a.row_groups;
+  const int c = t % a.n_chunks;
+  t /= a.n_chunks;
+  const int kvh = t % a.hkv;
+  const int b = t / a.hkv;
+
+  const int off = a.tree_off[b];
+  const int N = a.tree_off[b + 1] - off;
+  const int g = a.hq / a.hkv;
+  const int R = N * g;
+  const int row_base = rg * ROWS_WG;
+  if (row_base >= R || N > a.max_nodes) return;
+  const int P = min(max(a.prefix_len[b], 0), a.cap);
+  const bool tree_chunk = (c == a.n_chunks - 1);
+  int k0, k1;
+  if (tree_chunk) {
+    k0 = 0;
+    k1 = N;
+  } else {
+    k0 = c * a.kch;
+    k1 = min(P, k0 + a.kch);
+    if (k0 >= k1) return;
+  }
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const bf16* q = (const bf16*)a.q;
+
+  // Visibility words per query row: the tree chunk uses the node's ancestor words
+  // (key j visible iff bit j); prefix chunks see every key, so their words are all ones.
+  // Keeping the mask arithmetic free of branches matters: a branch between a score
+  // MFMA and the read of its accumulator has been seen to lose the required wait states.
+  bf16x8_t qf[RBW][4];
+  uint64_t vis0[RBW], vis1[RBW];
+#pragma unroll
+  for (int j = 0; j < RBW; ++j) {
+    const int row = row_base + (w * RBW + j) * 16 + lr;
+    vis0[j] = ~0ull;
+    vis1[j] = ~0ull;
+    if (row < R) {
+      const int node = row / g, hh = row % g;
+      const bf16* qp = q + ((int64_t)(off + node) * a.hq + kvh * g + hh) * HD;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qf[j][kk] = *(const bf16x8_t*)(qp + kk * 32 + lq * 8);
+      if (tree_chunk) {
+        vis0[j] = a.anc[(int64_t)(off + node) * a.mw];
+        vis1[j] = a.mw > 1 ? a.anc[(int64_t)(off + node) * a.mw + 1] : 0ull;
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qf[j][kk] = bf16x8_t{};
+    }
+  }
+
+  f32x4 o[RBW][8];
+  float mrow[RBW], lsum[RBW];
+#pragma unroll
+  for (int j = 0; j < RBW; ++j) {
+    mrow[j] = -INFINITY;
+    lsum[j] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // scores in log2 units: q.k / sqrt(128) * log2(e)
+  const float sl2 = 0.08838834764831845f * 1.4426950408889634f;
+
+  const bf16* kc = (const bf16*)a.k_cache + (int64_t)b * a.cb + (int64_t)kvh * a.ch;
+  const bf16* vc = (const bf16*)a.v_cache + (int64_t)b * a.cb + (int64_t)kvh * a.ch;
+  const bf16* kt_base = (const bf16*)a.k_tree + ((int64_t)off * a.hkv + kvh) * HD;
+  const bf16* vt_base = (const bf16*)a.v_tree + ((int64_t)off * a.hkv + kvh) * HD;
+  const int64_t tree_stride = (int64_t)a.hkv * HD;
+
+  for (int kt0 = k0; kt0 < k1; kt0 += KT) {
+    __syncthreads();
+    for (int i = tid; i < KT * 16; i += NWA * 64) {
+      const int kk = i >> 4, gd = i & 15;
+      const int key = kt0 + kk;
+      uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = make_uint4(0u, 0u, 0u, 0u);
+      if (key < k1) {
+        const bf16* kp = tree_chunk ? kt_base + key * tree_stride : kc + key * a.ct;
+        const bf16* vp = tree_chunk ? vt_base + key * tree_stride : vc + key * a.ct;
+        kv = *(const uint4*)(kp + gd * 8);
+        vv = *(const uint4*)(vp + gd * 8);
+      }
+      *(uint4*)(ks + kk * KS + gd * 8) = kv;
+      const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt[(gd * 8 + 2 * e) * VS + kk] = (bf16)(wv[e] & 0xffffu);
+        vt[(gd * 8 + 2 * e + 1) * VS + kk] = (bf16)(wv[e] >> 16);
+      }
+    }
+    __syncthreads();
+
+    float s[RBW][4][4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bf16x8_t kf[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kf[kk] = *(const bf16x8_t*)(ks + (st * 16 + lr) * KS + kk * 32 + lq * 8);
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[j][kk], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kt0 + st * 16 + lq * 4 + i;
+          const uint64_t word = (key & 64) ? vis1[j] : vis0[j];
+          const bool vis = (key < k1) & (bool)((word >> (key & 63)) & 1ull);
+          s[j][st][i] = vis ? acc[i] * sl2 : -INFINITY;
+        }
+      }
+    }
+
+#pragma unroll
+    for (int j = 0; j < RBW; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][st][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(mrow[j], mx);
+      const float mbase = (mnew == -INFINITY) ? 0.f : mnew;
+      const float fac = exp2f(mrow[j] - mbase);
+      mrow[j] = mnew;
+      float ps = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2f(s[j][st][i] - mbase);
+          s[j][st][i] = p;
+          ps += p;
+        }
+      lsum[j] = lsum[j] * fac + ps;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[j][db] *= fac;
+    }
+
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      bf16x8_t pb[RBW];
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) {
+        union {
+          uint32_t u[4];
+          bf16x8_t v;
+        } pk;
+        pk.u[0] = pack2bf(s[j][2 * G][0], s[j][2 * G][1]);
+        pk.u[1] = pack2bf(s[j][2 * G][2], s[j][2 * G][3]);
+        pk.u[2] = pack2bf(s[j][2 * G + 1][0], s[j][2 * G + 1][1]);
+        pk.u[3] = pack2bf(s[j][2 * G + 1][2], s[j][2 * G + 1][3]);
+        pb[j] = pk.v;
+      }
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16* vr = vt + (db * 16 + lr) * VS + G * 32 + lq * 4;
+        union {
+          uint2 u[2];
+          bf16x8_t v;
+        } va;
+        va.u[0] = *(const uint2*)(vr);
+        va.u[1] = *(const uint2*)(vr + 16);
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) o[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[j], o[j][db], 0, 0, 0);
+      }
+    }
+  }
+
+  const int rmax = a.max_nodes * g;
+#pragma unroll
+  for (int j = 0; j < RBW; ++j) {
+    float l = lsum[j];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int row = row_base + (w * RBW + j) * 16 + lr;
+    if (row < R) {
+      const int64_t pidx = ((int64_t)(b * a.hkv + kvh) * a.n_chunks + c) * rmax + row;
+      if (lq == 0) {
+        a.part_ml[pidx * 2] = mrow[j];
+        a.part_ml[pidx * 2 + 1] = l;
+      }
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *(f32x4*)(a.part_o + pidx * HD + db * 16 + lq * 4) = o[j][db];
+    }
+  }
+}
+
+// Combine the chunks of every query row in fixed order: o = sum_c 2^(m_c - M) o_c / L.
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int grid_real) {
+  const int bid = blockIdx.x;
+  if (bid >= grid_real) return;
+  const int g = a.hq / a.hkv;
+  const int rmax = a.max_nodes * g;
+  const int rpairs = (rmax + 1) / 2;
+  int t = bid;
+  const int rp = t % rpairs;
+  t /= rpairs;
+  const int kvh = t % a.hkv;
+  const int b = t / a.hkv;
+  const int off = a.tree_off[b];
+  const int N = a.tree_off[b + 1] - off;
+  const int row = rp * 2 + threadIdx.x / HD;
+  const int d = threadIdx.x % HD;
+  if (row >= N * g || N > a.max_nodes) return;
+  const int P = min(max(a.prefix_len[b], 0), a.cap);
+  const int n_pref = min((P + a.kch - 1) / a.kch, a.n_chunks - 1);
+  const int64_t base = (int64_t)(b * a.hkv + kvh) * a.n_chunks;
+  float M = -INFINITY;
+  for (int c = 0; c < a.n_chunks; ++c) {
+    if (c >= n_pref && c != a.n_chunks - 1) continue;
+    M = fmaxf(M, a.part_ml[((base + c) * rmax + row) * 2]);
+  }
+  float L = 0.f, O = 0.f;
+  for (int c = 0; c < a.n_chunks; ++c) {
+    if (c >= n_pref && c != a.n_chunks - 1) continue;
+    const int64_t pi = (base + c) * rmax + row;
+    const float f = exp2f(a.part_ml[pi * 2] - M);
+    L += f * a.part_ml[pi * 2 + 1];
+    O += f * a.part_o[pi * HD + d];
+  }
+  const float out = O / L;
+  const int node = row / g, hh = row % g;
+  const int64_t oi = (int64_t)(off + node) * a.hq * HD + (int64_t)(kvh * g + hh) * HD + d;
+  ((bf16*)a.out)[oi] = f2bf(out);
+  if (a.dbg) a.dbg[oi] = out;
+}
+
+// fp32 path: one wave per (node, query head); scores staged in LDS.
+__global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnArgs a) {
+  extern __shared__ float sm[];
+  const int hq = a.hq, hd = a.hd;
+  const int node_g = blockIdx.x / hq, h = blockIdx.x % hq;
+  int b = 0;
+  while (b + 1 < a.batch && a.tree_off[b + 1] <= node_g) ++b;
+  const int off = a.tree_off[b];
+  const int N = a.tree_off[b + 1] - off;
+  const int i = node_g - off;
+  if (N > a.max_nodes) return;
+  const int P = min(min(max(a.prefix_len[b], 0), a.cap), a.max_prefix);
+  const int kvh = h / (hq / a.hkv);
+  const int lane = threadIdx.x;
+  float* qs = sm;
+  float* sc = sm + hd;
+  const float* q = (const float*)a.q + ((int64_t)node_g * hq + h) * hd;
+  for (int d = lane; d < hd; d += 64) qs[d] = q[d];
+  __syncthreads();
+  const float* kc = (const float*)a.k_cache + (int64_t)b * a.cb + (int64_t)kvh * a.ch;
+  const float* vc = (const float*)a.v_cache + (int64_t)b * a.cb + (int64_t)kvh * a.ch;
+  const float* ktr = (const float*)a.k_tree;
+  const float* vtr = (const float*)a.v_tree;
+  const float scale = rsqrtf((float)hd);
+  float mx = -INFINITY;
+  for (int j = lane; j < P + N; j += 64) {
+    float s = -INFINITY;
+    const float* kp = nullptr;
+    if (j < P) {
+      kp = kc + (int64_t)j * a.ct;
+    } else {
+      const int jn = j - P;
+      const uint64_t word = a.anc[(int64_t)(off + i) * a.mw + (jn >> 6)];
+      if ((word >> (jn & 63)) & 1ull) kp = ktr + ((int64_t)(off + jn) * a.hkv + kvh) * hd;
+    }
+    if (kp) {
+      float acc = 0.f;
+      for (int d = 0; d < hd; ++d) acc += qs[d] * kp[d];
+      s = acc * scale;
+    }
+    sc[j] = s;
+    mx = fmaxf(mx, s);
+  }
+  mx = wave_max(mx);
+  float sum = 0.f;
+  for (int j = lane; j < P + N; j += 64) {
+    const float p = __expf(sc[j] - mx);
+    sc[j] = p;
+    sum += p;
+  }
+  sum = wave_sum(sum);
+  __syncthreads();
+  for (int d = lane; d < hd; d += 64) {
+    float acc = 0.f;
+    for (int j = 0; j < P + N; ++j) {
+      const float p = sc[j];
+      if (p == 0.f) continue;
+      const float* vp = j < P ? vc + (int64_t)j * a.ct : vtr + ((int64_t)(off + j - P) * a.hkv + kvh) * hd;
+      acc += p * vp[d];
+    }
+    const float out = acc / sum;
+    const int64_t oi = (int64_t)node_g * hq * hd + (int64_t)h * hd + d;
+    ((float*)a.out)[oi] = out;
+    if (a.dbg) a.dbg[oi] = out;
+  }
+}
+
+}  // namespace
+
+AttnPlan plan_attn(int dtype, int batch, int hq, int hkv, int hd, int max_nodes, int max_prefix) {
+  AttnPlan p{};
+  const int g = hq / hkv;
+  p.rmax = max_nodes * g;
+  if (dtype == EAGLE_F32) {
+    p.kch = 0;
+    p.n_chunks = 0;
+    p.row_groups = 0;
+    return p;
+  }
+  // prefix chunks: at least 512 keys, at most 32 chunks per (b, kv head)
+  int nch = std::max(1, (max_prefix + 511) / 512);
+  nch = std::min(nch, 32);
+  int kch = (max_prefix + nch - 1) / nch;
+  kch = std::max(KT, (kch + KT - 1) / KT * KT);
+  nch = std::max(1, (max_prefix + kch - 1) / kch);
+  p.kch = kch;
+  p.n_chunks = nch + 1;  // + the tree chunk
+  p.row_groups = (p.rmax + ROWS_WG - 1) / ROWS_WG;
+  (void)batch;
+  (void)hd;
+  return p;
+}
+
+size_t attn_workspace_floats(const AttnPlan& p, int batch, int hkv, int hd) {
+  if (p.n_chunks == 0) return 0;
+  const size_t rows = (size_t)batch * hkv * p.n_chunks * p.rmax;
+  return rows * hd + rows * 2;
+}
+
+int launch_attn(AttnArgs& a, const AttnPlan& p, eagle_timer* timer, hipStream_t s) {
+  if (a.dtype == EAGLE_F32) return EAGLE_ERR_ARG;  // the fp32 path is launch_attn_f32
+  if (a.hd != HD) return EAGLE_ERR_UNSUPPORTED;
+  a.kch = p.kch;
+  a.n_chunks = p.n_chunks;
+  a.row_groups = p.row_groups;
+  const int grid = a.batch * a.hkv * p.n_chunks * p.row_groups;
+  const int padded = (grid + kXcds - 1) / kXcds * kXcds;
+  timer_begin(timer, ST_ATTN, s);
+  hipLaunchKernelGGL(tree_attn_bf16_kernel, dim3(padded), dim3(NWA * 64), 0, s, a, grid);
+  timer_end(timer, s);
+  const int g = a.hq / a.hkv;
+  const int mgrid = a.batch * a.hkv * ((a.max_nodes * g + 1) / 2);
+  timer_begin(timer, ST_ATTN_MERGE, s);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(mgrid), dim3(256), 0, s, a, mgrid);
+  timer_end(timer, s);
+  return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
+}
+
+int launch_attn_f32(AttnArgs& a, int total_nodes, eagle_timer* timer, hipStream_t s) {
+  const size_t lds = (size_t)(a.hd + a.max_prefix + a.max_nodes) * sizeof(float);
+  if (lds > 60 * 1024) return EAGLE_ERR_UNSUPPORTED;
+  timer_begin(timer, ST_ATTN, s);
+  hipLaunchKernelGGL(tree_attn_f32_kernel, dim3(total_nodes * a.hq), dim3(64), lds, s, a);
+  timer_end(timer, s);
+  return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
+}
+
+}  // namespace eagle

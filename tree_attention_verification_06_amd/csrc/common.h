@@ -1,0 +1,73 @@
+// Internal helpers shared by the HIP sources of the EAGLE tree-verification library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/eagle.h"
+
+namespace eagle {
+
+typedef uint16_t bf16;  // IEEE bfloat16 bit pattern
+
+// Vector types for the gfx950 bf16 MFMA builtins.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(bf16 h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// float -> bf16, round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ bf16 f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack2bf(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key; -0 < +0).
+__device__ __forceinline__ uint32_t f2ord(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord2f(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+// 64-bit argmax key: value in the high word, (~index) in the low word, so the
+// unsigned maximum is the largest value and, among equal values, the lowest index.
+__device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) {
+  return ((unsigned long long)f2ord(v) << 32) | (unsigned long long)(0xffffffffu - idx);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Per-launch HIP event timing (optional).
+struct Timer;
+void timer_begin(eagle_timer* t, int stage, hipStream_t s);
+void timer_end(eagle_timer* t, hipStream_t s);
+
+enum Stage {
+  ST_TREE_BUILD = 0, ST_QKV = 1, ST_ATTN = 2, ST_ATTN_MERGE = 3, ST_O = 4, ST_GATE_UP = 5, ST_DOWN = 6,
+  ST_LM_HEAD = 7, ST_ACCEPT = 8, ST_DRAFT_FC = 9, ST_DRAFT_TOPK = 10, ST_DRAFT_SELECT = 11, ST_OTHER = 12
+};
+
+}  // namespace eagle
+
+#define EAGLE_HIP_CHECK(expr)                         \
+  do {                                                \
+    hipError_t e_ = (expr);                           \
+    if (e_ != hipSuccess) return EAGLE_ERR_HIP;       \
+  } while (0)

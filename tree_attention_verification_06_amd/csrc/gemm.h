@@ -1,0 +1,102 @@
+// Internal interface of the skinny (few-token) GEMM used for every projection of the
+// verify and draft paths: Y[m][n] = sum_k X[m][k] * W[n][k], W row-major [n][k].
+#pragma once
+
+#include "common.h"
+
+namespace eagle {
+
+// One segment of the activation source X.  Row m of the segment is row idx[m]
+// (idx == nullptr: row m) of a row-major matrix with row stride ld (elements).
+struct XSeg {
+  const void* ptr;
+  int dtype;  // EAGLE_BF16 / EAGLE_F32
+  int64_t ld;
+  const int32_t* idx;
+};
+
+// X = [segment a (k < ka) ; segment b (k >= ka)].  With norm != 0 the GEMM consumes
+// gain[k] * x[m][k] and the epilogue multiplies row m by rsqrt(mean_k x[m][k]^2 + eps):
+// W RMSNorm(x) = (W (gain * x)) / rms(x).
+struct XSrc {
+  XSeg a, b;
+  int ka;
+  const void* gain;
+  int gain_dtype;
+  int norm;
+  float eps;
+};
+
+enum EpiKind { EPI_STORE_F32 = 0, EPI_QKV = 1, EPI_RESID = 2, EPI_SILU = 3, EPI_ARGMAX = 4, EPI_TOPK = 5 };
+
+struct Epi {
+  int kind;
+  // EPI_STORE_F32 / EPI_RESID: out[m][n] (+= resid[m][n])
+  float* out;
+  int64_t ld_out;
+  const void* resid;
+  int resid_dtype;
+  int64_t ld_resid;
+  const int32_t* resid_idx;  // row m of the residual is row resid_idx[m] (nullptr: m)
+  // EPI_SILU: act[m][f] = SiLU(gate) * up, element type act_dtype
+  void* act;
+  int act_dtype;
+  int64_t ld_act;
+  // EPI_QKV: rotary at pos[m], scatter into q [m][hq][hd], k/v [m][hkv][hd] (element type out_dtype)
+  void* q_out;
+  void* k_out;
+  void* v_out;
+  int out_dtype;
+  const int32_t* pos;
+  int hq, hkv, hd;
+  float theta;
+  // EPI_ARGMAX: per-row packed (value, ~index) keys merged with atomicMax; the last
+  // workgroup unpacks them into argmax/max and clears keys and the counter.
+  unsigned long long* keys;
+  float* dbg_logits;
+  int64_t ld_logits;
+  int32_t* argmax_out;
+  float* max_out;
+  int* done;
+  // EPI_TOPK: per (row, tile) the tile's top-k (value, index) and its (max, sum exp) pair
+  float* topk_val;   // [m][n_tiles][topk]
+  int32_t* topk_idx; // [m][n_tiles][topk]
+  float* lse_part;   // [m][n_tiles][2]
+  int topk;
+};
+
+struct GemmDesc {
+  const void* w0;
+  const void* w1;  // second weight block (dual = 1: tile = gate columns + matching up columns)
+  int dual;
+  int dtype;       // EAGLE_BF16: MFMA path; EAGLE_F32: VALU path
+  int n;           // output columns (rows of each weight block)
+  int k;
+  int64_t ldw;
+  int m;           // tokens
+  XSrc x;
+  Epi epi;
+  // planning (filled by plan_gemm)
+  int cfg;
+  int splits;
+  // workspace
+  float* partials;
+  float* sumsq_part;
+  int* counters;
+};
+
+struct GemmPlan {
+  int cfg;       // tile configuration
+  int splits;    // K splits
+  int tile_cols; // output columns per tile
+  int tile_rows; // weight rows per tile (both blocks when dual)
+  int mt;        // tokens per tile
+  int n_tiles, m_tiles;
+};
+
+GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int head_dim);
+// Workspace floats for partials / sum-of-squares and ints for counters of one GEMM.
+void gemm_workspace(const GemmPlan& p, size_t* partial_floats, size_t* sumsq_floats, size_t* counter_ints);
+int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s);
+
+}  // namespace eagle

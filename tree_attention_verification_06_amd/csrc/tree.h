@@ -1,0 +1,39 @@
+// Internal interface of the tree encode and accept/commit kernels.
+#pragma once
+
+#include "common.h"
+
+namespace eagle {
+
+struct AcceptArgs {
+  const int32_t* tree_off;
+  const int32_t* parent;
+  const int32_t* tokens;
+  const int32_t* argmax;
+  const uint64_t* anc;
+  int mw;
+  const int32_t* depth;
+  const void* k_tree;
+  const void* v_tree;
+  void* k_cache;
+  void* v_cache;
+  int64_t cb, ch, ct;
+  int capacity;
+  int hkv, hd, elem;
+  int32_t* prefix_len;
+  const float* h_nodes;
+  int hidden;
+  float* next_feature;
+  int max_accept;
+  int32_t* accept_len;
+  int32_t* path;
+  int32_t* out_tokens;
+  int32_t* next_token;
+  int32_t* status;
+};
+
+int launch_tree_build(int batch, const int32_t* tree_off, const int32_t* parent, const int32_t* prefix_len, int mw,
+                      uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* status, hipStream_t s);
+int launch_accept_commit(const AcceptArgs& a, int batch, hipStream_t s);
+
+}  // namespace eagle

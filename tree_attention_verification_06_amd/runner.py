@@ -1,0 +1,77 @@
+"""Convenience runner for one verification step (tree encode -> verify -> accept + commit).
+
+Allocates the per-step device buffers once for a maximum batch shape and calls the
+three C entry points in order on the current stream.  Argument marshalling only;
+all arithmetic runs in the HIP library.
+"""
+import torch
+
+from . import _abi as A
+
+
+class TreeVerifier:
+    def __init__(self, dims, weights, k_cache, v_cache, *, batch, max_total_nodes, max_nodes, max_prefix,
+                 max_accept=None, device="cuda"):
+        self.dims = dims
+        self.dstruct = A.dims_struct(dims)
+        self.lstruct = A.layer_struct(weights)
+        self.w = weights
+        self.k_cache = k_cache
+        self.v_cache = v_cache
+        self.B = batch
+        self.max_total = max_total_nodes
+        self.max_nodes = max_nodes
+        self.max_prefix = max_prefix
+        self.mw = (max_nodes + 63) // 64
+        self.max_accept = max_accept if max_accept is not None else max_nodes - 1
+        dt = torch.bfloat16 if dims.dtype == "bf16" else torch.float32
+        H, Hkv, D = dims.hidden, dims.n_kv_heads, dims.head_dim
+        M = max_total_nodes
+        z = lambda *s, dtype=torch.int32: torch.zeros(*s, dtype=dtype, device=device)  # noqa: E731
+        self.anc = z(M, self.mw, dtype=torch.int64)
+        self.depth = z(M)
+        self.pos = z(M)
+        self.k_tree = z(M, Hkv, D, dtype=dt)
+        self.v_tree = z(M, Hkv, D, dtype=dt)
+        self.h = z(M, H, dtype=torch.float32)
+        self.argmax = z(M)
+        self.maxlogit = z(M, dtype=torch.float32)
+        self.accept_len = z(batch)
+        self.path = z(batch, self.max_accept + 1)
+        self.out_tokens = z(batch, self.max_accept + 1)
+        self.next_token = z(batch)
+        self.next_feature = z(batch, H, dtype=torch.float32)
+        self.status = z(1)
+        ws = A.eagle_workspace_size(0, dims, batch, M, max_nodes, max_prefix)
+        if ws == 0:
+            raise A.EagleError(A.EAGLE_ERR_UNSUPPORTED, "eagle_workspace_size")
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        A.eagle_workspace_init(self.workspace)
+
+    def encode(self, tree_off, parent, prefix_len, total_nodes):
+        A.eagle_tree_build(tree_off, parent, prefix_len, self.mw, self.anc, self.depth, self.pos, self.status,
+                           total_nodes=total_nodes, max_nodes=self.max_nodes)
+
+    def verify(self, tree_off, tokens, prefix_len, total_nodes, x=None, embed=None, dbg_attn=None, dbg_logits=None,
+               timer=None):
+        w = self.w
+        A.eagle_tree_verify(self.dstruct, self.lstruct, w.get("final_ln"), w["w_lm"], tree_off, x,
+                            embed if embed is not None else w.get("embed") if x is None else None, tokens, self.anc,
+                            self.mw, self.pos, prefix_len, self.k_cache, self.v_cache, self.k_tree, self.v_tree,
+                            self.h, self.argmax, self.maxlogit, self.workspace, total_nodes=total_nodes,
+                            max_nodes=self.max_nodes, max_prefix=self.max_prefix, dbg_attn=dbg_attn,
+                            dbg_logits=dbg_logits, timer=timer)
+
+    def accept(self, tree_off, parent, tokens, prefix_len):
+        d = self.dims
+        A.eagle_accept_commit(tree_off, parent, tokens, self.argmax, self.anc, self.mw, self.depth, self.k_tree,
+                              self.v_tree, self.k_cache, self.v_cache, prefix_len, self.h, self.next_feature,
+                              self.accept_len, self.path, self.out_tokens, self.next_token, self.status,
+                              max_nodes=self.max_nodes, max_accept=self.max_accept, n_kv_heads=d.n_kv_heads,
+                              head_dim=d.head_dim, dtype=A.EAGLE_BF16 if d.dtype == "bf16" else A.EAGLE_F32,
+                              hidden=d.hidden)
+
+    def step(self, tree_off, parent, tokens, prefix_len, total_nodes, x=None, timer=None):
+        self.encode(tree_off, parent, prefix_len, total_nodes)
+        self.verify(tree_off, tokens, prefix_len, total_nodes, x=x, timer=timer)
+        self.accept(tree_off, parent, tokens, prefix_len)
