@@ -143,7 +143,9 @@ def main():
     t["prefix_len"].copy_(prefix0)
     torch.cuda.synchronize()
 
-    timer = None if args.no_timer else E.Timer(capacity=16 * (args.steps + 1))
+    # the timed region records HIP events around the dominant kernel (LM head) only: an
+    # event pair around every kernel would itself slow the step down
+    timer = None if args.no_timer else E.Timer(capacity=4 * (args.steps + 1), stages=["lm_head"])
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -161,6 +163,15 @@ def main():
     st = int(v.status.item())
     if st != 0:
         raise RuntimeError(f"device status {st} ({E.status_str(st)})")
+
+    # per-kernel breakdown: a separate pass with events around every kernel (diagnostic)
+    t["prefix_len"].copy_(prefix0)
+    diag = E.Timer(capacity=16 * 11)
+    for _ in range(10):
+        step(diag)
+    torch.cuda.synchronize()
+    diag_stages = diag.collect()
+    diag.close()
 
     # accepted tokens per step: the same steps again, reading accept_len after each (untimed)
     t["prefix_len"].copy_(prefix0)
@@ -227,7 +238,7 @@ def main():
         "step_roofline": {"bound": "hbm", "algorithmic_bytes": byts, "algorithmic_flops": flops,
                           "t_roof_ms": round(t_roof_ms, 5), "frac": round(t_roof_ms / ms_per_step, 4)},
         "roofline": roof,
-        "stage_ms_per_step": {k: round(ms / max(args.steps, 1), 5) for k, (ms, n) in stages.items()},
+        "stage_ms_per_step": {k: round(ms / max(n, 1), 5) for k, (ms, n) in diag_stages.items()},
     }
     if args.pmc_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

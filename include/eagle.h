@@ -247,6 +247,10 @@ void eagle_timer_destroy(eagle_timer* t);
 /* Synchronises on the recorded events, adds elapsed ms per stage into
  * ms[EAGLE_N_STAGES] and launch counts into count[EAGLE_N_STAGES], and resets. */
 int eagle_timer_collect(eagle_timer* t, double* ms, int32_t* count);
+/* Record only the stages whose bit (1 << stage) is set in stage_mask (default: all).
+ * Each recorded event pair separates two kernels on the stream, so timing every
+ * stage slows the step down; timing one stage keeps the step close to untimed. */
+int eagle_timer_select(eagle_timer* t, uint32_t stage_mask);
 #define EAGLE_N_STAGES 13
 
 const char* eagle_status_str(int status);

@@ -75,6 +75,7 @@ PROTOTYPES = {
     "eagle_timer_create": (_P, [_I]),
     "eagle_timer_destroy": (None, [_P]),
     "eagle_timer_collect": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
+    "eagle_timer_select": (_I, [_P, ctypes.c_uint32]),
     "eagle_status_str": (ctypes.c_char_p, [_I]),
     "eagle_abi_version": (_I, []),
 }
@@ -205,10 +206,15 @@ def eagle_workspace_init(workspace, stream=None):
 class Timer:
     """Per-kernel HIP event timing through eagle_timer_*."""
 
-    def __init__(self, capacity=4096):
+    def __init__(self, capacity=4096, stages=None):
         self.handle = lib().eagle_timer_create(capacity)
         if not self.handle:
             raise RuntimeError("eagle_timer_create failed")
+        if stages is not None:
+            mask = 0
+            for st in stages:
+                mask |= 1 << STAGES.index(st)
+            _check(lib().eagle_timer_select(self.handle, mask), "eagle_timer_select")
 
     def collect(self):
         ms = (ctypes.c_double * N_STAGES)()

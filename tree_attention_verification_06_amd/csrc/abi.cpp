@@ -14,6 +14,7 @@ struct eagle_timer {
   int cap = 0;
   int n = 0;
   bool open = false;
+  uint32_t mask = 0xffffffffu;
   std::vector<hipEvent_t> ev;
   std::vector<int> stage;
 };
@@ -21,7 +22,7 @@ struct eagle_timer {
 namespace eagle {
 
 void timer_begin(eagle_timer* t, int stage, hipStream_t s) {
-  if (!t || t->n >= t->cap) return;
+  if (!t || t->n >= t->cap || !((t->mask >> stage) & 1u)) return;
   hipEventRecord(t->ev[2 * t->n], s);
   t->stage[t->n] = stage;
   t->open = true;
@@ -59,6 +60,7 @@ int check_dims(const eagle_dims* d) {
 
 struct VerifyLayout {
   size_t q, attn, y, act, attn_part, gemm_part, gemm_ssq, counters, keys, done, total;
+  size_t y16, h16, ssq_y, ssq_h;  // bf16 path: gain-scaled bf16 copies and row sum-of-squares partials
   GemmPlan p_qkv, p_o, p_gu, p_down, p_lm;
   AttnPlan pa;
 };
@@ -101,6 +103,10 @@ VerifyLayout plan_verify(const eagle_dims* d, int B, int total_nodes, int max_no
   L.counters = take(ci * 4);
   L.keys = take((size_t)M * 8);
   L.done = take(4);
+  L.y16 = take((size_t)M * H * 2);
+  L.h16 = take((size_t)M * H * 2);
+  L.ssq_y = take((size_t)std::max(L.p_o.n_tiles, 1) * M * 4);
+  L.ssq_h = take((size_t)std::max(F > 0 ? L.p_down.n_tiles : L.p_o.n_tiles, 1) * M * 4);
   L.total = off;
   return L;
 }
@@ -162,6 +168,16 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
 
   // x: the given node states, or the token embeddings
   const XSeg xseg = x_in ? seg(x_in, dt, H) : seg(embed, dt, H, tokens);
+  const bool bf = dt == EAGLE_BF16;
+  void* y16 = w + L.y16;
+  void* h16 = w + L.h16;
+  float* ssq_y = (float*)(w + L.ssq_y);
+  float* ssq_h = (float*)(w + L.ssq_h);
+  auto common = [&](GemmDesc& g) {
+    g.partials = gpart;
+    g.sumsq_part = gssq;
+    g.counters = counters;
+  };
 
   // 1. RMSNorm -> QKV projection -> rotary at pos -> q (workspace), k_tree, v_tree
   {
@@ -174,7 +190,7 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     g.x.a = xseg;
     g.x.b = xseg;
     g.x.ka = H;
-    g.x.norm = norm;
+    g.x.norm = norm ? 1 : 0;
     g.x.gain = norm ? lw->ln_attn : nullptr;
     g.x.gain_dtype = dt;
     g.x.eps = d->rms_eps;
@@ -188,9 +204,7 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     g.epi.hkv = Hkv;
     g.epi.hd = D;
     g.epi.theta = d->rope_theta;
-    g.partials = gpart;
-    g.sumsq_part = gssq;
-    g.counters = counters;
+    common(g);
     timer_begin(timer, ST_QKV, s);
     rc = launch_gemm(g, L.p_qkv, s);
     timer_end(timer, s);
@@ -226,7 +240,9 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     rc = dt == EAGLE_F32 ? launch_attn_f32(a, M, timer, s) : launch_attn(a, L.pa, timer, s);
     if (rc) return rc;
   }
-  // 3. O projection + residual -> y (or h_out for the attention-only layer)
+  // 3. O projection + residual -> y (or h_out for the attention-only layer); on the bf16
+  //    path the epilogue also writes bf16(gain * y) and row sums of squares for the
+  //    next RMSNorm, so the next GEMM streams bf16 activations
   float* yout = F > 0 ? y : h_out;
   {
     GemmDesc g = base_desc(d);
@@ -241,14 +257,16 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     g.epi.kind = EPI_RESID;
     g.epi.out = yout;
     g.epi.ld_out = H;
-    // residual = x: the given rows, or the embedding rows of the node tokens
     g.epi.resid = x_in ? x_in : embed;
     g.epi.resid_idx = x_in ? nullptr : tokens;
     g.epi.resid_dtype = dt;
     g.epi.ld_resid = H;
-    g.partials = gpart;
-    g.sumsq_part = gssq;
-    g.counters = counters;
+    if (bf) {
+      g.epi.xn_out = F > 0 ? y16 : h16;
+      g.epi.xn_gain = F > 0 ? lw->ln_mlp : final_ln;
+      g.epi.ssq_out = F > 0 ? ssq_y : ssq_h;
+    }
+    common(g);
     timer_begin(timer, ST_O, s);
     rc = launch_gemm(g, L.p_o, s);
     timer_end(timer, s);
@@ -264,25 +282,30 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     g.k = H;
     g.ldw = H;
     g.m = M;
-    g.x.a = seg(y, EAGLE_F32, H);
+    if (bf) {
+      g.x.a = seg(y16, dt, H);
+      g.x.norm = 2;
+      g.x.ssq_in = ssq_y;
+      g.x.np = L.p_o.n_tiles;
+    } else {
+      g.x.a = seg(y, EAGLE_F32, H);
+      g.x.norm = 1;
+      g.x.gain = lw->ln_mlp;
+      g.x.gain_dtype = dt;
+    }
     g.x.b = g.x.a;
     g.x.ka = H;
-    g.x.norm = 1;
-    g.x.gain = lw->ln_mlp;
-    g.x.gain_dtype = dt;
     g.x.eps = d->rms_eps;
     g.epi.kind = EPI_SILU;
     g.epi.act = act;
     g.epi.act_dtype = dt;
     g.epi.ld_act = F;
-    g.partials = gpart;
-    g.sumsq_part = gssq;
-    g.counters = counters;
+    common(g);
     timer_begin(timer, ST_GATE_UP, s);
     rc = launch_gemm(g, L.p_gu, s);
     timer_end(timer, s);
     if (rc) return rc;
-    // 5. down projection + residual -> h_out
+    // 5. down projection + residual -> h_out (and bf16(final gain * h) + row sums of squares)
     GemmDesc g2 = base_desc(d);
     g2.w0 = lw->w_down;
     g2.n = H;
@@ -298,9 +321,12 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     g2.epi.resid = y;
     g2.epi.resid_dtype = EAGLE_F32;
     g2.epi.ld_resid = H;
-    g2.partials = gpart;
-    g2.sumsq_part = gssq;
-    g2.counters = counters;
+    if (bf) {
+      g2.epi.xn_out = h16;
+      g2.epi.xn_gain = final_ln;
+      g2.epi.ssq_out = ssq_h;
+    }
+    common(g2);
     timer_begin(timer, ST_DOWN, s);
     rc = launch_gemm(g2, L.p_down, s);
     timer_end(timer, s);
@@ -314,12 +340,19 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     g.k = H;
     g.ldw = H;
     g.m = M;
-    g.x.a = seg(h_out, EAGLE_F32, H);
+    if (bf) {
+      g.x.a = seg(h16, dt, H);
+      g.x.norm = norm ? 2 : 0;
+      g.x.ssq_in = ssq_h;
+      g.x.np = F > 0 ? L.p_down.n_tiles : L.p_o.n_tiles;
+    } else {
+      g.x.a = seg(h_out, EAGLE_F32, H);
+      g.x.norm = norm ? 1 : 0;
+      g.x.gain = norm ? final_ln : nullptr;
+      g.x.gain_dtype = dt;
+    }
     g.x.b = g.x.a;
     g.x.ka = H;
-    g.x.norm = norm;
-    g.x.gain = norm ? final_ln : nullptr;
-    g.x.gain_dtype = dt;
     g.x.eps = d->rms_eps;
     g.epi.kind = EPI_ARGMAX;
     g.epi.keys = keys;
@@ -328,9 +361,7 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     g.epi.argmax_out = argmax;
     g.epi.max_out = maxlogit;
     g.epi.done = done;
-    g.partials = gpart;
-    g.sumsq_part = gssq;
-    g.counters = counters;
+    common(g);
     timer_begin(timer, ST_LM_HEAD, s);
     rc = launch_gemm(g, L.p_lm, s);
     timer_end(timer, s);
@@ -405,7 +436,7 @@ int eagle_accept_commit(int32_t batch, const int32_t* tree_off, int32_t max_node
   if (n_kv_heads < 1 || head_dim < 1 || (head_dim * es) % 16) return EAGLE_ERR_UNSUPPORTED;
   if ((cache->token_stride * es) % 16 || (cache->head_stride * es) % 16 || (cache->batch_stride * es) % 16)
     return EAGLE_ERR_ARG;
-  if (next_feature && (!h_nodes || hidden < 1)) return EAGLE_ERR_ARG;
+  if (next_feature && (!h_nodes || hidden < 1 || hidden % 4)) return EAGLE_ERR_ARG;
   AcceptArgs a{};
   a.tree_off = tree_off;
   a.parent = parent;
@@ -469,6 +500,12 @@ void eagle_timer_destroy(eagle_timer* t) {
   if (!t) return;
   for (auto& e : t->ev) hipEventDestroy(e);
   delete t;
+}
+
+int eagle_timer_select(eagle_timer* t, uint32_t stage_mask) {
+  if (!t) return EAGLE_ERR_ARG;
+  t->mask = stage_mask;
+  return EAGLE_OK;
 }
 
 int eagle_timer_collect(eagle_timer* t, double* ms, int32_t* count) {

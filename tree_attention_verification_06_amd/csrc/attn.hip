@@ -29,8 +29,8 @@ namespace eagle {
 namespace {
 
 constexpr int kXcds = 8;
-constexpr int NWA = 4;                  // waves per workgroup
-constexpr int RBW = 2;                  // 16-row query blocks per wave
+constexpr int NWA = 8;                  // waves per workgroup
+constexpr int RBW = 1;                  // 16-row query blocks per wave
 constexpr int ROWS_WG = NWA * RBW * 16; // query rows per workgroup
 constexpr int KT = 64;                  // keys per LDS tile
 constexpr int HD = 128;
@@ -122,18 +122,31 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
   const bf16* vt_base = (const bf16*)a.v_tree + ((int64_t)off * a.hkv + kvh) * HD;
   const int64_t tree_stride = (int64_t)a.hkv * HD;
 
-  for (int kt0 = k0; kt0 < k1; kt0 += KT) {
-    __syncthreads();
-    for (int i = tid; i < KT * 16; i += NWA * 64) {
+  // K/V tiles go global -> registers -> LDS; the next tile's loads are issued before the
+  // current tile's math so their latency overlaps it.  Loads are unconditional (keys
+  // past the chunk are clamped to its last key and zeroed when stored).
+  constexpr int GPT = KT * 16 / (NWA * 64);  // 16-byte groups per thread per tensor
+  uint4 kreg[GPT], vreg[GPT];
+  auto load_kv = [&](int kt0) {
+#pragma unroll
+    for (int u = 0; u < GPT; ++u) {
+      const int i = tid + u * NWA * 64;
+      const int key = min(kt0 + (i >> 4), k1 - 1);
+      const int gd = i & 15;
+      const bf16* kp = tree_chunk ? kt_base + key * tree_stride : kc + key * a.ct;
+      const bf16* vp = tree_chunk ? vt_base + key * tree_stride : vc + key * a.ct;
+      kreg[u] = *(const uint4*)(kp + gd * 8);
+      vreg[u] = *(const uint4*)(vp + gd * 8);
+    }
+  };
+  auto store_kv = [&](int kt0) {
+#pragma unroll
+    for (int u = 0; u < GPT; ++u) {
+      const int i = tid + u * NWA * 64;
       const int kk = i >> 4, gd = i & 15;
-      const int key = kt0 + kk;
-      uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = make_uint4(0u, 0u, 0u, 0u);
-      if (key < k1) {
-        const bf16* kp = tree_chunk ? kt_base + key * tree_stride : kc + key * a.ct;
-        const bf16* vp = tree_chunk ? vt_base + key * tree_stride : vc + key * a.ct;
-        kv = *(const uint4*)(kp + gd * 8);
-        vv = *(const uint4*)(vp + gd * 8);
-      }
+      const bool ok = kt0 + kk < k1;
+      const uint4 kv = ok ? kreg[u] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 vv = ok ? vreg[u] : make_uint4(0u, 0u, 0u, 0u);
       *(uint4*)(ks + kk * KS + gd * 8) = kv;
       const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
@@ -142,7 +155,15 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
         vt[(gd * 8 + 2 * e + 1) * VS + kk] = (bf16)(wv[e] >> 16);
       }
     }
+  };
+
+  load_kv(k0);
+  for (int kt0 = k0; kt0 < k1; kt0 += KT) {
     __syncthreads();
+    store_kv(kt0);
+    __syncthreads();
+    load_kv(min(kt0 + KT, k1 - 1));
+    __builtin_amdgcn_sched_barrier(0);
 
     float s[RBW][4][4];
 #pragma unroll
@@ -261,18 +282,34 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int grid_re
   const int P = min(max(a.prefix_len[b], 0), a.cap);
   const int n_pref = min((P + a.kch - 1) / a.kch, a.n_chunks - 1);
   const int64_t base = (int64_t)(b * a.hkv + kvh) * a.n_chunks;
+  // chunks with data: prefix chunks 0..n_pref-1, then the tree chunk; read four at a
+  // time with clamped (unconditional) loads so the round trips overlap
+  const int cnt = n_pref + 1;
+  auto chunk_of = [&](int j) { return j < n_pref ? j : a.n_chunks - 1; };
   float M = -INFINITY;
-  for (int c = 0; c < a.n_chunks; ++c) {
-    if (c >= n_pref && c != a.n_chunks - 1) continue;
-    M = fmaxf(M, a.part_ml[((base + c) * rmax + row) * 2]);
+  for (int j0 = 0; j0 < cnt; j0 += 4) {
+    float m4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m4[u] = a.part_ml[((base + chunk_of(min(j0 + u, cnt - 1))) * rmax + row) * 2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) M = fmaxf(M, m4[u]);
   }
   float L = 0.f, O = 0.f;
-  for (int c = 0; c < a.n_chunks; ++c) {
-    if (c >= n_pref && c != a.n_chunks - 1) continue;
-    const int64_t pi = (base + c) * rmax + row;
-    const float f = exp2f(a.part_ml[pi * 2] - M);
-    L += f * a.part_ml[pi * 2 + 1];
-    O += f * a.part_o[pi * HD + d];
+  for (int j0 = 0; j0 < cnt; j0 += 4) {
+    float m4[4], l4[4], o4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t pi = (base + chunk_of(min(j0 + u, cnt - 1))) * rmax + row;
+      m4[u] = a.part_ml[pi * 2];
+      l4[u] = a.part_ml[pi * 2 + 1];
+      o4[u] = a.part_o[pi * HD + d];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float f = (j0 + u < cnt) ? exp2f(m4[u] - M) : 0.f;
+      L += f * l4[u];
+      O += f * o4[u];
+    }
   }
   const float out = O / L;
   const int node = row / g, hh = row % g;
@@ -360,16 +397,18 @@ AttnPlan plan_attn(int dtype, int batch, int hq, int hkv, int hd, int max_nodes,
     p.row_groups = 0;
     return p;
   }
-  // prefix chunks: at least 512 keys, at most 32 chunks per (b, kv head)
-  int nch = std::max(1, (max_prefix + 511) / 512);
+  // prefix chunks: enough (b, kv head, chunk, row group) workgroups to cover the CUs
+  // about twice, with at least 256 keys and at most 32 chunks per (b, kv head)
+  p.row_groups = (p.rmax + ROWS_WG - 1) / ROWS_WG;
+  const int units = std::max(1, batch * hkv * p.row_groups);
+  int nch = std::max(1, (512 + units - 1) / units);
+  nch = std::min(nch, std::max(1, (max_prefix + 255) / 256));
   nch = std::min(nch, 32);
   int kch = (max_prefix + nch - 1) / nch;
   kch = std::max(KT, (kch + KT - 1) / KT * KT);
   nch = std::max(1, (max_prefix + kch - 1) / kch);
   p.kch = kch;
   p.n_chunks = nch + 1;  // + the tree chunk
-  p.row_groups = (p.rmax + ROWS_WG - 1) / ROWS_WG;
-  (void)batch;
   (void)hd;
   return p;
 }

@@ -43,6 +43,22 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) 
   return ((unsigned long long)f2ord(v) << 32) | (unsigned long long)(0xffffffffu - idx);
 }
 
+// Cross-workgroup hand-off without whole-cache maintenance: data meant for another
+// workgroup (which may run on another XCD, with its own L2) is written and read with
+// relaxed device-scope atomic accesses (global_store/load ... sc1: coherent at device
+// scope), and the writer waits for its stores to complete before bumping the
+// device-scope counter.  A device-scope release/acquire fence would instead write back
+// and invalidate the whole L2 of the XCD (buffer_wbl2 / buffer_inv), which costs far
+// more than the few kilobytes exchanged here.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until every memory operation this thread issued has completed
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

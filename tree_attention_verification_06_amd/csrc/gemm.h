@@ -15,9 +15,13 @@ struct XSeg {
   const int32_t* idx;
 };
 
-// X = [segment a (k < ka) ; segment b (k >= ka)].  With norm != 0 the GEMM consumes
-// gain[k] * x[m][k] and the epilogue multiplies row m by rsqrt(mean_k x[m][k]^2 + eps):
-// W RMSNorm(x) = (W (gain * x)) / rms(x).
+// X = [segment a (k < ka) ; segment b (k >= ka)].  RMSNorm is applied as a per-row
+// scale in the epilogue, W RMSNorm(x) = (W (gain * x)) * rsqrt(mean_k x[m][k]^2 + eps):
+//   norm == 0: no norm;
+//   norm == 1: the GEMM stages gain[k] * x[m][k] and accumulates sum_k x^2 itself;
+//   norm == 2: X already holds gain * x (written by the producing epilogue) and the
+//              row sums of squares come as np partials ssq_in[p][m], summed in order.
+// The bf16 MFMA kernel takes bf16 segments only; the fp32 kernel takes either type.
 struct XSrc {
   XSeg a, b;
   int ka;
@@ -25,6 +29,8 @@ struct XSrc {
   int gain_dtype;
   int norm;
   float eps;
+  const float* ssq_in;
+  int np;
 };
 
 enum EpiKind { EPI_STORE_F32 = 0, EPI_QKV = 1, EPI_RESID = 2, EPI_SILU = 3, EPI_ARGMAX = 4, EPI_TOPK = 5 };
@@ -38,6 +44,11 @@ struct Epi {
   int resid_dtype;
   int64_t ld_resid;
   const int32_t* resid_idx;  // row m of the residual is row resid_idx[m] (nullptr: m)
+  // EPI_RESID extras for the next normed GEMM: xn[m][n] = bf16(xn_gain[n] * out[m][n])
+  // (xn_gain nullptr: 1) and ssq_out[tile][m] = sum over the tile's columns of out^2
+  void* xn_out;
+  const void* xn_gain;
+  float* ssq_out;
   // EPI_SILU: act[m][f] = SiLU(gate) * up, element type act_dtype
   void* act;
   int act_dtype;
@@ -76,9 +87,10 @@ struct GemmDesc {
   int m;           // tokens
   XSrc x;
   Epi epi;
-  // planning (filled by plan_gemm)
+  // planning (filled from the GemmPlan at launch)
   int cfg;
   int splits;
+  int kps;  // K range per split (multiple of the kernel's K chunk)
   // workspace
   float* partials;
   float* sumsq_part;
@@ -88,6 +100,7 @@ struct GemmDesc {
 struct GemmPlan {
   int cfg;       // tile configuration
   int splits;    // K splits
+  int kps;       // K per split
   int tile_cols; // output columns per tile
   int tile_rows; // weight rows per tile (both blocks when dual)
   int mt;        // tokens per tile

@@ -77,13 +77,16 @@ __device__ __forceinline__ void store_out(void* p, int dtype, int64_t i, float v
     ((float*)p)[i] = v;
 }
 
-// Rotary angle pos * theta^(-2j/hd): argument built in fp64 and reduced to [-pi, pi]
-// before the fp32 sincos, so positions up to 10^5 keep full fp32 accuracy.
-__device__ __forceinline__ void rope_cs(int pos, int j, int hd, float theta, float* c, float* s) {
-  const double inv = exp2(-(2.0 * j / hd) * log2((double)theta));
+// Rotary inverse frequency theta^(-2j/hd) in fp64.
+__device__ __forceinline__ double rope_inv_freq(int j, int hd, float theta) {
+  return exp2(-(2.0 * j / hd) * log2((double)theta));
+}
+// Rotary angle pos * inv_freq: built in fp64 and reduced to [-pi, pi] before the fp32
+// sincos, so positions up to 10^5 keep full fp32 accuracy.
+__device__ __forceinline__ void rope_cs(int pos, double inv, float* c, float* s) {
   const double a = (double)pos * inv;
   const double twopi = 6.283185307179586476925286766559;
-  const double r = a - rint(a / twopi) * twopi;
+  const double r = a - rint(a * (1.0 / twopi)) * twopi;
   sincosf((float)r, s, c);
 }
 
@@ -97,16 +100,53 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
   switch (e.kind) {
     case EPI_STORE_F32:
     case EPI_RESID: {
-      for (int i = tid; i < tc * mv; i += nth) {
-        const int r = i % tc, t = i / tc;
-        const int c = col0 + r;
-        if (c >= d.n) continue;
-        float v = scale[t] * tile[r * ts + t];
-        if (e.kind == EPI_RESID) {
-          const int64_t rrow = e.resid_idx ? (int64_t)e.resid_idx[m0 + t] : (int64_t)(m0 + t);
-          v += load_elem(e.resid, e.resid_dtype, rrow * e.ld_resid + c);
+      // token-major: a wave per token row, lanes along the columns (coalesced stores); the
+      // row's sum of squares over this tile is a wave reduction.  The residual loads of U
+      // rows are issued together before any use, so their round trips overlap.
+      constexpr int U = 4, CPL = 8;  // rows per batch, max columns per lane (tc <= 512)
+      const int nw = nth / 64, w = tid / 64, lane = tid % 64;
+      const int tile_i = col0 / tc;
+      const int cpl = (tc + 63) / 64;
+      float gv[CPL];
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const int c = min(col0 + lane + 64 * min(q, cpl - 1), d.n - 1);
+        gv[q] = (e.xn_out && e.xn_gain) ? bf2f(((const bf16*)e.xn_gain)[c]) : 1.f;
+      }
+      for (int t0 = w * U; t0 < mv; t0 += nw * U) {
+        float rv[U][CPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int m = m0 + min(t0 + u, mv - 1);
+          const int64_t rrow = (e.kind == EPI_RESID && e.resid_idx) ? (int64_t)e.resid_idx[m] : (int64_t)m;
+#pragma unroll
+          for (int q = 0; q < CPL; ++q) {
+            const int c = min(col0 + lane + 64 * min(q, cpl - 1), d.n - 1);
+            rv[u][q] = e.kind == EPI_RESID ? load_elem(e.resid, e.resid_dtype, rrow * e.ld_resid + c) : 0.f;
+          }
         }
-        e.out[(int64_t)(m0 + t) * e.ld_out + c] = v;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int t = t0 + u;
+          if (t >= mv) break;
+          const int m = m0 + t;
+          float ss = 0.f;
+#pragma unroll
+          for (int q = 0; q < CPL; ++q) {
+            const int r = lane + 64 * q;
+            const int c = col0 + r;
+            if (q < cpl && r < tc && c < d.n) {
+              const float v = scale[t] * tile[r * ts + t] + rv[u][q];
+              e.out[(int64_t)m * e.ld_out + c] = v;
+              ss += v * v;
+              if (e.xn_out) ((bf16*)e.xn_out)[(int64_t)m * e.ld_out + c] = f2bf(gv[q] * v);
+            }
+          }
+          if (e.ssq_out) {
+            ss = wave_sum(ss);
+            if (lane == 0) e.ssq_out[(int64_t)tile_i * d.m + m] = ss;
+          }
+        }
       }
       break;
     }
@@ -122,10 +162,15 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
       break;
     }
     case EPI_QKV: {
+      __shared__ int s_pos[128];
+      for (int t = tid; t < mv && t < 128; t += nth) s_pos[t] = e.pos ? e.pos[m0 + t] : 0;
+      __syncthreads();
       const int hd = e.hd, half = hd / 2;
       const int heads_in_tile = tc / hd;
+      // nth is a multiple of half, so every thread keeps the same pair index j
+      const int j = tid % half;
+      const double inv = e.theta > 0.f ? rope_inv_freq(j, hd, e.theta) : 0.0;
       for (int i = tid; i < mv * heads_in_tile * half; i += nth) {
-        const int j = i % half;
         const int hl = (i / half) % heads_in_tile;
         const int t = i / (half * heads_in_tile);
         const int head = col0 / hd + hl;
@@ -135,7 +180,7 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
         float b = scale[t] * tile[(hl * hd + j + half) * ts + t];
         if (head < e.hq + e.hkv && e.theta > 0.f) {
           float c, s;
-          rope_cs(e.pos[m], j, hd, e.theta, &c, &s);
+          rope_cs(s_pos[t], inv, &c, &s);
           const float ra = a * c - b * s;
           const float rb = b * c + a * s;
           a = ra;
@@ -186,16 +231,16 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
         }
         atomicMax(&e.keys[m0 + tid], b2);
       }
-      // the last workgroup of the launch unpacks the keys and clears them
+      // the last workgroup of the launch unpacks the keys and clears them (keys are
+      // only touched by device-scope atomics, so no cache maintenance is needed)
+      wait_memory();
       __syncthreads();
       if (tid == 0) {
-        __threadfence();
-        const int old = atomicAdd(e.done, 1);
+        const int old = __hip_atomic_fetch_add(e.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *s_flag = (old == n_epi - 1);
       }
       __syncthreads();
       if (*s_flag) {
-        __threadfence();
         for (int m = tid; m < d.m; m += nth) {
           const unsigned long long key = __hip_atomic_load(&e.keys[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           e.argmax_out[m] = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
@@ -254,23 +299,50 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
   }
 }
 
+// Split-K fixup: tile[e] = sum over splits (in split order) of the S partial tiles.
+// All loads of an element group are issued before the first add: the partials come
+// from other workgroups through device-coherent loads, each a full memory round trip,
+// so a load-add chain per split would serialise those round trips.
+template <int S, int ELEMS, int MT_, int TS_, int NTH_>
+__device__ __forceinline__ void sum_partials(const float* p0, float* tile) {
+  constexpr int G = 4;  // elements per thread per pass
+  for (int i0 = threadIdx.x * G; i0 < ELEMS; i0 += NTH_ * G) {
+    float a[S][G];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int g = 0; g < G; ++g) a[s][g] = coherent_load(p0 + (int64_t)s * ELEMS + i0 + g);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float v = a[0][g];
+#pragma unroll
+      for (int s = 1; s < S; ++s) v += a[s][g];
+      const int i = i0 + g;
+      tile[(i / MT_) * TS_ + (i % MT_)] = v;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------------
-template <int NW, int RB, int PD, int MT, int KC, bool DUAL>
+constexpr int KC = 512;   // K chunk staged in LDS (one 16-byte group per lane per row)
+constexpr int MT = 64;    // tokens per tile
+
+template <int NW, int RB, int PD, bool DUAL>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid_real) {
   constexpr int NT = NW * RB * 16;        // weight rows per tile (both blocks when DUAL)
   constexpr int TC = DUAL ? NT / 2 : NT;  // output columns per tile
   constexpr int NSTEP = KC / 32;
-  constexpr int XS = KC + 8;              // LDS row stride of the X chunk (bf16)
+  constexpr int XS = KC + 8;              // LDS row stride of an X chunk (bf16)
   constexpr int TS = MT + 4;              // LDS row stride of the output tile (f32)
-  constexpr int LDS_X = MT * XS * 2;
+  constexpr int LDS_X = 2 * MT * XS * 2;  // double-buffered X chunks
   constexpr int LDS_T = NT * TS * 4;
   constexpr int LDS = LDS_X > LDS_T ? LDS_X : LDS_T;
   constexpr int RPW = MT / NW;            // X rows staged per wave
   constexpr int NTH = NW * 64;
   static_assert(NSTEP % PD == 0, "prefetch depth must divide the chunk steps");
-  static_assert(MT % NW == 0 && MT % 16 == 0, "token tile");
+  static_assert(MT % NW == 0, "token tile");
 
   __shared__ __align__(16) unsigned char smem[LDS];
   __shared__ float s_scale[MT];
@@ -280,7 +352,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
 
   const int bid = remap_xcd(blockIdx.x, gridDim.x);
   if (bid >= grid_real) return;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // the wave index is wave-uniform; saying so keeps per-wave row offsets in SGPRs
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
 
   const int m_tiles = (d.m + MT - 1) / MT;
@@ -291,9 +364,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   const int nt_i = b / m_tiles;
   const int col0 = nt_i * TC, m0 = mt_i * MT;
   const int mv = min(MT, d.m - m0);
-  const int kps = (((d.k + d.splits - 1) / d.splits) + 31) & ~31;
+  const int kps = d.kps;
   const int kb = split * kps;
   const int ke = min(d.k, kb + kps);
+  const int klast = ke - 32;
+  // chunks of this K range, visited in a rotated order so that concurrently running
+  // workgroups read different columns (spreads requests over HBM channels)
+  const int nchunk = (ke - kb + KC - 1) / KC;
+  const int c0 = (nt_i * 5 + split * 3 + mt_i) % nchunk;
 
   // this wave's weight rows
   const bf16* wblk;
@@ -313,6 +391,67 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
     wp[rb] = wblk + (int64_t)row * d.ldw + lq * 8;
   }
 
+  // X rows staged by this lane: r = wid + j * NW, 8 columns at lane * 8 of each chunk
+  int64_t xrow_a[RPW], xrow_b[RPW];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int m = min(m0 + wid + j * NW, d.m - 1);
+    xrow_a[j] = (d.x.a.idx ? (int64_t)d.x.a.idx[m] : (int64_t)m) * d.x.a.ld;
+    xrow_b[j] = (d.x.b.idx ? (int64_t)d.x.b.idx[m] : (int64_t)m) * d.x.b.ld;
+  }
+  auto chunk_k = [&](int ci) {
+    int c = c0 + ci;
+    if (c >= nchunk) c -= nchunk;
+    return kb + c * KC;
+  };
+  uint4 xr[RPW];
+  uint4 gr = make_uint4(0u, 0u, 0u, 0u);  // norm == 1: the 8 gain values of this lane's columns
+  const bool stage_gain = d.x.norm == 1 && d.x.gain;
+  auto load_x = [&](int kc) {
+    const int k = min(kc + lane * 8, ke - 8);  // clamped: out-of-range lanes are zeroed at store
+    if (stage_gain) gr = *(const uint4*)((const bf16*)d.x.gain + k);
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const bool in_a = k < d.x.ka;
+      const bf16* base = in_a ? (const bf16*)d.x.a.ptr + xrow_a[j] + k : (const bf16*)d.x.b.ptr + xrow_b[j] + (k - d.x.ka);
+      xr[j] = *(const uint4*)base;
+    }
+  };
+  float ssq[RPW];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) ssq[j] = 0.f;
+  auto store_x = [&](int buf, int kc, float ssq_w) {
+    bf16* xl = (bf16*)smem + buf * (MT * XS);
+    const int k = kc + lane * 8;
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int r = wid + j * NW;
+      uint4 v = xr[j];
+      if (!(m0 + r < d.m && k < ke)) v = make_uint4(0u, 0u, 0u, 0u);
+      if (d.x.norm == 1) {
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = __uint_as_float(w4[i] << 16);
+          f[2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ssq[j] += ssq_w * f[i] * f[i];
+        if (stage_gain) {
+          const uint32_t g4[4] = {gr.x, gr.y, gr.z, gr.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f[2 * i] *= __uint_as_float(g4[i] << 16);
+            f[2 * i + 1] *= __uint_as_float(g4[i] & 0xffff0000u);
+          }
+          v = make_uint4(pack2bf(f[0], f[1]), pack2bf(f[2], f[3]), pack2bf(f[4], f[5]), pack2bf(f[6], f[7]));
+        }
+      }
+      *(uint4*)(xl + r * XS + lane * 8) = v;
+    }
+  };
+
   f32x4 acc[RB][MT / 16];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -322,51 +461,36 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   // Weight prefetch ring.  Loads are unconditional (addresses past the K range are
   // clamped to its last step): a conditional load would make the compiler wait for it
   // before merging the ring register, which serialises the stream.
-  const int klast = ke - 32;
   bf16x8_t wbuf[PD][RB];
+  {
+    const int kc = chunk_k(0);
 #pragma unroll
-  for (int s = 0; s < PD; ++s) {
-    const int k = min(kb + s * 32, klast);
+    for (int s = 0; s < PD; ++s) {
+      const int k = min(kc + s * 32, klast);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) wbuf[s][rb] = *(const bf16x8_t*)(wp[rb] + k);
-  }
-
-  float ssq[RPW];
-#pragma unroll
-  for (int j = 0; j < RPW; ++j) ssq[j] = 0.f;
-
-  bf16* xl = (bf16*)smem;
-  for (int kc = kb; kc < ke; kc += KC) {
-    __syncthreads();
-    // stage X[m0 .. m0+MT)[kc .. kc+KC) into LDS as bf16
-    const int klen = min(KC, ke - kc);
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int r = wid + j * NW;
-      const int m = m0 + r;
-      for (int g = lane; g < KC / 8; g += 64) {
-        const int k = kc + g * 8;
-        uint4 pk = make_uint4(0u, 0u, 0u, 0u);
-        if (m < d.m && g * 8 < klen) {
-          float v[8];
-          load_x8(d.x, m, k, v);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) ssq[j] += v[i] * v[i];
-          apply_gain8(d.x, k, v);
-          pk = make_uint4(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]), pack2bf(v[4], v[5]), pack2bf(v[6], v[7]));
-        }
-        *(uint4*)(xl + r * XS + g * 8) = pk;
-      }
+      for (int rb = 0; rb < RB; ++rb) wbuf[s][rb] = *(const bf16x8_t*)(wp[rb] + k);
     }
-    __syncthreads();
+    load_x(kc);
+    store_x(0, kc, 1.f);
+  }
+  __syncthreads();
+
+  for (int ci = 0; ci < nchunk; ++ci) {
+    const int kc = chunk_k(ci);
+    const bool more = ci + 1 < nchunk;
+    const int kcn = chunk_k(more ? ci + 1 : 0);
+    // next chunk's X: issued now, stored to the other buffer after this chunk's math
+    if (more) load_x(kcn);
+    const bf16* xl = (const bf16*)smem + (ci & 1) * (MT * XS);
     // Every chunk runs all NSTEP steps: past the K range X is zero in LDS, so the
-    // extra steps of a short last chunk add exact zeros (and stay branch-free).
+    // extra steps of a short chunk add exact zeros (and stay branch-free).
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       bf16x8_t cur[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) cur[rb] = wbuf[s % PD][rb];
-      const int kn = min(kc + (s + PD) * 32, klast);
+      int kn = (s + PD < NSTEP) ? kc + (s + PD) * 32 : (more ? kcn + (s + PD - NSTEP) * 32 : klast);
+      kn = min(kn, klast);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) wbuf[s % PD][rb] = *(const bf16x8_t*)(wp[rb] + kn);
       // keep the prefetch of step s + PD ahead of the math of step s (the scheduler
@@ -380,9 +504,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
           acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[rb], xf, acc[rb][t], 0, 0, 0);
       }
     }
+    if (more) store_x((ci + 1) & 1, kcn, 1.f);
+    __syncthreads();
   }
 
-  // row sums of squares of this K range
+  // row sums of squares of this K range (norm == 1)
 #pragma unroll
   for (int j = 0; j < RPW; ++j) {
     const float v = wave_sum(ssq[j]);
@@ -392,6 +518,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
 
   float* tile = (float*)smem;
   const int tile_id = nt_i * m_tiles + mt_i;
+  auto row_scale = [&](float ssq_total) -> float {
+    if (d.x.norm == 1) return rsqrtf(ssq_total / (float)d.k + d.x.eps);
+    return 1.f;
+  };
   if (d.splits == 1) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -399,37 +529,49 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
       for (int t = 0; t < MT / 16; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) tile[((wid * RB + rb) * 16 + lq * 4 + i) * TS + t * 16 + lr] = acc[rb][t][i];
-    if (tid < MT) s_scale[tid] = d.x.norm ? rsqrtf(s_ssq[tid] / (float)d.k + d.x.eps) : 1.f;
+    if (tid < MT) s_scale[tid] = row_scale(s_ssq[tid]);
   } else {
+    // split-K: publish this split's partial tile; the last split of the tile to arrive
+    // sums all partials in split order (deterministic) and runs the epilogue
     float* part = d.partials + ((int64_t)tile_id * d.splits + split) * (NT * MT);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int t = 0; t < MT / 16; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part[((wid * RB + rb) * 16 + lq * 4 + i) * MT + t * 16 + lr] = acc[rb][t][i];
-    if (tid < MT) d.sumsq_part[((int64_t)tile_id * d.splits + split) * MT + tid] = s_ssq[tid];
+        for (int i = 0; i < 4; ++i)
+          coherent_store(part + ((wid * RB + rb) * 16 + lq * 4 + i) * MT + t * 16 + lr, acc[rb][t][i]);
+    if (tid < MT) coherent_store(d.sumsq_part + ((int64_t)tile_id * d.splits + split) * MT + tid, s_ssq[tid]);
+    wait_memory();
     __syncthreads();
     if (tid == 0) {
-      __threadfence();
-      const int old = atomicAdd(&d.counters[tile_id], 1);
+      const int old = __hip_atomic_fetch_add(&d.counters[tile_id], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_flag = (old == d.splits - 1);
     }
     __syncthreads();
     if (!s_flag) return;
-    __threadfence();
     const float* p0 = d.partials + (int64_t)tile_id * d.splits * (NT * MT);
-    for (int i = tid; i < NT * MT; i += NTH) {
-      float v = 0.f;
-      for (int s = 0; s < d.splits; ++s) v += p0[(int64_t)s * NT * MT + i];
-      tile[(i / MT) * TS + (i % MT)] = v;
+    switch (d.splits) {
+      case 2: sum_partials<2, NT * MT, MT, TS, NTH>(p0, tile); break;
+      case 3: sum_partials<3, NT * MT, MT, TS, NTH>(p0, tile); break;
+      case 4: sum_partials<4, NT * MT, MT, TS, NTH>(p0, tile); break;
+      case 5: sum_partials<5, NT * MT, MT, TS, NTH>(p0, tile); break;
+      case 6: sum_partials<6, NT * MT, MT, TS, NTH>(p0, tile); break;
+      case 7: sum_partials<7, NT * MT, MT, TS, NTH>(p0, tile); break;
+      default: sum_partials<8, NT * MT, MT, TS, NTH>(p0, tile); break;
     }
     if (tid < MT) {
       float v = 0.f;
-      for (int s = 0; s < d.splits; ++s) v += d.sumsq_part[((int64_t)tile_id * d.splits + s) * MT + tid];
-      s_scale[tid] = d.x.norm ? rsqrtf(v / (float)d.k + d.x.eps) : 1.f;
+      for (int s = 0; s < d.splits; ++s) v += coherent_load(d.sumsq_part + ((int64_t)tile_id * d.splits + s) * MT + tid);
+      s_scale[tid] = row_scale(v);
     }
-    if (tid == 0) d.counters[tile_id] = 0;
+    if (tid == 0) __hip_atomic_store(&d.counters[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (d.x.norm == 2 && tid < MT) {
+    float v = 0.f;
+    const int m = min(m0 + tid, d.m - 1);
+    for (int p = 0; p < d.x.np; ++p) v += d.x.ssq_in[(int64_t)p * d.m + m];
+    s_scale[tid] = rsqrtf(v / (float)d.k + d.x.eps);
   }
   __syncthreads();
   run_epilogue(d, tile, TS, TC, col0, m0, mv, MT, s_scale, (float*)s_red, &s_flag,
@@ -509,7 +651,7 @@ constexpr CfgInfo kCfgs[4] = {{8, 4, 64}, {8, 2, 64}, {8, 1, 64}, {4, 1, 64}};
 template <int NW, int RB, int PD, bool DUAL>
 void launch_cfg(const GemmDesc& d, int grid, hipStream_t s) {
   const int padded = (grid + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((gemm_bf16_kernel<NW, RB, PD, 64, 512, DUAL>), dim3(padded), dim3(NW * 64), 0, s, d, grid);
+  hipLaunchKernelGGL((gemm_bf16_kernel<NW, RB, PD, DUAL>), dim3(padded), dim3(NW * 64), 0, s, d, grid);
 }
 
 }  // namespace
@@ -519,6 +661,7 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
   if (dtype == EAGLE_F32) {
     p.cfg = 100;
     p.splits = 1;
+    p.kps = k;
     p.tile_rows = F32_NT;
     p.tile_cols = dual ? F32_NT / 2 : F32_NT;
     p.mt = F32_MT;
@@ -526,38 +669,45 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
     p.m_tiles = (m + F32_MT - 1) / F32_MT;
     return p;
   }
-  const int mt = 64;
-  const int m_tiles = (m + mt - 1) / mt;
-  int chosen = -1;
-  for (int c = 0; c < 4; ++c) {
+  // Cost model, per CU, in bytes at the HBM rate: every workgroup needs the whole CU's
+  // LDS (double-buffered X), so workgroups run in rounds of 256.  A workgroup moves its
+  // weight slice (HBM), its X slice (L2, weighted 1/4), split-K partials (written and
+  // read back, after a device-scope release) and a fixed launch/epilogue overhead.
+  const int m_tiles = (m + MT - 1) / MT;
+  const int kchunks = (k + KC - 1) / KC;
+  double best = 1e30;
+  int best_c = -1, best_s = 1;
+  // (the 4-wave configuration keeps too few loads in flight to stream at full rate; it
+  // is kept for completeness but not planned)
+  for (int c = 0; c < 3; ++c) {
     const int nt = kCfgs[c].nw * kCfgs[c].rb * 16;
     const int tc = dual ? nt / 2 : nt;
     if (epi_kind == EPI_QKV && tc % head_dim) continue;
     const int tiles = ((n + tc - 1) / tc) * m_tiles;
-    if (tiles >= 240) {
-      chosen = c;
-      break;
+    for (int s = 1; s <= std::min(kchunks, 8); ++s) {
+      const int cps = (kchunks + s - 1) / s;  // chunks per split
+      const int se = (kchunks + cps - 1) / cps;
+      if (se != s) continue;
+      const double kps = (double)cps * KC;
+      const int G = tiles * se;
+      const int rounds = (G + 255) / 256;
+      const double per = nt * kps * 2 + 0.25 * MT * kps * 2 + (se > 1 ? nt * MT * 4.0 * 2 : 0.0) + 50e3;
+      const double cost = rounds * per;
+      if (cost < best * 0.999) {
+        best = cost;
+        best_c = c;
+        best_s = se;
+      }
     }
   }
-  int splits = 1;
-  if (chosen < 0) {
-    chosen = 2;
-    const int nt = kCfgs[chosen].nw * kCfgs[chosen].rb * 16;
-    const int tc = dual ? nt / 2 : nt;
-    const int tiles = ((n + tc - 1) / tc) * m_tiles;
-    splits = (256 + tiles - 1) / tiles;
-    splits = std::max(1, std::min(splits, k / 512));
-  }
-  p.cfg = chosen;
-  p.splits = splits;
-  p.tile_rows = kCfgs[chosen].nw * kCfgs[chosen].rb * 16;
+  p.cfg = best_c;
+  p.splits = best_s;
+  p.kps = ((kchunks + best_s - 1) / best_s) * KC;
+  p.tile_rows = kCfgs[best_c].nw * kCfgs[best_c].rb * 16;
   p.tile_cols = dual ? p.tile_rows / 2 : p.tile_rows;
-  p.mt = mt;
+  p.mt = MT;
   p.n_tiles = (n + p.tile_cols - 1) / p.tile_cols;
   p.m_tiles = m_tiles;
-  // splits must each cover >= 32 k
-  const int kps = (((k + p.splits - 1) / p.splits) + 31) & ~31;
-  p.splits = (k + kps - 1) / kps;
   return p;
 }
 
@@ -577,7 +727,9 @@ void gemm_workspace(const GemmPlan& p, size_t* partial_floats, size_t* sumsq_flo
 int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s) {
   d.cfg = p.cfg;
   d.splits = p.splits;
-  if (d.k % 32 || (d.x.ka % 8)) return EAGLE_ERR_UNSUPPORTED;
+  d.kps = p.kps;
+  if (d.k % 32 || (d.x.ka % 8) || p.cfg < 0) return EAGLE_ERR_UNSUPPORTED;
+  if (p.cfg != 100 && (d.x.a.dtype != EAGLE_BF16 || d.x.b.dtype != EAGLE_BF16)) return EAGLE_ERR_UNSUPPORTED;
   const int grid = p.n_tiles * p.m_tiles * p.splits;
   if (grid <= 0) return EAGLE_OK;
   if (p.cfg == 100) {

@@ -54,18 +54,23 @@ __global__ __launch_bounds__(128) void tree_build_kernel(const int32_t* tree_off
   }
 }
 
-// One workgroup (256 threads) per sequence.
+// One workgroup (256 threads) per sequence.  Every per-node array of the tree is read
+// into LDS in a single round of independent loads; the match / consistency / leaf /
+// path logic then runs in LDS, and all output stores and K/V copies go out together.
 __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptArgs a) {
+  constexpr int NMAX = 128;
+  __shared__ int s_tok[NMAX], s_par[NMAX], s_dep[NMAX], s_am[NMAX];
+  __shared__ uint64_t s_anc[NMAX][2];
   __shared__ uint64_t s_match[2];
   __shared__ unsigned long long s_best;
-  __shared__ int s_path[129];
+  __shared__ int s_path[NMAX + 1];
   __shared__ int s_L, s_leaf, s_P, s_ok;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int off = a.tree_off[b];
   const int N = a.tree_off[b + 1] - off;
   const int mw = a.mw;
-  if (N < 1 || N > 64 * mw) {
+  if (N < 1 || N > 64 * mw || N > NMAX) {
     if (tid == 0) {
       set_status(a.status, EAGLE_ERR_CAPACITY);
       a.accept_len[b] = -1;
@@ -73,8 +78,16 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptArgs a) {
     }
     return;
   }
+  for (int i = tid; i < N; i += blockDim.x) {
+    s_tok[i] = a.tokens[off + i];
+    s_par[i] = a.parent[off + i];
+    s_dep[i] = a.depth[off + i];
+    s_am[i] = a.argmax[off + i];
+    s_anc[i][0] = a.anc[(int64_t)(off + i) * mw];
+    s_anc[i][1] = mw > 1 ? a.anc[(int64_t)(off + i) * mw + 1] : 0ull;
+  }
+  for (int i = tid; i <= NMAX; i += blockDim.x) s_path[i] = 0;
   if (tid < 2) s_match[tid] = 0ull;
-  for (int i = tid; i < 129; i += blockDim.x) s_path[i] = 0;
   if (tid == 0) {
     s_best = 0ull;
     s_P = a.prefix_len[b];
@@ -85,19 +98,18 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptArgs a) {
   for (int i = tid; i < N; i += blockDim.x) {
     bool m = true;
     if (i > 0) {
-      const int p = a.parent[off + i];
-      m = p >= 0 && p < i && a.tokens[off + i] == a.argmax[off + p];
+      const int p = s_par[i];
+      m = p >= 0 && p < i && s_tok[i] == s_am[p];
     }
     if (m) atomicOr((unsigned long long*)&s_match[i >> 6], 1ull << (i & 63));
   }
   __syncthreads();
   // consistent nodes: every node on the root path matches; pick the deepest, lowest index
   for (int i = tid; i < N; i += blockDim.x) {
-    bool ok = true;
-    for (int w = 0; w < mw; ++w) ok = ok && ((a.anc[(int64_t)(off + i) * mw + w] & ~s_match[w]) == 0ull);
+    const bool ok = ((s_anc[i][0] & ~s_match[0]) == 0ull) && ((s_anc[i][1] & ~s_match[1]) == 0ull);
     if (ok) {
       const unsigned long long key =
-          ((unsigned long long)(uint32_t)a.depth[off + i] << 32) | (unsigned long long)(0xffffffffu - (uint32_t)i);
+          ((unsigned long long)(uint32_t)s_dep[i] << 32) | (unsigned long long)(0xffffffffu - (uint32_t)i);
       atomicMax(&s_best, key);
     }
   }
@@ -128,15 +140,15 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptArgs a) {
   // path: ancestors of the leaf have increasing index and depth, so node j on the path
   // sits at position depth[j]
   for (int j = tid; j < N; j += blockDim.x) {
-    const int dj = a.depth[off + j];
-    if (((a.anc[(int64_t)(off + leaf) * mw + (j >> 6)] >> (j & 63)) & 1ull) && dj >= 0 && dj <= L) s_path[dj] = j;
+    const int dj = s_dep[j];
+    if (((s_anc[leaf][j >> 6] >> (j & 63)) & 1ull) && dj >= 0 && dj <= L) s_path[dj] = j;
   }
   __syncthreads();
-  const int bonus = a.argmax[off + leaf];
+  const int bonus = s_am[leaf];
   for (int d = tid; d < stride; d += blockDim.x) {
     a.path[(int64_t)b * stride + d] = d <= L ? s_path[d] : -1;
     int t = -1;
-    if (d < L) t = a.tokens[off + s_path[d + 1]];
+    if (d < L) t = s_tok[s_path[d + 1]];
     else if (d == L) t = bonus;
     a.out_tokens[(int64_t)b * stride + d] = t;
   }
@@ -163,10 +175,10 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptArgs a) {
     *(uint4*)dst = *(const uint4*)src;
   }
   if (a.next_feature) {
-    for (int i = tid; i < a.hidden; i += blockDim.x)
-      a.next_feature[(int64_t)b * a.hidden + i] = a.h_nodes[(int64_t)(off + leaf) * a.hidden + i];
+    for (int i = tid * 4; i < a.hidden; i += blockDim.x * 4)
+      *(float4*)(a.next_feature + (int64_t)b * a.hidden + i) =
+          *(const float4*)(a.h_nodes + (int64_t)(off + leaf) * a.hidden + i);
   }
-  __syncthreads();
   if (tid == 0) a.prefix_len[b] = P + L + 1;
 }
 
