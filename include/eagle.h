@@ -125,7 +125,8 @@ typedef struct {
  *   pos[i] = prefix_len[b] + depth[i].
  * tree_off [B+1], parent [total_nodes], prefix_len [B] are inputs;
  * anc [total_nodes][mask_words] (uint64), depth and pos [total_nodes] outputs.
- * Host: total_nodes = tree_off[B], max_nodes >= every tree size, both host ints.
+ * Host: total_nodes >= tree_off[B] (rows past tree_off[B] are padding and are
+ * not touched), max_nodes >= every tree size, both host ints.
  * Errors: mask_words*64 < max_nodes -> EAGLE_ERR_CAPACITY (host).  A tree with
  * parent[0] != -1 or parent[i] outside [0, i) sets *dev_status = EAGLE_ERR_TREE
  * and its anc words are all zero (depth/pos then undefined). */
@@ -147,7 +148,9 @@ int eagle_tree_build(int32_t batch, const int32_t* tree_off, int32_t total_nodes
  * Inputs: x_in [total_nodes][H] (dtype) or NULL; embed [V][H] or NULL; tokens
  * [total_nodes]; anc [total_nodes][mask_words]; pos [total_nodes]; prefix_len
  * [B]; k_cache/v_cache (read only).  Host ints: total_nodes, max_nodes,
- * max_prefix >= every prefix_len[b] (bounds the work grid).
+ * max_prefix >= every prefix_len[b] (bounds the work grid).  total_nodes may
+ * exceed tree_off[B]: rows past it are padding, computed row by row and never
+ * attended to (their tokens must still be valid ids when x_in is NULL).
  * Outputs: k_tree, v_tree [total_nodes][Hkv][D] (dtype; post-rotary keys),
  * h_out [total_nodes][H] f32, argmax [total_nodes] i32, maxlogit [total_nodes] f32.
  * Optional outputs (NULL to skip): dbg_attn [total_nodes][Hq D] f32 attention
@@ -201,30 +204,57 @@ int eagle_accept_commit(int32_t batch, const int32_t* tree_off, int32_t max_node
  * candidates expanded into a tree), EAGLE vs EAGLE-2 table and FAQ Q3
  * (confidence-adaptive trees, pruning threshold).  Level-synchronous, per
  * sequence b, starting from the root (root_token[b], feature root_feature[b]):
- *   draft row of node n = W_fc [f_parent(n) ; embed[token n]] -> the draft
- *   decoder layer at position prefix_len[b] + depth(n), attending to the draft
- *   KV prefix and the expanded draft nodes on n's root path -> feature f_hat(n);
- *   log p = log_softmax(W_lm RMSNorm(f_hat(n))) over the vocabulary; the top_k
- *   tokens (ties: lower id) become children with
+ *   draft row of node n = W_fc [f_parent(n) ; embed[token n]] (f_parent of the
+ *   root = root_feature[b]) -> the draft decoder layer at position
+ *   prefix_len[b] + depth(n), attending to the draft KV prefix and the expanded
+ *   draft nodes on n's root path (itself included) -> feature f_hat(n);
+ *   log p = log_softmax(W_lm RMSNorm_final(f_hat(n))) over the vocabulary; the
+ *   top_k tokens (ties: lower id) become children with
  *   cum = cum(n) + min(0, log p) (cum(root) = 0);
- *   children with p >= conf_threshold are expandable; the next level expands
- *   the `frontier` best expandable children by (cum desc, depth asc, generation
+ *   children with log p >= log(conf_threshold) are expandable; the next level
+ *   expands the `frontier` best expandable children by (cum desc, generation
  *   order asc), generation order = (level, parent rank, child rank).
- * After `depth` levels the tree is the root plus the best max_nodes-1 generated
- * nodes by the same key, re-indexed by (depth asc, cum desc, generation order).
+ * After `depth` levels the tree is the root plus the best max_nodes-1 candidates
+ * by (cum desc, depth asc, generation order asc), re-indexed by (depth asc, cum
+ * desc, generation order asc); cum never grows along a path, so the kept set
+ * contains every kept node's parent.
+ * Weights: w_fc [H][2H] (feature columns first), draft_layer (all seven
+ * tensors), the target's final_ln [H] and w_lm [V][H], embed [V][H]; all bf16.
  * Inputs: root_feature [B][H] f32, root_token [B], dk_cache/dv_cache (the draft
- * layer's own KV prefix, read only), prefix_len [B]; host int max_prefix.
+ * layer's own KV prefix, post-rotary keys, read only), prefix_len [B]; host int
+ * max_prefix >= every prefix_len[b].
  * Outputs: tree_off [B+1]; parent, tokens [B*max_nodes] i32 and cum_logp
- * [B*max_nodes] f32, tree b stored at tree_off[b] (trees are compacted; a tree
- * is smaller than max_nodes only when pruning leaves fewer nodes).
- * Supported: dtype bf16. */
+ * [B*max_nodes] f32.  Tree b occupies [tree_off[b], tree_off[b+1]) with local
+ * parent indices (root first, parent -1).  A tree has fewer than max_nodes nodes
+ * only when pruning leaves fewer candidates; entries from tree_off[B] up to
+ * B*max_nodes are then padding (parent -1, token 0, cum -inf), so the arrays can
+ * go straight into eagle_tree_verify with total_nodes = B*max_nodes and no
+ * host synchronisation (padding rows are computed and ignored).
+ * Supported: dtype bf16, head_dim 128, a normed layer (ffn > 0, rms_eps > 0),
+ * top_k and frontier in 1..16, 1 + (depth-1)*frontier <= 64,
+ * 1 + top_k + (depth-1)*frontier*top_k <= 2048, frontier*top_k <= 256.
+ * The workspace (eagle_workspace_size(1, ...)) must be zero-filled once
+ * (eagle_workspace_init) and not shared with a concurrent call. */
 int eagle_draft_expand(const eagle_dims* dims, const eagle_draft_params* params, const void* w_fc,
                        const eagle_layer_w* draft_layer, const void* final_ln, const void* w_lm,
                        const void* embed, int32_t batch, const float* root_feature, const int32_t* root_token,
                        const void* dk_cache, const void* dv_cache, const eagle_cache_layout* cache,
                        const int32_t* prefix_len, int32_t max_prefix, int32_t* tree_off, int32_t* parent,
                        int32_t* tokens, float* cum_logp, void* workspace, size_t ws_bytes,
-                       eagle_timer* timer, int32_t* dev_status, void* stream);
+                       eagle_timer* timer, void* stream);
+
+/* Candidate pool of the last eagle_draft_expand that used this workspace (same
+ * dims, params, batch, max_prefix), for inspection.  Per sequence b, with
+ * P = 1 + top_k + (depth-1)*frontier*top_k: pool_n[b] candidates in generation
+ * order (root first, then each level's children by parent frontier rank and
+ * child rank); token, parent (pool index, -1 for the root), depth [B][P] i32,
+ * cum_logp and logp (the child's own log-probability; 0 for the root) [B][P]
+ * f32, entries past pool_n[b] are -1 / -inf; expanded [B][depth][frontier] i32
+ * = pool indices expanded on each level (-1 padded).  Any output may be NULL. */
+int eagle_draft_pool(const eagle_dims* dims, const eagle_draft_params* params, int32_t batch,
+                     int32_t max_prefix, const void* workspace, size_t ws_bytes, int32_t* pool_n,
+                     int32_t* token, int32_t* parent, int32_t* depth, float* cum_logp, float* logp,
+                     int32_t* expanded, void* stream);
 
 /* ---- workspace -------------------------------------------------------------
  * Bytes of workspace a call needs.  which: 0 = eagle_tree_verify, 1 =

@@ -74,9 +74,16 @@ def draft_rerank(pool, max_nodes):
 
 
 def draft_expand(dims, params, weights, dweights, root_feature, root_token, dk_cache, dv_cache, prefix_len,
-                 *, trace=False):
+                 *, trace=False, force=None):
     """Expand one draft tree per sequence.  Returns a list of per-sequence dicts
-    (parent, tokens, cum, and with ``trace`` the pool and per-level records)."""
+    (parent, tokens, cum, and with ``trace`` the pool and per-level records).
+
+    ``force`` (teacher forcing, for checking another implementation's decisions):
+    a per-sequence list of dicts with ``tokens[level]`` = the children tokens of
+    each expanded row and ``frontier[level]`` = the pool ids expanded on that
+    level (level >= 2).  The oracle then takes those decisions instead of its own
+    top-k and selection; every value (features, log-probabilities, cum) is still
+    its own, and the trace records its own top-k and selection beside them."""
     H, Hkv, D = dims.hidden, dims.n_kv_heads, dims.head_dim
     E = weights["embed"]
     out = []
@@ -115,12 +122,17 @@ def draft_expand(dims, params, weights, dweights, root_feature, root_token, dk_c
             res = layer_rows(dims, dweights, rows, pos, k_pre, v_pre, proc_k, proc_v, vis)
             proc_k = np.concatenate([proc_k, res["k"]])
             proc_v = np.concatenate([proc_v, res["v"]])
-            logp = log_softmax(lm_head_logits(dims, weights, res["h"]))
+            z = lm_head_logits(dims, weights, res["h"])
+            logp = log_softmax(z)
+            fb = force[b] if force is not None else None
             children = []
             tops = []
+            own_tops = []
             for r, n in enumerate(frontier):
                 fhat[n] = res["h"][r]
-                top = topk_stable(logp[r], params.top_k)
+                own = topk_stable(logp[r], params.top_k + 1)
+                own_tops.append((own, logp[r][own]))
+                top = own[: params.top_k] if fb is None else np.asarray(fb["tokens"][level][r])
                 tops.append(top)
                 for c, t in enumerate(top):
                     children.append(dict(token=int(t), parent=n, depth=pool[n]["depth"] + 1,
@@ -129,11 +141,15 @@ def draft_expand(dims, params, weights, dweights, root_feature, root_token, dk_c
             base = len(pool)
             pool.extend(children)
             sel = draft_select_level(children, params.frontier, params.conf_threshold)
+            nxt = [base + i for i in sel]
             if trace:
-                levels.append(dict(frontier=list(frontier), rows=rows, fhat=res["h"], logp_top=[lp[t] for lp, t in zip(logp, tops)],
-                                   tops=tops, logp=logp, children=list(range(base, len(pool))),
-                                   next=[base + i for i in sel]))
-            frontier = [base + i for i in sel]
+                levels.append(dict(frontier=list(frontier), rows=rows, fhat=res["h"],
+                                   logp_top=[lp[t] for lp, t in zip(logp, tops)], tops=tops, own_tops=own_tops,
+                                   zscale=np.abs(z).max(axis=1),
+                                   children=list(range(base, len(pool))), next=nxt))
+            if fb is not None:
+                nxt = list(fb["frontier"].get(level + 1, []))
+            frontier = nxt
         parent, tokens, cum, order = draft_rerank(pool, params.max_nodes)
         rec = dict(parent=parent, tokens=tokens, cum=cum)
         if trace:

@@ -1,0 +1,191 @@
+"""GPU parity of the draft-head tree expansion and of the full speculative step.
+
+The draft takes discrete decisions from floating point (top-k tokens, frontier,
+rerank), so the comparison is split:
+  * teacher forcing: the oracle follows the GPU's decisions and computes every value
+    itself; log-probabilities and cumulative scores agree within the bf16 tolerance,
+    and the GPU's children are the oracle's own top-k wherever its ranking is decisive;
+  * the GPU's selection, pruning and rerank are replayed exactly (bit for bit) from the
+    GPU's own fp32 values with the oracle's definitions.
+"""
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from tests._gpu import (GAP_BF16, TOL_BF16, check_draft_numerics, check_draft_structure, check_verify,
+                        gpu_draft_outputs, np_of, rel_err)
+from workloads import DraftParams, make_workload
+from workloads.configs import with_trees
+from workloads.bf16 import bf16_bits_to_f32, f32_to_bf16_bits
+from workloads.configs import mini_dims
+from workloads.device import upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def _mini(seed, B, prefix, params, lm_scale):
+    wl = make_workload(5, seed=seed, dims=mini_dims(), batch=B, prefix=prefix, draft=params)
+    # a power-of-two scale is exact in bf16; it sets how peaked the draft distribution is
+    wl.weights["w_lm"] = f32_to_bf16_bits(bf16_bits_to_f32(wl.weights["w_lm"]) * lm_scale)
+    return wl
+
+
+def _drafter(wl, t):
+    from tree_attention_verification_06_amd.runner import TreeDrafter
+    return TreeDrafter(wl.dims, wl.draft, t["weights"], t["draft_weights"], t["dk_cache"], t["dv_cache"],
+                       batch=wl.batch, max_prefix=int(wl.prefix_len.max()))
+
+
+def _draft(wl):
+    t = upload(wl)
+    d = _drafter(wl, t)
+    d.expand(t["root_feature"], t["root_token"], t["prefix_len"])
+    tree, pool = gpu_draft_outputs(d)
+    return t, d, tree, pool
+
+
+CASES = [
+    # (seed, B, prefix, params, lm scale): peaked full trees; near-uniform draft with many
+    # near-ties; pruning at 0.3 that leaves short trees (padded outputs); a wide frontier
+    (11, 3, [37, 100, 0], DraftParams(depth=4, top_k=4, frontier=3, max_nodes=16), 16),
+    (12, 2, [64, 5], DraftParams(depth=3, top_k=5, frontier=4, max_nodes=20), 1),
+    (11, 3, [37, 100, 0], DraftParams(depth=4, top_k=4, frontier=3, max_nodes=16, conf_threshold=0.3), 8),
+    (13, 2, [130, 257], DraftParams(depth=6, top_k=10, frontier=10, max_nodes=60), 16),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_draft_mini_teacher_forced(case):
+    seed, B, prefix, params, scale = CASES[case]
+    _log(f"draft case {case}: B={B} prefix={prefix} {params} lm_scale={scale}")
+    wl = _mini(seed, B, prefix, params, scale)
+    t, d, tree, pool = _draft(wl)
+    check_draft_structure(tree, pool, params, B)
+    _, frac = check_draft_numerics(wl, params, pool, range(B), label=f"case {case}")
+    assert frac > 0.1  # enough decisive ranks for the top-k check to bite
+
+
+def test_draft_pruned_trees_are_short_and_padded():
+    seed, B, prefix, params, scale = CASES[2]
+    wl = _mini(seed, B, prefix, params, scale)
+    t, d, tree, pool = _draft(wl)
+    sizes = np.diff(tree["tree_off"])
+    assert sizes.min() < params.max_nodes, sizes
+    assert tree["tree_off"][-1] < B * params.max_nodes
+
+
+def test_draft_is_deterministic_and_reusable():
+    """Two expansions with the same workspace give identical trees (bitwise)."""
+    seed, B, prefix, params, scale = CASES[0]
+    wl = _mini(seed, B, prefix, params, scale)
+    t, d, tree, pool = _draft(wl)
+    d.expand(t["root_feature"], t["root_token"], t["prefix_len"])
+    tree2, pool2 = gpu_draft_outputs(d)
+    for k in tree:
+        assert np.array_equal(tree[k], tree2[k]), k
+    for k in pool:
+        assert np.array_equal(pool[k], pool2[k]), k
+
+
+def test_draft_unsupported_params_rejected():
+    from tree_attention_verification_06_amd import EagleError, eagle_workspace_size
+    dims = mini_dims()
+    for p in [DraftParams(depth=8, top_k=4, frontier=10, max_nodes=16),   # 71 expanded nodes > 64
+              DraftParams(depth=3, top_k=17, frontier=3, max_nodes=16),   # top_k > 16
+              DraftParams(depth=3, top_k=4, frontier=0, max_nodes=16),    # unbounded frontier
+              DraftParams(depth=3, top_k=4, frontier=3, max_nodes=200)]:  # tree too large
+        assert eagle_workspace_size(1, dims, 2, 0, 0, 64, p) == 0
+    wl = _mini(11, 1, [8], DraftParams(depth=2, top_k=2, frontier=2, max_nodes=4), 1)
+    t = upload(wl)
+    d = _drafter(wl, t)
+    bad = DraftParams(depth=2, top_k=2, frontier=2, max_nodes=4, conf_threshold=1.5)
+    from tree_attention_verification_06_amd import _abi as A
+    with pytest.raises(EagleError):
+        A.eagle_draft_expand(d.dstruct, bad, d.dw["w_fc"], d.lstruct, d.w["final_ln"], d.w["w_lm"], d.w["embed"],
+                             t["root_feature"], t["root_token"], d.dk_cache, d.dv_cache, t["prefix_len"],
+                             d.tree_off, d.parent, d.tokens, d.cum, d.workspace, max_prefix=d.max_prefix)
+
+
+def _step_check(wl, seqs, label):
+    """Full step on the GPU (draft -> encode -> verify -> accept + commit, no host sync), then
+    the oracle's verification of the GPU-drafted trees of sequences ``seqs``."""
+    import torch
+    from tree_attention_verification_06_amd.runner import EagleStep
+    t = upload(wl)
+    k_before = wl.k_cache.copy()
+    st = EagleStep(wl.dims, wl.draft, t["weights"], t["draft_weights"], t["k_cache"], t["v_cache"], t["dk_cache"],
+                   t["dv_cache"], batch=wl.batch, max_prefix=int(wl.prefix_len.max()))
+    st.step(t["root_feature"], t["root_token"], t["prefix_len"])
+    torch.cuda.synchronize()
+    d, v = st.drafter, st.verifier
+    tree, pool = gpu_draft_outputs(d)
+    check_draft_structure(tree, pool, wl.draft, wl.batch)
+    off = tree["tree_off"]
+    parents = [tree["parent"][off[b]:off[b + 1]].tolist() for b in range(wl.batch)]
+    toks = np.concatenate([tree["tokens"][off[b]:off[b + 1]] for b in range(wl.batch)])
+    sel = list(seqs)
+    sub = with_trees(wl, [parents[b] for b in sel], tokens=np.concatenate([toks[off[b]:off[b + 1]] for b in sel]))
+    sub.prefix_len = wl.prefix_len[sel]
+    sub.k_cache = k_before[sel]
+    sub.v_cache = wl.v_cache[sel]
+    sub.batch = len(sel)
+    ref = oracle.verify_forward(sub.dims, sub.weights, None, sub.parents, sub.prefix_len, sub.k_cache, sub.v_cache,
+                                embed_tokens=sub.tokens, want_logits=False)
+    rows = np.concatenate([np.arange(off[b], off[b + 1]) for b in sel])
+    g = dict(k_tree=np_of(v.k_tree)[rows], v_tree=np_of(v.v_tree)[rows], h=np_of(v.h)[rows],
+             argmax=np_of(v.argmax)[rows], maxlogit=np_of(v.maxlogit)[rows])
+    tl = TOL_BF16
+    errs = {k: rel_err(g[k], ref[kk]) for k, kk in [("k_tree", "k_tree"), ("v_tree", "v_tree"), ("h", "h"),
+                                                    ("maxlogit", "maxlogit")]}
+    _log(label, "verify max rel err", {k: f"{e:.2e}" for k, e in errs.items()})
+    assert all(e <= tl for e in errs.values()), errs
+    decisive = ref["gap"] > GAP_BF16
+    assert not np.any(decisive & (g["argmax"] != ref["argmax"]))
+    # acceptance on the GPU's own argmax (every sequence), and the committed K/V
+    am = np_of(v.argmax)
+    acc = v.accept_len.cpu().numpy()
+    kc = np_of(t["k_cache"])
+    plen = t["prefix_len"].cpu().numpy()
+    for b in range(wl.batch):
+        o, n = off[b], off[b + 1] - off[b]
+        depth = np.zeros(n, dtype=int)
+        for i in range(1, n):
+            depth[i] = depth[parents[b][i]] + 1
+        L, path, *_ = oracle.accept_sequence(parents[b], tree["tokens"][o:o + n], am[o:o + n], depth)
+        assert acc[b] == L
+        assert plen[b] == wl.prefix_len[b] + L + 1
+        kt = np_of(v.k_tree)
+        for dd, node in enumerate(path):
+            assert np.array_equal(kc[b, :, wl.prefix_len[b] + dd], kt[o + node])
+    return acc
+
+
+def test_full_step_mini_with_pruning():
+    """Pruned (short, padded) trees flow straight into verify with total_nodes = B * max_nodes."""
+    seed, B, prefix, params, scale = CASES[2]
+    wl = _mini(seed, B, prefix, params, scale)
+    _step_check(wl, range(B), "mini step")
+
+
+def test_full_eagle_step_llama8b_b16():
+    """Full EAGLE step at the 8B shape, batch 16, prefix 2048, depth 6, top-10, 60-node trees.
+    The GPU runs all 16 sequences; the oracle (teacher-forced draft and verification) checks a
+    sample of them one by one; selection, rerank and acceptance are checked on all 16."""
+    t0 = time.time()
+    wl = make_workload(5)
+    _log(f"cfg {wl.name}: generated in {time.time() - t0:.1f}s")
+    sample = [0, 9]
+    acc = _step_check(wl, sample, wl.name)
+    _log(f"  step checked {time.time() - t0:.1f}s, accept lengths {acc.tolist()}")
+    # teacher-forced draft numerics on the sample (re-drafts: the step consumed prefix_len)
+    t, d, tree, pool = _draft(wl)
+    check_draft_structure(tree, pool, wl.draft, wl.batch)
+    assert (np.diff(tree["tree_off"]) == wl.draft.max_nodes).all()
+    check_draft_numerics(wl, wl.draft, pool, sample, label=wl.name)
+    _log(f"  draft checked {time.time() - t0:.1f}s")

@@ -150,3 +150,26 @@ def test_rerank_brute_force():
     for a, b in itertools.combinations(range(1, 8), 2):
         da, db = pool[order[a]]["depth"], pool[order[b]]["depth"]
         assert da < db or (da == db and cum[a] >= cum[b])
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.2])
+def test_forcing_own_decisions_reproduces_free_run(tau):
+    """Teacher forcing with the oracle's own top-k and frontier choices changes nothing."""
+    wl = _wl(4)
+    params = DraftParams(depth=4, top_k=3, frontier=2, max_nodes=9, conf_threshold=tau)
+    free = _run(wl, params, trace=True)
+    force = []
+    for r in free:
+        pool = r["pool"]
+        f = dict(tokens={}, frontier={})
+        for lvl, lv in enumerate(r["levels"], start=1):
+            f["tokens"][lvl] = [[pool[c]["token"] for c in lv["children"] if pool[c]["parent"] == n]
+                                for n in lv["frontier"]]
+            if lvl >= 2:
+                f["frontier"][lvl] = list(lv["frontier"])
+        force.append(f)
+    forced = draft_expand(wl.dims, params, wl.weights, wl.draft_weights, wl.root_feature, wl.root_token,
+                          wl.dk_cache, wl.dv_cache, wl.prefix_len, trace=True, force=force)
+    for a, b in zip(free, forced):
+        assert a["parent"] == b["parent"] and a["tokens"] == b["tokens"] and a["cum"] == b["cum"]
+        assert [c["token"] for c in a["pool"]] == [c["token"] for c in b["pool"]]

@@ -69,7 +69,9 @@ PROTOTYPES = {
                                  _P, _P]),
     "eagle_draft_expand": (_I, [ctypes.POINTER(EagleDims), ctypes.POINTER(EagleDraftParams), _P,
                                 ctypes.POINTER(EagleLayerW), _P, _P, _P, _I, _P, _P, _P, _P,
-                                ctypes.POINTER(EagleCacheLayout), _P, _I, _P, _P, _P, _P, _P, _S, _P, _P, _P]),
+                                ctypes.POINTER(EagleCacheLayout), _P, _I, _P, _P, _P, _P, _P, _S, _P, _P]),
+    "eagle_draft_pool": (_I, [ctypes.POINTER(EagleDims), ctypes.POINTER(EagleDraftParams), _I, _I, _P, _S, _P, _P,
+                              _P, _P, _P, _P, _P, _P]),
     "eagle_workspace_size": (_S, [_I, ctypes.POINTER(EagleDims), _I, _I, _I, _I, ctypes.POINTER(EagleDraftParams)]),
     "eagle_workspace_init": (_I, [_P, _S, _P]),
     "eagle_timer_create": (_P, [_I]),
@@ -139,6 +141,13 @@ def cache_struct(cache):
     return EagleCacheLayout(s[0], s[1], s[2], cap)
 
 
+def draft_params_struct(p):
+    """EagleDraftParams from any object with depth, top_k, frontier, max_nodes, conf_threshold."""
+    if isinstance(p, EagleDraftParams):
+        return p
+    return EagleDraftParams(int(p.depth), int(p.top_k), int(p.frontier), int(p.max_nodes), float(p.conf_threshold))
+
+
 def eagle_tree_build(tree_off, parent, prefix_len, mask_words, anc, depth, pos, dev_status=None, *,
                      total_nodes, max_nodes, stream=None):
     B = tree_off.numel() - 1
@@ -177,23 +186,34 @@ def eagle_accept_commit(tree_off, parent, tokens, argmax, anc, mask_words, depth
 
 
 def eagle_draft_expand(dims, params, w_fc, draft_layer, final_ln, w_lm, embed, root_feature, root_token, dk_cache,
-                       dv_cache, prefix_len, tree_off, parent, tokens, cum_logp, workspace, dev_status=None, *,
-                       max_prefix, timer=None, stream=None):
+                       dv_cache, prefix_len, tree_off, parent, tokens, cum_logp, workspace, *, max_prefix,
+                       timer=None, stream=None):
     d = dims_struct(dims) if not isinstance(dims, EagleDims) else dims
     lw = layer_struct(draft_layer) if not isinstance(draft_layer, EagleLayerW) else draft_layer
     cl = cache_struct(dk_cache)
     B = root_token.numel()
+    params = draft_params_struct(params)
     st = lib().eagle_draft_expand(ctypes.byref(d), ctypes.byref(params), _p(w_fc), ctypes.byref(lw), _p(final_ln),
                                   _p(w_lm), _p(embed), B, _p(root_feature), _p(root_token), _p(dk_cache),
                                   _p(dv_cache), ctypes.byref(cl), _p(prefix_len), max_prefix, _p(tree_off),
                                   _p(parent), _p(tokens), _p(cum_logp), _p(workspace),
-                                  workspace.numel() * workspace.element_size(), _t(timer), _p(dev_status),
-                                  _stream(stream))
+                                  workspace.numel() * workspace.element_size(), _t(timer), _stream(stream))
     _check(st, "eagle_draft_expand")
+
+
+def eagle_draft_pool(dims, params, batch, max_prefix, workspace, pool_n=None, token=None, parent=None, depth=None,
+                     cum_logp=None, logp=None, expanded=None, *, stream=None):
+    d = dims_struct(dims) if not isinstance(dims, EagleDims) else dims
+    params = draft_params_struct(params)
+    st = lib().eagle_draft_pool(ctypes.byref(d), ctypes.byref(params), batch, max_prefix, _p(workspace),
+                                workspace.numel() * workspace.element_size(), _p(pool_n), _p(token), _p(parent),
+                                _p(depth), _p(cum_logp), _p(logp), _p(expanded), _stream(stream))
+    _check(st, "eagle_draft_pool")
 
 
 def eagle_workspace_size(which, dims, batch, total_nodes, max_nodes, max_prefix, params=None):
     d = dims_struct(dims) if not isinstance(dims, EagleDims) else dims
+    params = draft_params_struct(params) if params is not None else None
     return int(lib().eagle_workspace_size(which, ctypes.byref(d), batch, total_nodes, max_nodes, max_prefix,
                                           ctypes.byref(params) if params is not None else None))
 

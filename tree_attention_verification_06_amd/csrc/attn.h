@@ -19,7 +19,14 @@ struct AttnArgs {
   int mw;
   const int32_t* tree_off;
   const int32_t* prefix_len;
-  int max_nodes, max_prefix;
+  int max_nodes, max_prefix;  // max_nodes bounds the query nodes of a sequence
+  // Optional query subset (draft levels): sequence b has n_nodes[b] key nodes starting at
+  // tree_off[b]; only nodes q_lo[b] .. n_nodes[b]-1 are queries, and their q / output rows
+  // are b * q_stride + (node - q_lo[b]).  nullptr / 0: every node is a query and its row is
+  // tree_off[b] + node, with n_nodes = tree_off[b+1] - tree_off[b].
+  const int32_t* n_nodes;
+  const int32_t* q_lo;
+  int q_stride;
   void* out;             // [sum N][hq * hd] (dtype)
   float* dbg;            // optional [sum N][hq * hd] f32
   // split-KV plan and partials (bf16 path)

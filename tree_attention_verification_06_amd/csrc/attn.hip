@@ -57,11 +57,12 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
   const int b = t / a.hkv;
 
   const int off = a.tree_off[b];
-  const int N = a.tree_off[b + 1] - off;
+  const int N = a.n_nodes ? a.n_nodes[b] : a.tree_off[b + 1] - off;
+  const int qlo = a.q_lo ? a.q_lo[b] : 0;
   const int g = a.hq / a.hkv;
-  const int R = N * g;
+  const int R = (N - qlo) * g;
   const int row_base = rg * ROWS_WG;
-  if (row_base >= R || N > a.max_nodes) return;
+  if (row_base >= R || N - qlo > a.max_nodes || N > 64 * a.mw) return;
   const int P = min(max(a.prefix_len[b], 0), a.cap);
   const bool tree_chunk = (c == a.n_chunks - 1);
   int k0, k1;
@@ -90,8 +91,9 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
     vis0[j] = ~0ull;
     vis1[j] = ~0ull;
     if (row < R) {
-      const int node = row / g, hh = row % g;
-      const bf16* qp = q + ((int64_t)(off + node) * a.hq + kvh * g + hh) * HD;
+      const int node = qlo + row / g, hh = row % g;
+      const int64_t qrow = a.q_stride ? (int64_t)b * a.q_stride + (node - qlo) : (int64_t)(off + node);
+      const bf16* qp = q + (qrow * a.hq + kvh * g + hh) * HD;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) qf[j][kk] = *(const bf16x8_t*)(qp + kk * 32 + lq * 8);
       if (tree_chunk) {
@@ -275,10 +277,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int grid_re
   const int kvh = t % a.hkv;
   const int b = t / a.hkv;
   const int off = a.tree_off[b];
-  const int N = a.tree_off[b + 1] - off;
+  const int N = a.n_nodes ? a.n_nodes[b] : a.tree_off[b + 1] - off;
+  const int qlo = a.q_lo ? a.q_lo[b] : 0;
   const int row = rp * 2 + threadIdx.x / HD;
   const int d = threadIdx.x % HD;
-  if (row >= N * g || N > a.max_nodes) return;
+  if (row >= (N - qlo) * g || N - qlo > a.max_nodes || N > 64 * a.mw) return;
   const int P = min(max(a.prefix_len[b], 0), a.cap);
   const int n_pref = min((P + a.kch - 1) / a.kch, a.n_chunks - 1);
   const int64_t base = (int64_t)(b * a.hkv + kvh) * a.n_chunks;
@@ -312,8 +315,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int grid_re
     }
   }
   const float out = O / L;
-  const int node = row / g, hh = row % g;
-  const int64_t oi = (int64_t)(off + node) * a.hq * HD + (int64_t)(kvh * g + hh) * HD + d;
+  const int node = qlo + row / g, hh = row % g;
+  const int64_t orow = a.q_stride ? (int64_t)b * a.q_stride + (node - qlo) : (int64_t)(off + node);
+  const int64_t oi = orow * a.hq * HD + (int64_t)(kvh * g + hh) * HD + d;
   ((bf16*)a.out)[oi] = f2bf(out);
   if (a.dbg) a.dbg[oi] = out;
 }

@@ -59,6 +59,7 @@ struct Epi {
   void* v_out;
   int out_dtype;
   const int32_t* pos;
+  const int32_t* kv_idx;  // k/v of row m go to row kv_idx[m] (< 0: dropped); nullptr: row m
   int hq, hkv, hd;
   float theta;
   // EPI_ARGMAX: per-row packed (value, ~index) keys merged with atomicMax; the last

@@ -122,7 +122,7 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
 #pragma unroll
           for (int q = 0; q < CPL; ++q) {
             const int c = min(col0 + lane + 64 * min(q, cpl - 1), d.n - 1);
-            rv[u][q] = e.kind == EPI_RESID ? load_elem(e.resid, e.resid_dtype, rrow * e.ld_resid + c) : 0.f;
+            rv[u][q] = (e.kind == EPI_RESID && e.resid) ? load_elem(e.resid, e.resid_dtype, rrow * e.ld_resid + c) : 0.f;
           }
         }
 #pragma unroll
@@ -162,8 +162,11 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
       break;
     }
     case EPI_QKV: {
-      __shared__ int s_pos[128];
-      for (int t = tid; t < mv && t < 128; t += nth) s_pos[t] = e.pos ? e.pos[m0 + t] : 0;
+      __shared__ int s_pos[128], s_kvrow[128];
+      for (int t = tid; t < mv && t < 128; t += nth) {
+        s_pos[t] = e.pos ? e.pos[m0 + t] : 0;
+        s_kvrow[t] = e.kv_idx ? e.kv_idx[m0 + t] : m0 + t;
+      }
       __syncthreads();
       const int hd = e.hd, half = hd / 2;
       const int heads_in_tile = tc / hd;
@@ -192,11 +195,13 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
           dst = e.q_out;
           base = ((int64_t)m * e.hq + head) * hd;
         } else if (head < e.hq + e.hkv) {
+          if (s_kvrow[t] < 0) continue;
           dst = e.k_out;
-          base = ((int64_t)m * e.hkv + (head - e.hq)) * hd;
+          base = ((int64_t)s_kvrow[t] * e.hkv + (head - e.hq)) * hd;
         } else {
+          if (s_kvrow[t] < 0) continue;
           dst = e.v_out;
-          base = ((int64_t)m * e.hkv + (head - e.hq - e.hkv)) * hd;
+          base = ((int64_t)s_kvrow[t] * e.hkv + (head - e.hq - e.hkv)) * hd;
         }
         store_out(dst, e.out_dtype, base + j, a);
         store_out(dst, e.out_dtype, base + j + half, b);

@@ -75,3 +75,85 @@ class TreeVerifier:
         self.encode(tree_off, parent, prefix_len, total_nodes)
         self.verify(tree_off, tokens, prefix_len, total_nodes, x=x, timer=timer)
         self.accept(tree_off, parent, tokens, prefix_len)
+
+
+class TreeDrafter:
+    """Draft-tree expansion for a batch of sequences (eagle_draft_expand), with its
+    output buffers and workspace allocated once.
+
+    weights: the target's tensors (final_ln, w_lm, embed); draft_weights: w_fc and the
+    draft decoder layer.  Trees come out compacted (tree_off, parent, tokens, cum) in
+    arrays of batch * max_nodes entries, padded past tree_off[batch]."""
+
+    def __init__(self, dims, params, weights, draft_weights, dk_cache, dv_cache, *, batch, max_prefix,
+                 device="cuda"):
+        self.dims = dims
+        self.params = A.draft_params_struct(params)
+        self.dstruct = A.dims_struct(dims)
+        self.lstruct = A.layer_struct(draft_weights)
+        self.w = weights
+        self.dw = draft_weights
+        self.dk_cache = dk_cache
+        self.dv_cache = dv_cache
+        self.B = batch
+        self.max_prefix = max_prefix
+        p = self.params
+        self.max_nodes = p.max_nodes
+        self.pool_cap = 1 + p.top_k + (p.depth - 1) * p.frontier * p.top_k
+        N = batch * p.max_nodes
+        z = lambda *s, dtype=torch.int32: torch.zeros(*s, dtype=dtype, device=device)  # noqa: E731
+        self.tree_off = z(batch + 1)
+        self.parent = z(N)
+        self.tokens = z(N)
+        self.cum = z(N, dtype=torch.float32)
+        ws = A.eagle_workspace_size(1, dims, batch, 0, 0, max_prefix, self.params)
+        if ws == 0:
+            raise A.EagleError(A.EAGLE_ERR_UNSUPPORTED, "eagle_workspace_size")
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        A.eagle_workspace_init(self.workspace)
+
+    def expand(self, root_feature, root_token, prefix_len, timer=None):
+        w, dw = self.w, self.dw
+        A.eagle_draft_expand(self.dstruct, self.params, dw["w_fc"], self.lstruct, w["final_ln"], w["w_lm"],
+                             w["embed"], root_feature, root_token, self.dk_cache, self.dv_cache, prefix_len,
+                             self.tree_off, self.parent, self.tokens, self.cum, self.workspace,
+                             max_prefix=self.max_prefix, timer=timer)
+
+    def pool(self):
+        """Candidate pool of the last expansion (device tensors)."""
+        p, B, P = self.params, self.B, self.pool_cap
+        dev = self.workspace.device
+        out = dict(pool_n=torch.zeros(B, dtype=torch.int32, device=dev),
+                   token=torch.zeros(B, P, dtype=torch.int32, device=dev),
+                   parent=torch.zeros(B, P, dtype=torch.int32, device=dev),
+                   depth=torch.zeros(B, P, dtype=torch.int32, device=dev),
+                   cum=torch.zeros(B, P, dtype=torch.float32, device=dev),
+                   logp=torch.zeros(B, P, dtype=torch.float32, device=dev),
+                   expanded=torch.zeros(B, p.depth, p.frontier, dtype=torch.int32, device=dev))
+        A.eagle_draft_pool(self.dstruct, self.params, B, self.max_prefix, self.workspace, out["pool_n"], out["token"],
+                           out["parent"], out["depth"], out["cum"], out["logp"], out["expanded"])
+        return out
+
+
+class EagleStep:
+    """One full speculative step on device, with no host synchronisation: draft a tree
+    per sequence, encode it, verify every node with the target layer (inputs are the
+    token embeddings), accept the longest matching path and commit its K/V.  The next
+    step's roots are the accepted bonus tokens and their features."""
+
+    def __init__(self, dims, params, weights, draft_weights, k_cache, v_cache, dk_cache, dv_cache, *, batch,
+                 max_prefix, device="cuda"):
+        self.drafter = TreeDrafter(dims, params, weights, draft_weights, dk_cache, dv_cache, batch=batch,
+                                   max_prefix=max_prefix, device=device)
+        M = self.drafter.max_nodes
+        self.total = batch * M
+        self.verifier = TreeVerifier(dims, weights, k_cache, v_cache, batch=batch, max_total_nodes=self.total,
+                                     max_nodes=M, max_prefix=max_prefix, device=device)
+
+    def step(self, root_feature, root_token, prefix_len, timer=None):
+        d, v = self.drafter, self.verifier
+        d.expand(root_feature, root_token, prefix_len, timer=timer)
+        v.encode(d.tree_off, d.parent, prefix_len, self.total)
+        v.verify(d.tree_off, d.tokens, prefix_len, self.total, timer=timer)
+        v.accept(d.tree_off, d.parent, d.tokens, prefix_len)
+        return v.next_feature, v.next_token
