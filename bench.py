@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="also run a 1 GiB torch copy so counter runs can scale FETCH/WRITE_SIZE")
     ap.add_argument("--no-timer", action="store_true", help="time without per-kernel events")
+    ap.add_argument("--no-eagle-step", action="store_true",
+                    help="skip the full EAGLE step (draft + verify + accept, batch 16)")
+    ap.add_argument("--eagle-steps", type=int, default=20)
     return ap.parse_args()
 
 
@@ -88,6 +91,112 @@ def step_roofline_bytes_flops(dims, wl):
             d[i] = d[par[i]] + 1
         flops += int(np.sum(4 * Hq * D * (int(wl.prefix_len[b]) + d + 1)))
     return byts, flops
+
+
+def draft_roofline_bytes_flops(dims, p, batch, prefix_len):
+    """Algorithmic bytes and flops of one draft expansion: every level streams the FC, the
+    draft layer and the LM head once and reads the draft KV prefix once; rows per level are
+    B on the first level and B * frontier after it."""
+    H, Hq, Hkv, D, F, V = dims.hidden, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.ffn, dims.vocab
+    w = 2 * H * H + (Hq + 2 * Hkv) * D * H + H * Hq * D + 3 * F * H + V * H
+    kv = int(np.sum(prefix_len)) * Hkv * D * 2 * 2
+    byts = p.depth * (w * 2 + kv)
+    rows = batch + (p.depth - 1) * batch * p.frontier
+    flops = 2 * rows * w + rows * 4 * Hq * D * (int(np.mean(prefix_len)) + p.depth)
+    return byts, flops
+
+
+def bench_eagle_step(args):
+    """The full speculative step at the 8B shape with batch 16 (draft -> tree build -> verify
+    of the 16 x 60 drafted nodes -> accept + commit), as a decode loop: each step's roots are
+    the previous step's bonus tokens and their features.  All on device, no host sync."""
+    import torch
+    import tree_attention_verification_06_amd as E
+    from tree_attention_verification_06_amd.runner import EagleStep
+    from workloads import make_workload
+    from workloads.device import upload
+
+    n = args.eagle_steps
+    t0 = time.perf_counter()
+    wl = make_workload(5, seed=args.seed, cache_slack=(n + 8) * 8)
+    log(f"workload {wl.name}: generated in {time.perf_counter() - t0:.1f}s")
+    t = upload(wl)
+    dims, p, B = wl.dims, wl.draft, wl.batch
+    st = EagleStep(dims, p, t["weights"], t["draft_weights"], t["k_cache"], t["v_cache"], t["dk_cache"],
+                   t["dv_cache"], batch=B, max_prefix=wl.cache_cap)
+    d, v = st.drafter, st.verifier
+    prefix0 = t["prefix_len"].clone()
+    feat = t["root_feature"].clone()
+    tok = t["root_token"].clone()
+
+    def run_steps(k, timer=None, count=False):
+        nonlocal feat, tok
+        acc = []
+        for _ in range(k):
+            nf, nt = st.step(feat, tok, t["prefix_len"], timer=timer)
+            feat = nf.clone()
+            tok = nt.clone()
+            if count:
+                acc.append(int((v.accept_len + 1).sum().item()))
+        return acc
+
+    run_steps(3)
+    t["prefix_len"].copy_(prefix0)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run_steps(n)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / n
+    st_code = int(v.status.item())
+    if st_code != 0:
+        raise RuntimeError(f"device status {st_code} ({E.status_str(st_code)})")
+    # the draft alone and the verification alone (same trees), same stream, no sync inside
+    e0.record(stream)
+    for _ in range(n):
+        d.expand(feat, tok, t["prefix_len"])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_draft = e0.elapsed_time(e1) / n
+    tokens_fixed = d.tokens.clone()
+    plen = t["prefix_len"].clone()
+    e0.record(stream)
+    for _ in range(n):
+        v.encode(d.tree_off, d.parent, plen, st.total)
+        v.verify(d.tree_off, tokens_fixed, plen, st.total)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_verify = e0.elapsed_time(e1) / n
+    # accepted tokens per step (a separate pass that reads accept_len after each step)
+    t["prefix_len"].copy_(prefix0)
+    acc = run_steps(min(n, 10), count=True)
+    # per-stage breakdown of one draft expansion (diagnostic: events around every kernel)
+    diag = E.Timer(capacity=4096)
+    for _ in range(3):
+        d.expand(feat, tok, t["prefix_len"], timer=diag)
+    torch.cuda.synchronize()
+    stages = {k: round(ms / 3, 5) for k, (ms, c) in diag.collect().items()}
+    diag.close()
+    dbytes, dflops = draft_roofline_bytes_flops(dims, p, B, wl.prefix_len)
+    d_roof_ms = max(dbytes / (HBM_PEAK_GBS * 1e9), dflops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    nodes = B * p.max_nodes
+    acc_mean = float(np.mean(acc))
+    return {
+        "workload": wl.name, "batch": B, "prefix": int(wl.prefix_len.max()),
+        "draft": {"depth": p.depth, "top_k": p.top_k, "frontier": p.frontier, "max_nodes": p.max_nodes,
+                  "conf_threshold": p.conf_threshold},
+        "steps": n, "ms_per_step": round(ms_step, 4), "ms_draft": round(ms_draft, 4),
+        "ms_verify": round(ms_verify, 4),
+        "accepted_per_step": acc_mean, "accepted_tok_s": round(acc_mean / (ms_step * 1e-3), 1),
+        "verify_nodes_s": round(nodes / (ms_verify * 1e-3), 1),
+        "draft_roofline": {"bound": "hbm", "algorithmic_bytes": dbytes, "algorithmic_flops": dflops,
+                           "t_roof_ms": round(d_roof_ms, 4), "frac": round(d_roof_ms / ms_draft, 4)},
+        "draft_stage_ms": stages,
+        "data": "synthetic: random-init draft head and target layer N(0,0.02), root features N(0,1), "
+                "draft KV prefix N(0,1); the roots of each step are the previous step's bonus tokens",
+    }
 
 
 def cpu_baseline(wl, sample_nodes, min_seconds=10.0, max_steps=100):
@@ -266,6 +375,10 @@ def main():
         "roofline": roof,
         "stage_ms_per_step": {k: round(ms / max(n, 1), 5) for k, (ms, n) in diag_stages.items()},
     }
+    if not args.no_eagle_step and dims.dtype == "bf16":
+        del v, t
+        torch.cuda.empty_cache()
+        out["eagle_step"] = bench_eagle_step(args)
     if args.pmc_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
