@@ -255,16 +255,19 @@ __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
   __shared__ unsigned long long red[4];
   __shared__ float fred[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const float* lp = s.tk_lse + (int64_t)r * s.n_tk * 2;
+  // per-tile outputs are stored tile-major: [tile][row][...] with Rl rows per tile
+  const int Rl = s.B * s.FL;
+  const float* lp = s.tk_lse + (int64_t)r * 2;
+  const int64_t ls = (int64_t)Rl * 2;
   float mx = -INFINITY;
-  for (int t = tid; t < s.n_tk; t += blockDim.x) mx = fmaxf(mx, lp[2 * t]);
+  for (int t = tid; t < s.n_tk; t += blockDim.x) mx = fmaxf(mx, lp[t * ls]);
   mx = wave_max(mx);
   if (lane == 0) fred[w] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
   __syncthreads();
   float se = 0.f;
-  for (int t = tid; t < s.n_tk; t += blockDim.x) se += lp[2 * t + 1] * __expf(lp[2 * t] - mx);
+  for (int t = tid; t < s.n_tk; t += blockDim.x) se += lp[t * ls + 1] * __expf(lp[t * ls] - mx);
   se = wave_sum(se);
   if (lane == 0) fred[w] = se;
   __syncthreads();
@@ -274,11 +277,10 @@ __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) lst[i] = 0ull;
   const int ncand = s.n_tk * s.K;
-  const float* cv = s.tk_val + (int64_t)r * ncand;
-  const int32_t* ci = s.tk_idx + (int64_t)r * ncand;
   for (int c = tid; c < ncand; c += blockDim.x) {
-    const int id = ci[c];
-    unsigned long long key = id < 0 ? 0ull : argmax_key(cv[c], (uint32_t)id);
+    const int64_t o = ((int64_t)(c / s.K) * Rl + r) * s.K + c % s.K;
+    const int id = s.tk_idx[o];
+    unsigned long long key = id < 0 ? 0ull : argmax_key(s.tk_val[o], (uint32_t)id);
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
       const unsigned long long hi = key > lst[i] ? key : lst[i];

@@ -70,10 +70,10 @@ struct Epi {
   int32_t* argmax_out;
   float* max_out;
   int* done;
-  // EPI_TOPK: per (row, tile) the tile's top-k (value, index) and its (max, sum exp) pair
-  float* topk_val;   // [m][n_tiles][topk]
-  int32_t* topk_idx; // [m][n_tiles][topk]
-  float* lse_part;   // [m][n_tiles][2]
+  // EPI_TOPK: per (tile, row) the tile's top-k (value, index) and its (max, sum exp) pair
+  float* topk_val;   // [n_tiles][m][topk]
+  int32_t* topk_idx; // [n_tiles][m][topk]
+  float* lse_part;   // [n_tiles][m][2]
   int topk;
 };
 

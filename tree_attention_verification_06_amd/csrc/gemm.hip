@@ -162,8 +162,8 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
       break;
     }
     case EPI_QKV: {
-      __shared__ int s_pos[128], s_kvrow[128];
-      for (int t = tid; t < mv && t < 128; t += nth) {
+      __shared__ int s_pos[256], s_kvrow[256];  // token tiles hold at most 256 rows
+      for (int t = tid; t < mv; t += nth) {
         s_pos[t] = e.pos ? e.pos[m0 + t] : 0;
         s_kvrow[t] = e.kv_idx ? e.kv_idx[m0 + t] : m0 + t;
       }
@@ -257,44 +257,78 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
       break;
     }
     case EPI_TOPK: {
-      // per token: this tile's top-k (value desc, index asc) and (max, sum exp(v - max))
+      // Per token: this tile's top-k (value desc, index asc) and (max, sum exp(v - max)).
+      // Thread (token t = tid % mt, part = tid / mt) scans columns part, part + P, ...
+      // (P = nth / mt parts per token): a wave reads one column for 64 consecutive tokens,
+      // which is conflict-free in the column-major tile.  Each thread keeps its best
+      // candidates as a sorted register list (branch-free insertion, static indices); the
+      // lists and partial (max, sum) pairs of a token are then merged through LDS.
+      constexpr int KMAX = 16;
       const int K = e.topk;
-      const int n_tiles = (d.n + tc - 1) / tc;
       const int tile_i = col0 / tc;
-      const int nw = nth / 64, w = tid / 64, lane = tid % 64;
-      for (int t = w; t < mv; t += nw) {
+      const int P = nth / mt;
+      const int t = tid % mt, part = tid / mt;
+      const int ncol = min(tc, d.n - col0);
+      unsigned long long lst[KMAX];
+#pragma unroll
+      for (int q = 0; q < KMAX; ++q) lst[q] = 0ull;
+      float mx = -INFINITY, se = 0.f;
+      if (t < mv) {
         const float sc = scale[t];
-        // (max, sumexp) over valid columns
-        float mx = -INFINITY;
-        for (int r = lane; r < tc && col0 + r < d.n; r += 64) mx = fmaxf(mx, sc * tile[r * ts + t]);
-        mx = wave_max(mx);
-        float se = 0.f;
-        for (int r = lane; r < tc && col0 + r < d.n; r += 64) se += __expf(sc * tile[r * ts + t] - mx);
-        se = wave_sum(se);
-        const int64_t ob = ((int64_t)(m0 + t) * n_tiles + tile_i);
-        if (lane == 0) {
-          e.lse_part[ob * 2] = mx;
-          e.lse_part[ob * 2 + 1] = se;
+        for (int r = part; r < ncol; r += P) mx = fmaxf(mx, sc * tile[r * ts + t]);
+        for (int r = part; r < ncol; r += P) {
+          const float v = sc * tile[r * ts + t];
+          se += __expf(v - mx);
+          unsigned long long key = argmax_key(v, (uint32_t)(col0 + r));
+#pragma unroll
+          for (int q = 0; q < KMAX; ++q) {
+            const unsigned long long hi = key > lst[q] ? key : lst[q];
+            key = key > lst[q] ? lst[q] : key;
+            lst[q] = hi;
+          }
         }
-        // top-k by repeated wave argmax, excluding the keys already chosen
-        unsigned long long last = ~0ull;
+      }
+      __syncthreads();  // every read of the tile is done: its LDS is reused below
+      unsigned long long* sl = (unsigned long long*)tile;          // [P][mt][KMAX]
+      float* sm = (float*)(sl + (size_t)P * mt * KMAX);             // [P][mt][2]
+#pragma unroll
+      for (int q = 0; q < KMAX; ++q) sl[((size_t)part * mt + t) * KMAX + q] = lst[q];
+      sm[(part * mt + t) * 2] = mx;
+      sm[(part * mt + t) * 2 + 1] = se;
+      __syncthreads();
+      if (part == 0 && t < mv) {
+        float M = -INFINITY;
+        for (int p2 = 0; p2 < P; ++p2) M = fmaxf(M, sm[(p2 * mt + t) * 2]);
+        float S = 0.f;
+        for (int p2 = 0; p2 < P; ++p2) {
+          const float m2 = sm[(p2 * mt + t) * 2];
+          if (m2 > -INFINITY) S += sm[(p2 * mt + t) * 2 + 1] * __expf(m2 - M);
+        }
+        const int64_t ob = (int64_t)tile_i * d.m + m0 + t;  // tile-major: coalesced per workgroup
+        e.lse_part[ob * 2] = M;
+        e.lse_part[ob * 2 + 1] = S;
+        // P-way merge of the sorted lists (keys are unique: one per column)
+        int head[8];
+#pragma unroll
+        for (int p2 = 0; p2 < 8; ++p2) head[p2] = 0;
         for (int q = 0; q < K; ++q) {
-          unsigned long long bk = 0ull;
-          for (int r = lane; r < tc && col0 + r < d.n; r += 64) {
-            const unsigned long long key = argmax_key(sc * tile[r * ts + t], (uint32_t)(col0 + r));
-            if (key < last && key > bk) bk = key;
+          unsigned long long best = 0ull;
+          int bp = 0;
+#pragma unroll
+          for (int p2 = 0; p2 < 8; ++p2) {
+            if (p2 < P && head[p2] < KMAX) {
+              const unsigned long long c = sl[((size_t)p2 * mt + t) * KMAX + head[p2]];
+              if (c > best) {
+                best = c;
+                bp = p2;
+              }
+            }
           }
 #pragma unroll
-          for (int o = 32; o > 0; o >>= 1) {
-            const unsigned long long ok = __shfl_xor(bk, o, 64);
-            bk = ok > bk ? ok : bk;
-          }
-          last = bk;
-          if (lane == 0) {
-            const bool valid = bk != 0ull;
-            e.topk_val[ob * K + q] = valid ? ord2f((uint32_t)(bk >> 32)) : -INFINITY;
-            e.topk_idx[ob * K + q] = valid ? (int32_t)(0xffffffffu - (uint32_t)(bk & 0xffffffffull)) : -1;
-          }
+          for (int p2 = 0; p2 < 8; ++p2) head[p2] += (p2 == bp && best != 0ull);
+          const bool valid = best != 0ull;
+          e.topk_val[ob * K + q] = valid ? ord2f((uint32_t)(best >> 32)) : -INFINITY;
+          e.topk_idx[ob * K + q] = valid ? (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull)) : -1;
         }
       }
       break;
@@ -304,26 +338,47 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
   }
 }
 
-// Split-K fixup: tile[e] = sum over splits (in split order) of the S partial tiles.
-// All loads of an element group are issued before the first add: the partials come
-// from other workgroups through device-coherent loads, each a full memory round trip,
-// so a load-add chain per split would serialise those round trips.
-template <int S, int ELEMS, int MT_, int TS_, int NTH_>
+// Split-K partial tiles are exchanged in MFMA-fragment order (fragment f = (16-row block,
+// 16-token block), lane l: its four accumulators as one 16-byte vector) with 16-byte
+// buffer loads and stores carrying the device-coherent cache policy (SC1, the policy of
+// agent-scope atomic accesses): the partials come from workgroups on other XCDs, whose L2
+// is not coherent with this one.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kSc1 = 16;  // cache-policy bits of a buffer access: SC1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Split-K fixup: tile = sum over splits (in split order) of the S partial tiles of NF4
+// fragments each.  All loads of a pass are issued before the first add, so the round
+// trips to memory overlap.
+template <int S, int NF4, int MT_, int TS_, int NTH_>
 __device__ __forceinline__ void sum_partials(const float* p0, float* tile) {
-  constexpr int G = 4;  // elements per thread per pass
-  for (int i0 = threadIdx.x * G; i0 < ELEMS; i0 += NTH_ * G) {
-    float a[S][G];
+  constexpr int G = S <= 2 ? 4 : (S <= 4 ? 2 : 1);  // fragments per thread per pass
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p0, (uint32_t)S * NF4 * 16);
+  for (int f0 = threadIdx.x; f0 < NF4; f0 += NTH_ * G) {
+    f32x4 a[S][G];
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
-      for (int g = 0; g < G; ++g) a[s][g] = coherent_load(p0 + (int64_t)s * ELEMS + i0 + g);
+      for (int g = 0; g < G; ++g) {
+        const int f = min(f0 + g * NTH_, NF4 - 1);
+        a[s][g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (s * NF4 + f) * 16, 0, kSc1));
+      }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float v = a[0][g];
+      const int f = f0 + g * NTH_;
+      if (f >= NF4) break;
+      f32x4 v = a[0][g];
 #pragma unroll
       for (int s = 1; s < S; ++s) v += a[s][g];
-      const int i = i0 + g;
-      tile[(i / MT_) * TS_ + (i % MT_)] = v;
+      // fragment f: 16-row block blk, 16-token block t, lane l -> rows blk*16 + (l/16)*4 + i
+      const int l = f % 64, bt = f / 64;
+      const int t = bt % (MT_ / 16), blk = bt / (MT_ / 16);
+      float* dst = tile + (blk * 16 + (l / 16) * 4) * TS_ + t * 16 + (l % 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i * TS_] = v[i];
     }
   }
 }
@@ -331,23 +386,29 @@ __device__ __forceinline__ void sum_partials(const float* p0, float* tile) {
 // ---------------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------------
-constexpr int KC = 512;   // K chunk staged in LDS (one 16-byte group per lane per row)
-constexpr int MT = 64;    // tokens per tile
-
-template <int NW, int RB, int PD, bool DUAL>
+// Tile shapes: NW waves x RB 16-row weight blocks per wave, MT tokens, K chunks of KC,
+// XB X-chunk buffers in LDS (1: the next chunk is stored after a barrier).  Wider token
+// tiles (MT 128 / 256) use shorter K chunks so that the X chunks and the output tile both
+// fit the 160 KB of LDS; each weight byte is then streamed once per MT tokens instead of
+// once per 64.
+template <int NW, int RB, int PD, bool DUAL, int MT, int KC, int XB>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid_real) {
   constexpr int NT = NW * RB * 16;        // weight rows per tile (both blocks when DUAL)
   constexpr int TC = DUAL ? NT / 2 : NT;  // output columns per tile
   constexpr int NSTEP = KC / 32;
   constexpr int XS = KC + 8;              // LDS row stride of an X chunk (bf16)
   constexpr int TS = MT + 4;              // LDS row stride of the output tile (f32)
-  constexpr int LDS_X = 2 * MT * XS * 2;  // double-buffered X chunks
+  constexpr int LDS_X = XB * MT * XS * 2;  // X chunk buffers
   constexpr int LDS_T = NT * TS * 4;
   constexpr int LDS = LDS_X > LDS_T ? LDS_X : LDS_T;
-  constexpr int RPW = MT / NW;            // X rows staged per wave
+  constexpr int LPR = KC / 8;             // lanes staging one X row (16 bytes each)
+  constexpr int RPP = 64 / LPR;           // X rows per wave per pass
+  constexpr int RPW = MT / (NW * RPP);    // passes: X registers per thread
   constexpr int NTH = NW * 64;
   static_assert(NSTEP % PD == 0, "prefetch depth must divide the chunk steps");
-  static_assert(MT % NW == 0, "token tile");
+  static_assert(LPR <= 64 && 64 % LPR == 0 && MT % (NW * RPP) == 0, "X staging layout");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(MT <= NTH && MT <= 256, "token tile");
 
   __shared__ __align__(16) unsigned char smem[LDS];
   __shared__ float s_scale[MT];
@@ -374,9 +435,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   const int ke = min(d.k, kb + kps);
   const int klast = ke - 32;
   // chunks of this K range, visited in a rotated order so that concurrently running
-  // workgroups read different columns (spreads requests over HBM channels)
+  // workgroups read different columns (spreads requests over HBM channels); the token
+  // tiles of one weight tile run side by side on one XCD and keep the same order, so
+  // the weight lines the first one fetches are still in that XCD's L2 for the others
   const int nchunk = (ke - kb + KC - 1) / KC;
-  const int c0 = (nt_i * 5 + split * 3 + mt_i) % nchunk;
+  const int c0 = (nt_i * 5 + split * 3) % nchunk;
 
   // this wave's weight rows
   const bf16* wblk;
@@ -396,13 +459,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
     wp[rb] = wblk + (int64_t)row * d.ldw + lq * 8;
   }
 
-  // X rows staged by this lane: r = wid + j * NW, 8 columns at lane * 8 of each chunk
-  int64_t xrow_a[RPW], xrow_b[RPW];
+  // X rows staged by this lane: r = (wid + j * NW) * RPP + lane / LPR, 8 columns at
+  // (lane % LPR) * 8 of each chunk
+  const int xl_row = lane / LPR, xl_col = (lane % LPR) * 8;
+  // (source row indices kept as 32-bit values: wide tiles stage many rows per thread)
+  int32_t xrow_a[RPW], xrow_b[RPW];
 #pragma unroll
   for (int j = 0; j < RPW; ++j) {
-    const int m = min(m0 + wid + j * NW, d.m - 1);
-    xrow_a[j] = (d.x.a.idx ? (int64_t)d.x.a.idx[m] : (int64_t)m) * d.x.a.ld;
-    xrow_b[j] = (d.x.b.idx ? (int64_t)d.x.b.idx[m] : (int64_t)m) * d.x.b.ld;
+    const int m = min(m0 + (wid + j * NW) * RPP + xl_row, d.m - 1);
+    xrow_a[j] = d.x.a.idx ? d.x.a.idx[m] : m;
+    xrow_b[j] = d.x.b.idx ? d.x.b.idx[m] : m;
   }
   auto chunk_k = [&](int ci) {
     int c = c0 + ci;
@@ -413,12 +479,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   uint4 gr = make_uint4(0u, 0u, 0u, 0u);  // norm == 1: the 8 gain values of this lane's columns
   const bool stage_gain = d.x.norm == 1 && d.x.gain;
   auto load_x = [&](int kc) {
-    const int k = min(kc + lane * 8, ke - 8);  // clamped: out-of-range lanes are zeroed at store
+    const int k = min(kc + xl_col, ke - 8);  // clamped: out-of-range lanes are zeroed at store
     if (stage_gain) gr = *(const uint4*)((const bf16*)d.x.gain + k);
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
       const bool in_a = k < d.x.ka;
-      const bf16* base = in_a ? (const bf16*)d.x.a.ptr + xrow_a[j] + k : (const bf16*)d.x.b.ptr + xrow_b[j] + (k - d.x.ka);
+      const bf16* base = in_a ? (const bf16*)d.x.a.ptr + (int64_t)xrow_a[j] * d.x.a.ld + k
+                              : (const bf16*)d.x.b.ptr + (int64_t)xrow_b[j] * d.x.b.ld + (k - d.x.ka);
       xr[j] = *(const uint4*)base;
     }
   };
@@ -427,10 +494,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   for (int j = 0; j < RPW; ++j) ssq[j] = 0.f;
   auto store_x = [&](int buf, int kc, float ssq_w) {
     bf16* xl = (bf16*)smem + buf * (MT * XS);
-    const int k = kc + lane * 8;
+    const int k = kc + xl_col;
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
-      const int r = wid + j * NW;
+      const int r = (wid + j * NW) * RPP + xl_row;
       uint4 v = xr[j];
       if (!(m0 + r < d.m && k < ke)) v = make_uint4(0u, 0u, 0u, 0u);
       if (d.x.norm == 1) {
@@ -453,7 +520,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
           v = make_uint4(pack2bf(f[0], f[1]), pack2bf(f[2], f[3]), pack2bf(f[4], f[5]), pack2bf(f[6], f[7]));
         }
       }
-      *(uint4*)(xl + r * XS + lane * 8) = v;
+      *(uint4*)(xl + r * XS + xl_col) = v;
     }
   };
 
@@ -486,7 +553,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
     const int kcn = chunk_k(more ? ci + 1 : 0);
     // next chunk's X: issued now, stored to the other buffer after this chunk's math
     if (more) load_x(kcn);
-    const bf16* xl = (const bf16*)smem + (ci & 1) * (MT * XS);
+    const bf16* xl = (const bf16*)smem + (XB == 2 ? (ci & 1) : 0) * (MT * XS);
     // Every chunk runs all NSTEP steps: past the K range X is zero in LDS, so the
     // extra steps of a short chunk add exact zeros (and stay branch-free).
 #pragma unroll
@@ -509,15 +576,26 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
           acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[rb], xf, acc[rb][t], 0, 0, 0);
       }
     }
-    if (more) store_x((ci + 1) & 1, kcn, 1.f);
-    __syncthreads();
+    if (XB == 2) {
+      if (more) store_x((ci + 1) & 1, kcn, 1.f);
+      __syncthreads();
+    } else {
+      // one buffer: every wave is done with this chunk before it is overwritten
+      __syncthreads();
+      if (more) {
+        store_x(0, kcn, 1.f);
+        __syncthreads();
+      }
+    }
   }
 
-  // row sums of squares of this K range (norm == 1)
+  // row sums of squares of this K range (norm == 1): the LPR lanes of a row are adjacent
 #pragma unroll
   for (int j = 0; j < RPW; ++j) {
-    const float v = wave_sum(ssq[j]);
-    if (lane == 0) s_ssq[wid + j * NW] = v;
+    float v = ssq[j];
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane % LPR == 0) s_ssq[(wid + j * NW) * RPP + xl_row] = v;
   }
   __syncthreads();
 
@@ -539,13 +617,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
     // split-K: publish this split's partial tile; the last split of the tile to arrive
     // sums all partials in split order (deterministic) and runs the epilogue
     float* part = d.partials + ((int64_t)tile_id * d.splits + split) * (NT * MT);
+    const __amdgpu_buffer_rsrc_t prs = buffer_rsrc(part, NT * MT * 4);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int t = 0; t < MT / 16; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          coherent_store(part + ((wid * RB + rb) * 16 + lq * 4 + i) * MT + t * 16 + lr, acc[rb][t][i]);
+      for (int t = 0; t < MT / 16; ++t) {
+        const int f = ((wid * RB + rb) * (MT / 16) + t) * 64 + lane;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[rb][t]), prs, f * 16, 0, kSc1);
+      }
     if (tid < MT) coherent_store(d.sumsq_part + ((int64_t)tile_id * d.splits + split) * MT + tid, s_ssq[tid]);
     wait_memory();
     __syncthreads();
@@ -557,13 +636,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
     if (!s_flag) return;
     const float* p0 = d.partials + (int64_t)tile_id * d.splits * (NT * MT);
     switch (d.splits) {
-      case 2: sum_partials<2, NT * MT, MT, TS, NTH>(p0, tile); break;
-      case 3: sum_partials<3, NT * MT, MT, TS, NTH>(p0, tile); break;
-      case 4: sum_partials<4, NT * MT, MT, TS, NTH>(p0, tile); break;
-      case 5: sum_partials<5, NT * MT, MT, TS, NTH>(p0, tile); break;
-      case 6: sum_partials<6, NT * MT, MT, TS, NTH>(p0, tile); break;
-      case 7: sum_partials<7, NT * MT, MT, TS, NTH>(p0, tile); break;
-      default: sum_partials<8, NT * MT, MT, TS, NTH>(p0, tile); break;
+      case 2: sum_partials<2, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
+      case 3: sum_partials<3, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
+      case 4: sum_partials<4, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
+      case 5: sum_partials<5, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
+      case 6: sum_partials<6, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
+      case 7: sum_partials<7, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
+      default: sum_partials<8, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
     }
     if (tid < MT) {
       float v = 0.f;
@@ -649,14 +728,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d, int grid_real
 }
 
 struct CfgInfo {
-  int nw, rb, mt;
+  int nw, rb, pd, mt, kc;
 };
-constexpr CfgInfo kCfgs[4] = {{8, 4, 64}, {8, 2, 64}, {8, 1, 64}, {4, 1, 64}};
+// 0-2: 64-token tiles for a few dozen rows (weight streaming); 3: 4 waves (kept, not
+// planned: too few loads in flight); 4, 5: 128- and 256-token tiles for hundreds of rows.
+constexpr CfgInfo kCfgs[6] = {{8, 4, 4, 64, 512}, {8, 2, 4, 64, 512}, {8, 1, 8, 64, 512},
+                              {4, 1, 8, 64, 512}, {8, 2, 4, 128, 256}, {8, 1, 4, 256, 128}};
 
-template <int NW, int RB, int PD, bool DUAL>
+template <int NW, int RB, int PD, bool DUAL, int MT, int KC, int XB>
 void launch_cfg(const GemmDesc& d, int grid, hipStream_t s) {
   const int padded = (grid + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((gemm_bf16_kernel<NW, RB, PD, DUAL>), dim3(padded), dim3(NW * 64), 0, s, d, grid);
+  hipLaunchKernelGGL((gemm_bf16_kernel<NW, RB, PD, DUAL, MT, KC, XB>), dim3(padded), dim3(NW * 64), 0, s, d, grid);
 }
 
 }  // namespace
@@ -674,30 +756,42 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
     p.m_tiles = (m + F32_MT - 1) / F32_MT;
     return p;
   }
-  // Cost model, per CU, in bytes at the HBM rate: every workgroup needs the whole CU's
-  // LDS (double-buffered X), so workgroups run in rounds of 256.  A workgroup moves its
-  // weight slice (HBM), its X slice (L2, weighted 1/4), split-K partials (written and
-  // read back, after a device-scope release) and a fixed launch/epilogue overhead.
-  const int m_tiles = (m + MT - 1) / MT;
-  const int kchunks = (k + KC - 1) / KC;
+  // Cost model (microseconds), fitted to measured launch times of every tile configuration
+  // and split count at the 8B- and 70B-shaped projections with 16..960 tokens (rms error
+  // ~15%).  Each workgroup needs most of a CU's LDS, so workgroups run in rounds of 256.
+  // Per workgroup: its weight slice streams at min(38 GB/s, 6.8 TB/s / resident
+  // workgroups) while its MFMAs run (4.0 TFLOP/s per CU with one 16-row block per wave,
+  // 12.7 with more: X comes from LDS once per block), plus its X slice from L2 at 75 GB/s,
+  // a fixed ~8 us (launch, pipeline fill, epilogue), and the write of its split-K partial.
+  // Split-K adds a serial tail: the last workgroup of a tile reads every partial tile at
+  // ~60 GB/s.  The top-k epilogue costs ~1.1 us per 1000 (token, column) pairs of a tile.
+  constexpr double kBcu = 35.6e3, kBchip = 6.65e6, kBx = 75e3, kP1 = 4.0e6, kP2 = 12.7e6, kF0 = 8.4,
+                   kBfix = 59.6e3, kFsplit = 0.76, kTopk = 10.8e-4;  // bytes/us, flop/us, us
   double best = 1e30;
   int best_c = -1, best_s = 1;
-  // (the 4-wave configuration keeps too few loads in flight to stream at full rate; it
-  // is kept for completeness but not planned)
-  for (int c = 0; c < 3; ++c) {
-    const int nt = kCfgs[c].nw * kCfgs[c].rb * 16;
+  for (int c : {0, 1, 2, 4, 5}) {
+    const CfgInfo& cf = kCfgs[c];
+    const int nt = cf.nw * cf.rb * 16;
     const int tc = dual ? nt / 2 : nt;
     if (epi_kind == EPI_QKV && tc % head_dim) continue;
+    const int m_tiles = (m + cf.mt - 1) / cf.mt;
+    const int kchunks = (k + cf.kc - 1) / cf.kc;
     const int tiles = ((n + tc - 1) / tc) * m_tiles;
     for (int s = 1; s <= std::min(kchunks, 8); ++s) {
       const int cps = (kchunks + s - 1) / s;  // chunks per split
       const int se = (kchunks + cps - 1) / cps;
       if (se != s) continue;
-      const double kps = (double)cps * KC;
+      const double kps = (double)cps * cf.kc;
       const int G = tiles * se;
       const int rounds = (G + 255) / 256;
-      const double per = nt * kps * 2 + 0.25 * MT * kps * 2 + (se > 1 ? nt * MT * 4.0 * 2 : 0.0) + 50e3;
-      const double cost = rounds * per;
+      const double bw = std::min(kBcu, kBchip / std::min(G, 256));
+      const double flops = 2.0 * nt * cf.mt * kps;
+      const double part = (double)nt * cf.mt * 4;
+      double per = std::max(nt * kps * 2 / bw, flops / (cf.rb == 1 ? kP1 : kP2)) + cf.mt * kps * 2 / kBx + kF0;
+      if (se > 1) per += part / kBx;
+      if (epi_kind == EPI_TOPK) per += kTopk * cf.mt * tc;
+      double cost = rounds * per;
+      if (se > 1) cost += se * part / kBfix + kFsplit;
       if (cost < best * 0.999) {
         best = cost;
         best_c = c;
@@ -705,14 +799,16 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
       }
     }
   }
+  const CfgInfo& cf = kCfgs[best_c];
+  const int kchunks = (k + cf.kc - 1) / cf.kc;
   p.cfg = best_c;
   p.splits = best_s;
-  p.kps = ((kchunks + best_s - 1) / best_s) * KC;
-  p.tile_rows = kCfgs[best_c].nw * kCfgs[best_c].rb * 16;
+  p.kps = ((kchunks + best_s - 1) / best_s) * cf.kc;
+  p.tile_rows = cf.nw * cf.rb * 16;
   p.tile_cols = dual ? p.tile_rows / 2 : p.tile_rows;
-  p.mt = MT;
+  p.mt = cf.mt;
   p.n_tiles = (n + p.tile_cols - 1) / p.tile_cols;
-  p.m_tiles = m_tiles;
+  p.m_tiles = (m + cf.mt - 1) / cf.mt;
   return p;
 }
 
@@ -735,6 +831,7 @@ int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s) {
   d.kps = p.kps;
   if (d.k % 32 || (d.x.ka % 8) || p.cfg < 0) return EAGLE_ERR_UNSUPPORTED;
   if (p.cfg != 100 && (d.x.a.dtype != EAGLE_BF16 || d.x.b.dtype != EAGLE_BF16)) return EAGLE_ERR_UNSUPPORTED;
+  if (p.cfg == 100 && d.epi.kind == EPI_TOPK) return EAGLE_ERR_UNSUPPORTED;  // its LDS tile is too small
   const int grid = p.n_tiles * p.m_tiles * p.splits;
   if (grid <= 0) return EAGLE_OK;
   if (p.cfg == 100) {
@@ -743,10 +840,12 @@ int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s) {
   } else {
     const bool dual = d.dual != 0;
     switch (p.cfg) {
-      case 0: dual ? launch_cfg<8, 4, 4, true>(d, grid, s) : launch_cfg<8, 4, 4, false>(d, grid, s); break;
-      case 1: dual ? launch_cfg<8, 2, 4, true>(d, grid, s) : launch_cfg<8, 2, 4, false>(d, grid, s); break;
-      case 2: dual ? launch_cfg<8, 1, 8, true>(d, grid, s) : launch_cfg<8, 1, 8, false>(d, grid, s); break;
-      case 3: dual ? launch_cfg<4, 1, 8, true>(d, grid, s) : launch_cfg<4, 1, 8, false>(d, grid, s); break;
+      case 0: dual ? launch_cfg<8, 4, 4, true, 64, 512, 2>(d, grid, s) : launch_cfg<8, 4, 4, false, 64, 512, 2>(d, grid, s); break;
+      case 1: dual ? launch_cfg<8, 2, 4, true, 64, 512, 2>(d, grid, s) : launch_cfg<8, 2, 4, false, 64, 512, 2>(d, grid, s); break;
+      case 2: dual ? launch_cfg<8, 1, 8, true, 64, 512, 2>(d, grid, s) : launch_cfg<8, 1, 8, false, 64, 512, 2>(d, grid, s); break;
+      case 3: dual ? launch_cfg<4, 1, 8, true, 64, 512, 2>(d, grid, s) : launch_cfg<4, 1, 8, false, 64, 512, 2>(d, grid, s); break;
+      case 4: dual ? launch_cfg<8, 2, 4, true, 128, 256, 2>(d, grid, s) : launch_cfg<8, 2, 4, false, 128, 256, 2>(d, grid, s); break;
+      case 5: dual ? launch_cfg<8, 1, 4, true, 256, 128, 2>(d, grid, s) : launch_cfg<8, 1, 4, false, 256, 128, 2>(d, grid, s); break;
       default: return EAGLE_ERR_UNSUPPORTED;
     }
   }
