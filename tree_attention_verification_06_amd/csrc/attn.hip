@@ -10,19 +10,25 @@
 // handles up to 128 query rows against one chunk of prefix keys, or against the tree
 // keys (the last chunk), and writes fp32 partials (running max, sum, unnormalised o);
 // a merge kernel combines the chunks in fixed order (deterministic).
-//  * K and V tiles (64 keys) are read with 16-byte coalesced loads and staged in LDS;
-//    V is written transposed so that the PV product reads 8-byte runs of keys.
+//  * K and V tiles (64 keys) are read with 16-byte coalesced loads two tiles ahead
+//    (a register ring) and stored to double-buffered LDS in their natural [key][d]
+//    layout with 16-byte writes: one barrier per tile.
 //  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 d from LDS, B = Q held
 //    in registers); each lane then owns 4 consecutive keys of one query row, so the
 //    row max needs only two cross-lane swaps and the softmax rescale of the output is
 //    lane-local.
-//  * O^T += V^T P^T with the same MFMA (A = V^T from LDS, B = P packed to bf16 in
-//    registers, exactly the lane layout the score MFMA produced).
+//  * O^T += V^T P^T with the same MFMA: B = P packed to bf16 in registers (exactly the
+//    lane layout the score MFMA produced: k-slots 8q..8q+7 of lane group q are keys
+//    4q..4q+3 and 16+4q..16+4q+3 of a 32-key step), A = V^T read from the natural V tile
+//    with the gfx950 LDS transpose read (ds_read_b64_tr_b16): within a 16-lane group,
+//    output lane 4a+c receives element c of the 8-byte pieces addressed by lanes a, a+4,
+//    a+8, a+12, so lane s of group q addresses key 4q + s/4, d 4(s%4) of the d-block.
 //  * tree keys are masked with the node's ancestor words: key j is visible iff bit j.
 // fp32 path: a plain VALU kernel, one wave per (node, query head).
 #include "attn.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace eagle {
 
@@ -35,7 +41,9 @@ constexpr int ROWS_WG = NWA * RBW * 16; // query rows per workgroup
 constexpr int KT = 64;                  // keys per LDS tile
 constexpr int HD = 128;
 constexpr int KS = HD + 8;              // LDS row stride of the K tile (bf16)
-constexpr int VS = KT + 8;              // LDS row stride of the transposed V tile (bf16)
+constexpr int VS = HD + 16;             // LDS row stride of the V tile (bf16): the four keys
+                                        // of one transpose read land in distinct banks
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int remap_xcd(int b, int total) {
   const int per = (total + kXcds - 1) / kXcds;
@@ -43,8 +51,8 @@ __device__ __forceinline__ int remap_xcd(int b, int total) {
 }
 
 __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, int grid_real) {
-  __shared__ __align__(16) bf16 ks[KT * KS];
-  __shared__ __align__(16) bf16 vt[HD * VS];
+  __shared__ __align__(16) bf16 ks[2][KT * KS];
+  __shared__ __align__(16) bf16 vs[2][KT * VS];
 
   const int bid = remap_xcd(blockIdx.x, gridDim.x);
   if (bid >= grid_real) return;
@@ -124,12 +132,13 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
   const bf16* vt_base = (const bf16*)a.v_tree + ((int64_t)off * a.hkv + kvh) * HD;
   const int64_t tree_stride = (int64_t)a.hkv * HD;
 
-  // K/V tiles go global -> registers -> LDS; the next tile's loads are issued before the
-  // current tile's math so their latency overlaps it.  Loads are unconditional (keys
-  // past the chunk are clamped to its last key and zeroed when stored).
+  // K/V tiles go global -> registers -> LDS.  The loads of tile i + 2 are issued before
+  // the math of tile i, into the register slot whose tile was stored to LDS one step
+  // earlier, so two tiles of math cover each load's latency.  Loads are unconditional
+  // (keys past the chunk are clamped to its last key and zeroed when stored).
   constexpr int GPT = KT * 16 / (NWA * 64);  // 16-byte groups per thread per tensor
-  uint4 kreg[GPT], vreg[GPT];
-  auto load_kv = [&](int kt0) {
+  uint4 kreg[2][GPT], vreg[2][GPT];
+  auto load_kv = [&](int slot, int kt0) {
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
       const int i = tid + u * NWA * 64;
@@ -137,42 +146,43 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
       const int gd = i & 15;
       const bf16* kp = tree_chunk ? kt_base + key * tree_stride : kc + key * a.ct;
       const bf16* vp = tree_chunk ? vt_base + key * tree_stride : vc + key * a.ct;
-      kreg[u] = *(const uint4*)(kp + gd * 8);
-      vreg[u] = *(const uint4*)(vp + gd * 8);
+      kreg[slot][u] = *(const uint4*)(kp + gd * 8);
+      vreg[slot][u] = *(const uint4*)(vp + gd * 8);
     }
   };
-  auto store_kv = [&](int kt0) {
+  auto store_kv = [&](int slot, int buf, int kt0) {
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
       const int i = tid + u * NWA * 64;
       const int kk = i >> 4, gd = i & 15;
       const bool ok = kt0 + kk < k1;
-      const uint4 kv = ok ? kreg[u] : make_uint4(0u, 0u, 0u, 0u);
-      const uint4 vv = ok ? vreg[u] : make_uint4(0u, 0u, 0u, 0u);
-      *(uint4*)(ks + kk * KS + gd * 8) = kv;
-      const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt[(gd * 8 + 2 * e) * VS + kk] = (bf16)(wv[e] & 0xffffu);
-        vt[(gd * 8 + 2 * e + 1) * VS + kk] = (bf16)(wv[e] >> 16);
-      }
+      *(uint4*)(ks[buf] + kk * KS + gd * 8) = ok ? kreg[slot][u] : make_uint4(0u, 0u, 0u, 0u);
+      *(uint4*)(vs[buf] + kk * VS + gd * 8) = ok ? vreg[slot][u] : make_uint4(0u, 0u, 0u, 0u);
     }
   };
 
-  load_kv(k0);
-  for (int kt0 = k0; kt0 < k1; kt0 += KT) {
-    __syncthreads();
-    store_kv(kt0);
-    __syncthreads();
-    load_kv(min(kt0 + KT, k1 - 1));
+  const int ntile = (k1 - k0 + KT - 1) / KT;
+  load_kv(0, k0);
+  load_kv(1, min(k0 + KT, k1 - 1));
+  store_kv(0, 0, k0);
+  __syncthreads();
+  // one tile: SL (compile-time, so the register ring never needs dynamic indexing) is the
+  // register slot and LDS buffer of tile it
+  auto tile_step = [&](auto SLC, int it) {
+    constexpr int SL = decltype(SLC)::value;
+    const int kt0 = k0 + it * KT;
+    // tile it + 2 into the slot tile it came through
+    load_kv(SL, min(kt0 + 2 * KT, k1 - 1));
     __builtin_amdgcn_sched_barrier(0);
+    const bf16* ksb = ks[SL];
+    const bf16* vsb = vs[SL];
 
     float s[RBW][4][4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       bf16x8_t kf[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kf[kk] = *(const bf16x8_t*)(ks + (st * 16 + lr) * KS + kk * 32 + lq * 8);
+      for (int kk = 0; kk < 4; ++kk) kf[kk] = *(const bf16x8_t*)(ksb + (st * 16 + lr) * KS + kk * 32 + lq * 8);
 #pragma unroll
       for (int j = 0; j < RBW; ++j) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -230,19 +240,30 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
         pk.u[3] = pack2bf(s[j][2 * G + 1][2], s[j][2 * G + 1][3]);
         pb[j] = pk.v;
       }
+      // V^T fragments by transpose reads: lane (q = lq, s = lr) addresses key
+      // G*32 + 4q + s/4 (and + 16), d = db*16 + 4*(s%4)
+      const bf16* vr = vsb + (G * 32 + 4 * lq + (lr >> 2)) * VS + 4 * (lr & 3);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const bf16* vr = vt + (db * 16 + lr) * VS + G * 32 + lq * 4;
         union {
-          uint2 u[2];
+          s16x4_t h[2];
           bf16x8_t v;
         } va;
-        va.u[0] = *(const uint2*)(vr);
-        va.u[1] = *(const uint2*)(vr + 16);
+        va.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(vr + db * 16));
+        va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(vr + 16 * VS + db * 16));
 #pragma unroll
         for (int j = 0; j < RBW; ++j) o[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va.v, pb[j], o[j][db], 0, 0, 0);
       }
     }
+    // next tile (loaded one step ago) into the other LDS buffer; the barrier also ends
+    // every wave's reads of this buffer before it is refilled
+    if (it + 1 < ntile) store_kv(1 - SL, 1 - SL, kt0 + KT);
+    __syncthreads();
+  };
+  for (int it = 0; it < ntile; it += 2) {
+    tile_step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < ntile) tile_step(std::integral_constant<int, 1>{}, it + 1);
   }
 
   const int rmax = a.max_nodes * g;
