@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-eagle-step", action="store_true",
                     help="skip the full EAGLE step (draft + verify + accept, batch 16)")
     ap.add_argument("--eagle-steps", type=int, default=20)
+    ap.add_argument("--eagle-only", action="store_true",
+                    help="run only the full EAGLE step (for profiling its kernels apart from the verify step)")
     return ap.parse_args()
 
 
@@ -253,6 +255,9 @@ def main():
     from workloads.device import upload
 
     E.lib()  # fail loudly if the HIP library is not built
+    if args.eagle_only:
+        print(json.dumps({"eagle_step": bench_eagle_step(args)}), flush=True)
+        return
     cfg = args.config
     extra = args.warmup + args.steps + 8
     t0 = time.perf_counter()

@@ -156,21 +156,6 @@ struct DraftState {
 // -0 and +0 compare equal but map to different ordered keys; cum values are kept at +0
 __device__ __forceinline__ float canon_zero(float v) { return v == 0.f ? 0.f : v; }
 
-__device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v, unsigned long long* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long other = __shfl_xor(v, o, 64);
-    v = other > v ? other : v;
-  }
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  unsigned long long m = red[0];
-  for (int i = 1; i < nw; ++i) m = red[i] > m ? red[i] : m;
-  return m;
-}
-
 // Root features to bf16, pool = {root}, frontier = {root}, attention tree offsets b * maxp.
 __global__ __launch_bounds__(256) void draft_init_kernel(DraftState s) {
   const int b = blockIdx.x;
@@ -200,20 +185,22 @@ __global__ __launch_bounds__(256) void draft_init_kernel(DraftState s) {
 
 // Frontier of sequence b -> rows b*FL .. b*FL+FL-1.  Also stores the previous level's
 // predicted features (bf16) in the feature rows of the nodes expanded there.
+// Workgroup (b, 0) does the bookkeeping; workgroup (b, 1 + j) copies row j of the previous
+// level (one feature row each, so the copy runs on B * FLprev workgroups).
 __global__ __launch_bounds__(256) void draft_prep_kernel(DraftState s) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const int m0 = s.cnt[C_NNODES * s.B + b];  // nodes expanded before this level
   const int qlo_prev = s.cnt[C_QLO * s.B + b];
   const int nf = s.cnt[C_NF * s.B + b];
-  if (s.h) {
-    const int nprev = m0 - qlo_prev;  // nodes expanded on the previous level: slots qlo_prev ..
-    const int hv = s.H / 4;
-    for (int i = tid; i < nprev * hv; i += blockDim.x) {
-      const int j = i / hv, c = (i % hv) * 4;
+  if (blockIdx.y > 0) {
+    const int j = blockIdx.y - 1;
+    if (!s.h || j >= m0 - qlo_prev) return;  // nodes expanded on the previous level: slots qlo_prev ..
+    const int64_t frow = (int64_t)s.B + (int64_t)b * s.maxp + qlo_prev + j;
+    for (int c = tid * 4; c < s.H; c += blockDim.x * 4) {
       const float4 v = *(const float4*)(s.h + ((int64_t)b * s.FLprev + j) * s.H + c);
-      const int64_t frow = (int64_t)s.B + (int64_t)b * s.maxp + qlo_prev + j;
       *(uint2*)(s.feat + frow * s.H + c) = make_uint2(pack2bf(v.x, v.y), pack2bf(v.z, v.w));
     }
+    return;
   }
   if (tid < s.FL) {
     const int j = tid, r = b * s.FL + j;
@@ -247,12 +234,12 @@ __global__ __launch_bounds__(256) void draft_prep_kernel(DraftState s) {
 
 // Row top-k over the LM-head tiles (ties to the lower id) and the row log-sum-exp.
 // Each thread keeps a sorted list of its best KMAX candidates (branch-free insertion,
-// static indices), then K rounds of a block maximum pop the heads of those lists.
+// static indices); each wave then selects its top K from its lanes' lists, and one
+// thread merges the four wave lists.
 __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
   const int r = blockIdx.x;
   const int b = r / s.FL, j = r % s.FL;
   if (j >= s.cnt[C_NF * s.B + b]) return;
-  __shared__ unsigned long long red[4];
   __shared__ float fred[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   // per-tile outputs are stored tile-major: [tile][row][...] with Rl rows per tile
@@ -276,32 +263,58 @@ __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
   unsigned long long lst[KMAX];
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) lst[i] = 0ull;
-  const int ncand = s.n_tk * s.K;
-  for (int c = tid; c < ncand; c += blockDim.x) {
-    const int64_t o = ((int64_t)(c / s.K) * Rl + r) * s.K + c % s.K;
-    const int id = s.tk_idx[o];
-    unsigned long long key = id < 0 ? 0ull : argmax_key(s.tk_val[o], (uint32_t)id);
+  // thread tid scans tiles tid, tid + 256, ... (the K candidates of a (tile, row) are adjacent)
+  for (int t = tid; t < s.n_tk; t += blockDim.x) {
+    for (int q = 0; q < s.K; ++q) {
+      const int64_t o = ((int64_t)t * Rl + r) * s.K + q;
+      const int id = s.tk_idx[o];
+      unsigned long long key = id < 0 ? 0ull : argmax_key(s.tk_val[o], (uint32_t)id);
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      const unsigned long long hi = key > lst[i] ? key : lst[i];
-      key = key > lst[i] ? lst[i] : key;
-      lst[i] = hi;
+      for (int i = 0; i < KMAX; ++i) {
+        const unsigned long long hi = key > lst[i] ? key : lst[i];
+        key = key > lst[i] ? lst[i] : key;
+        lst[i] = hi;
+      }
     }
   }
+  // each wave: K rounds of a wave maximum over its lanes' list heads (no barriers); the
+  // winner pops its head (keys are unique: one per vocabulary id)
+  __shared__ unsigned long long wtop[4][KMAX];
   for (int q = 0; q < s.K; ++q) {
-    const unsigned long long best = block_max_u64(lst[0], red);
-    if (best != 0ull && lst[0] == best) {  // keys are unique (one per vocabulary id)
+    unsigned long long best = lst[0];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long other = __shfl_xor(best, o, 64);
+      best = other > best ? other : best;
+    }
+    if (best != 0ull && lst[0] == best) {
 #pragma unroll
       for (int i = 0; i < KMAX - 1; ++i) lst[i] = lst[i + 1];
       lst[KMAX - 1] = 0ull;
     }
-    if (tid == 0) {
+    if (lane == 0) wtop[w][q] = best;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // 4-way merge of the wave lists
+    int head[4] = {0, 0, 0, 0};
+    for (int q = 0; q < s.K; ++q) {
+      unsigned long long best = 0ull;
+      int bw = 0;
+      for (int i = 0; i < 4; ++i) {
+        const unsigned long long c = head[i] < s.K ? wtop[i][head[i]] : 0ull;
+        if (c > best) {
+          best = c;
+          bw = i;
+        }
+      }
+      if (best != 0ull) head[bw]++;
       const bool ok = best != 0ull;
       s.row_val[(int64_t)r * s.K + q] = ok ? ord2f((uint32_t)(best >> 32)) : -INFINITY;
       s.row_idx[(int64_t)r * s.K + q] = ok ? (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull)) : -1;
     }
+    s.row_lse[r] = lse;
   }
-  if (tid == 0) s.row_lse[r] = lse;
 }
 
 // Children of this level's frontier are appended to the pool; the next frontier is the
@@ -576,7 +589,7 @@ int draft_expand_impl(const eagle_dims* d, const eagle_draft_params* pr, const v
     st.n_tk = L.p_lm[i].n_tiles;
 
     timer_begin(timer, ST_DRAFT_SELECT, s);
-    hipLaunchKernelGGL(draft_prep_kernel, dim3(B), dim3(256), 0, s, st);
+    hipLaunchKernelGGL(draft_prep_kernel, dim3(B, 1 + st.FLprev), dim3(256), 0, s, st);
     timer_end(timer, s);
     // FC over [parent feature ; token embedding] -> x, bf16(ln_attn * x), row sums of squares
     {
