@@ -175,3 +175,73 @@ def test_accept_commit_bit_exact(cfg):
         assert (bits(vc[b][:, others]) == bits(pre_v[b][:, others])).all()
         nf = v.next_feature[b].cpu().numpy()
         assert (nf == g["h"][o + leaf]).all()
+
+
+def test_verify_and_accept_degenerate_trees():
+    """Root-only trees (with and without a prefix), a 128-node chain (two mask words, the
+    deepest path the library accepts) and a star, in one ragged batch; then acceptance with
+    the chain planted along its whole length."""
+    dims = mini_dims()
+    parents = [[-1], [-1], T.chain(128), T.star(40)]
+    wl = make_workload(2, seed=31, dims=dims, batch=4, prefix=[0, 17, 0, 1000], parents=parents)
+    assert wl.mask_words == 2
+    _print("verify degenerate", wl.tree_off)
+    run0 = GpuRun(wl)
+    g0 = run0.run().outputs()
+    ref = oracle_verify(wl)
+    _print(check_verify(g0, ref, dims, label="degenerate"))
+    # plant the whole chain: every node's token is the GPU's argmax at its parent
+    tokens = wl.tokens.copy()
+    o = wl.tree_off[2]
+    for i in range(1, 128):
+        tokens[o + i] = g0["argmax"][o + i - 1]
+    wl.tokens = tokens
+    run = GpuRun(wl, want_logits=False)
+    run.run(accept=True)
+    g = run.outputs()
+    v = run.v
+    acc = v.accept_len.cpu().numpy()
+    nxt = v.next_token.cpu().numpy()
+    newP = run.t["prefix_len"].cpu().numpy()
+    assert g["status"] == 0
+    for b, par in enumerate(parents):
+        ob = wl.tree_off[b]
+        n = len(par)
+        L, pth, out, nt, leaf = oracle.accept_sequence(par, tokens[ob:ob + n], g["argmax"][ob:ob + n],
+                                                      g["depth"][ob:ob + n])
+        assert acc[b] == L and nxt[b] == nt and newP[b] == int(wl.prefix_len[b]) + L + 1
+    assert acc[0] == 0 and acc[1] == 0 and acc[2] == 127   # root-only trees accept only the bonus
+
+
+def test_accept_reports_cache_overflow():
+    """A sequence whose accepted path would run past the cache capacity gets accept_len -1,
+    no commit and EAGLE_ERR_CAPACITY in the device status; the other sequences commit."""
+    import tree_attention_verification_06_amd as E
+    dims = mini_dims()
+    parents = [T.chain(6), T.chain(6)]
+    wl = make_workload(2, seed=33, dims=dims, batch=2, prefix=[10, 10], parents=parents, cache_slack=0)
+    cap = wl.cache_cap
+    # sequence 1 starts 3 slots short of the end: committing its 6-node path cannot fit
+    wl.prefix_len = np.array([10, cap - 3], dtype=np.int32)
+    run0 = GpuRun(wl, want_logits=False, max_prefix=cap)
+    g0 = run0.run().outputs()
+    tokens = wl.tokens.copy()
+    for b in range(2):
+        o = wl.tree_off[b]
+        for i in range(1, 6):
+            tokens[o + i] = g0["argmax"][o + i - 1]
+    wl.tokens = tokens
+    run = GpuRun(wl, want_logits=False, max_prefix=cap)
+    pre_k = run.t["k_cache"].clone()
+    t, v = run.t, run.v
+    v.encode(t["tree_off"], t["parent"], t["prefix_len"], run.M)
+    v.verify(t["tree_off"], t["tokens"], t["prefix_len"], run.M, x=t["x"])
+    v.accept(t["tree_off"], t["parent"], t["tokens"], t["prefix_len"])
+    import torch
+    torch.cuda.synchronize()
+    assert int(v.status.item()) == E._abi.EAGLE_ERR_CAPACITY
+    acc = v.accept_len.cpu().numpy()
+    newP = t["prefix_len"].cpu().numpy()
+    assert acc[0] == 5 and newP[0] == 10 + 6
+    assert acc[1] == -1 and newP[1] == cap - 3
+    assert (bits(t["k_cache"][1]) == bits(pre_k[1])).all()
