@@ -102,10 +102,12 @@ struct GemmPlan {
   int cfg;       // tile configuration
   int splits;    // K splits
   int kps;       // K per split
-  int tile_cols; // output columns per tile
-  int tile_rows; // weight rows per tile (both blocks when dual)
+  int tile_cols; // output columns per epilogue tile
+  int tile_rows; // weight rows per workgroup tile (both blocks when dual)
   int mt;        // tokens per tile
-  int n_tiles, m_tiles;
+  int n_tiles;   // epilogue tiles along the output columns (what per-tile outputs are sized by)
+  int w_tiles;   // workgroup tiles along the output columns (n_tiles / epilogue halves)
+  int m_tiles;
 };
 
 GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int head_dim);

@@ -211,10 +211,10 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
     case EPI_ARGMAX: {
       // thread -> (token t, row stripe); rows are scanned in increasing order so the
       // first maximum wins, then stripes are merged through LDS with the packed key.
-      const int stripes = nth / mt;
+      const int stripes = nth / mt;  // threads past stripes * mt (mt not dividing nth) sit out
       const int t = tid % mt, st = tid / mt;
       unsigned long long best = 0ull;
-      if (t < mv) {
+      if (t < mv && st < stripes) {
         const float sc = scale[t];
         for (int r = st; r < tc; r += stripes) {
           const int c = col0 + r;
@@ -266,14 +266,15 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
       constexpr int KMAX = 16;
       const int K = e.topk;
       const int tile_i = col0 / tc;
-      const int P = nth / mt;
+      const int P = nth / mt;  // parts per token; threads past P * mt (mt not dividing nth) sit out
       const int t = tid % mt, part = tid / mt;
+      const bool active = part < P;
       const int ncol = min(tc, d.n - col0);
       unsigned long long lst[KMAX];
 #pragma unroll
       for (int q = 0; q < KMAX; ++q) lst[q] = 0ull;
       float mx = -INFINITY, se = 0.f;
-      if (t < mv) {
+      if (active && t < mv) {
         const float sc = scale[t];
         for (int r = part; r < ncol; r += P) mx = fmaxf(mx, sc * tile[r * ts + t]);
         for (int r = part; r < ncol; r += P) {
@@ -291,10 +292,12 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
       __syncthreads();  // every read of the tile is done: its LDS is reused below
       unsigned long long* sl = (unsigned long long*)tile;          // [P][mt][KMAX]
       float* sm = (float*)(sl + (size_t)P * mt * KMAX);             // [P][mt][2]
+      if (active) {
 #pragma unroll
-      for (int q = 0; q < KMAX; ++q) sl[((size_t)part * mt + t) * KMAX + q] = lst[q];
-      sm[(part * mt + t) * 2] = mx;
-      sm[(part * mt + t) * 2 + 1] = se;
+        for (int q = 0; q < KMAX; ++q) sl[((size_t)part * mt + t) * KMAX + q] = lst[q];
+        sm[(part * mt + t) * 2] = mx;
+        sm[(part * mt + t) * 2 + 1] = se;
+      }
       __syncthreads();
       if (part == 0 && t < mv) {
         float M = -INFINITY;
@@ -350,33 +353,64 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uin
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// Split-K fixup: tile = sum over splits (in split order) of the S partial tiles of NF4
-// fragments each.  All loads of a pass are issued before the first add, so the round
-// trips to memory overlap.
-template <int S, int NF4, int MT_, int TS_, int NTH_>
-__device__ __forceinline__ void sum_partials(const float* p0, float* tile) {
+// Epilogue halves: a tile whose fp32 output would not fit LDS runs its epilogue twice, on
+// half of its weight-row blocks each time.  Block blk (of NB) belongs to half h and is
+// block lb of that half's tile; for gate/up tiles each half holds matching gate and up
+// column blocks (gate blocks first), so it is itself a gate/up tile of half the columns.
+template <int EH, bool DUAL, int NB>
+__device__ __forceinline__ int half_to_block(int h, int lb) {
+  if (EH == 1) return lb;
+  if (!DUAL) return h * (NB / 2) + lb;
+  constexpr int Q = NB / 4;  // gate (or up) blocks per half
+  return lb < Q ? h * Q + lb : NB / 2 + h * Q + (lb - Q);
+}
+template <int EH, bool DUAL, int NB>
+__device__ __forceinline__ bool block_in_half(int blk, int h, int* lb) {
+  if (EH == 1) {
+    *lb = blk;
+    return true;
+  }
+  if (!DUAL) {
+    *lb = blk % (NB / 2);
+    return blk / (NB / 2) == h;
+  }
+  constexpr int Q = NB / 4;
+  const bool up = blk >= NB / 2;
+  const int b2 = up ? blk - NB / 2 : blk;
+  *lb = (up ? Q : 0) + b2 % Q;
+  return b2 / Q == h;
+}
+
+// Split-K fixup of epilogue half h: tile = sum over splits (in split order) of the S partial
+// tiles of NF4 fragments each.  All loads of a pass are issued before the first add, so
+// the round trips to memory overlap.
+template <int S, int NF4, int MT_, int TS_, int NTH_, int EH, bool DUAL, int NB>
+__device__ __forceinline__ void sum_partials(const float* p0, float* tile, int h) {
   constexpr int G = S <= 2 ? 4 : (S <= 4 ? 2 : 1);  // fragments per thread per pass
+  constexpr int NFH = NF4 / EH;                     // fragments of one half
   const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p0, (uint32_t)S * NF4 * 16);
-  for (int f0 = threadIdx.x; f0 < NF4; f0 += NTH_ * G) {
+  for (int f0 = threadIdx.x; f0 < NFH; f0 += NTH_ * G) {
     f32x4 a[S][G];
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const int f = min(f0 + g * NTH_, NF4 - 1);
+        const int fl = min(f0 + g * NTH_, NFH - 1);  // fragment of the half tile
+        const int bt = fl / 64;
+        const int f = (half_to_block<EH, DUAL, NB>(h, bt / (MT_ / 16)) * (MT_ / 16) + bt % (MT_ / 16)) * 64 + fl % 64;
         a[s][g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (s * NF4 + f) * 16, 0, kSc1));
       }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int f = f0 + g * NTH_;
-      if (f >= NF4) break;
+      const int fl = f0 + g * NTH_;
+      if (fl >= NFH) break;
       f32x4 v = a[0][g];
 #pragma unroll
       for (int s = 1; s < S; ++s) v += a[s][g];
-      // fragment f: 16-row block blk, 16-token block t, lane l -> rows blk*16 + (l/16)*4 + i
-      const int l = f % 64, bt = f / 64;
-      const int t = bt % (MT_ / 16), blk = bt / (MT_ / 16);
-      float* dst = tile + (blk * 16 + (l / 16) * 4) * TS_ + t * 16 + (l % 16);
+      // fragment: 16-row block lb, 16-token block t, lane l -> rows lb*16 + (l/16)*4 + i
+      const int l = fl % 64, bt = fl / 64;
+      const int t = bt % (MT_ / 16), lb = bt / (MT_ / 16);
+      float* dst = tile + (lb * 16 + (l / 16) * 4) * TS_ + t * 16 + (l % 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[i * TS_] = v[i];
     }
@@ -387,11 +421,12 @@ __device__ __forceinline__ void sum_partials(const float* p0, float* tile) {
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------------
 // Tile shapes: NW waves x RB 16-row weight blocks per wave, MT tokens, K chunks of KC,
-// XB X-chunk buffers in LDS (1: the next chunk is stored after a barrier).  Wider token
+// XB X-chunk buffers in LDS (1: the next chunk is stored after a barrier), EH epilogue
+// halves (2: the fp32 output tile is formed and consumed one half at a time).  Wider token
 // tiles (MT 128 / 256) use shorter K chunks so that the X chunks and the output tile both
 // fit the 160 KB of LDS; each weight byte is then streamed once per MT tokens instead of
 // once per 64.
-template <int NW, int RB, int PD, bool DUAL, int MT, int KC, int XB>
+template <int NW, int RB, int PD, bool DUAL, int MT, int KC, int XB, int EH>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid_real) {
   constexpr int NT = NW * RB * 16;        // weight rows per tile (both blocks when DUAL)
   constexpr int TC = DUAL ? NT / 2 : NT;  // output columns per tile
@@ -399,7 +434,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   constexpr int XS = KC + 8;              // LDS row stride of an X chunk (bf16)
   constexpr int TS = MT + 4;              // LDS row stride of the output tile (f32)
   constexpr int LDS_X = XB * MT * XS * 2;  // X chunk buffers
-  constexpr int LDS_T = NT * TS * 4;
+  constexpr int LDS_T = NT / EH * TS * 4;  // one epilogue half of the output tile
+  constexpr int NB = NT / 16;               // 16-row weight blocks per tile
   constexpr int LDS = LDS_X > LDS_T ? LDS_X : LDS_T;
   constexpr int LPR = KC / 8;             // lanes staging one X row (16 bytes each)
   constexpr int RPP = 64 / LPR;           // X rows per wave per pass
@@ -440,6 +476,30 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   // the weight lines the first one fetches are still in that XCD's L2 for the others
   const int nchunk = (ke - kb + KC - 1) / KC;
   const int c0 = (nt_i * 5 + split * 3) % nchunk;
+
+  // norm == 2: the row sums of squares arrive as np per-tile partials.  Their loads are
+  // issued here, spread over all threads (part = tid / MT, 4 loads in flight per thread),
+  // so the round trips hide under the main loop; the tail adds the parts in fixed order.
+  constexpr int NPART = NTH / MT;
+  float* s_np = (float*)s_red;  // [NPART][MT]; s_red is not used before the epilogue
+  if (d.x.norm == 2) {
+    const int row = tid % MT, part = tid / MT;
+    if (part < NPART) {
+      const int m = min(m0 + row, d.m - 1);
+      float v = 0.f;
+      for (int p0 = part; p0 < d.x.np; p0 += 4 * NPART) {
+        float a4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int p = min(p0 + u * NPART, d.x.np - 1);
+          a4[u] = d.x.ssq_in[(int64_t)p * d.m + m];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v += (p0 + u * NPART < d.x.np) ? a4[u] : 0.f;
+      }
+      s_np[part * MT + row] = v;
+    }
+  }
 
   // this wave's weight rows
   const bf16* wblk;
@@ -605,15 +665,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
     if (d.x.norm == 1) return rsqrtf(ssq_total / (float)d.k + d.x.eps);
     return 1.f;
   };
-  if (d.splits == 1) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int t = 0; t < MT / 16; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tile[((wid * RB + rb) * 16 + lq * 4 + i) * TS + t * 16 + lr] = acc[rb][t][i];
-    if (tid < MT) s_scale[tid] = row_scale(s_ssq[tid]);
-  } else {
+  if (d.splits > 1) {
     // split-K: publish this split's partial tile; the last split of the tile to arrive
     // sums all partials in split order (deterministic) and runs the epilogue
     float* part = d.partials + ((int64_t)tile_id * d.splits + split) * (NT * MT);
@@ -633,33 +685,52 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
       s_flag = (old == d.splits - 1);
     }
     __syncthreads();
-    if (!s_flag) return;
-    const float* p0 = d.partials + (int64_t)tile_id * d.splits * (NT * MT);
-    switch (d.splits) {
-      case 2: sum_partials<2, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
-      case 3: sum_partials<3, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
-      case 4: sum_partials<4, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
-      case 5: sum_partials<5, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
-      case 6: sum_partials<6, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
-      case 7: sum_partials<7, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
-      default: sum_partials<8, NT * MT / 4, MT, TS, NTH>(p0, tile); break;
-    }
+    if (!s_flag) return;  // another split runs this tile's epilogue
     if (tid < MT) {
       float v = 0.f;
       for (int s = 0; s < d.splits; ++s) v += coherent_load(d.sumsq_part + ((int64_t)tile_id * d.splits + s) * MT + tid);
-      s_scale[tid] = row_scale(v);
+      s_ssq[tid] = v;
     }
     if (tid == 0) __hip_atomic_store(&d.counters[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (d.x.norm == 2 && tid < MT) {
-    float v = 0.f;
-    const int m = min(m0 + tid, d.m - 1);
-    for (int p = 0; p < d.x.np; ++p) v += d.x.ssq_in[(int64_t)p * d.m + m];
-    s_scale[tid] = rsqrtf(v / (float)d.k + d.x.eps);
+  if (tid < MT) {
+    float sc = row_scale(s_ssq[tid]);
+    if (d.x.norm == 2) {
+      float v = 0.f;
+      for (int part = 0; part < NPART; ++part) v += s_np[part * MT + tid];
+      sc = rsqrtf(v / (float)d.k + d.x.eps);
+    }
+    s_scale[tid] = sc;
   }
-  __syncthreads();
-  run_epilogue(d, tile, TS, TC, col0, m0, mv, MT, s_scale, (float*)s_red, &s_flag,
-               ((d.n + TC - 1) / TC) * m_tiles);
+  constexpr int TCH = TC / EH;  // output columns of one epilogue half
+  const int n_epi = ((d.n + TC - 1) / TC) * m_tiles * EH;
+  for (int h = 0; h < EH; ++h) {
+    if (h) __syncthreads();  // the previous half's epilogue is done with the tile
+    if (d.splits == 1) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        int lb;
+        if (!block_in_half<EH, DUAL, NB>(wid * RB + rb, h, &lb)) continue;  // wave-uniform
+#pragma unroll
+        for (int t = 0; t < MT / 16; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tile[(lb * 16 + lq * 4 + i) * TS + t * 16 + lr] = acc[rb][t][i];
+      }
+    } else {
+      const float* p0 = d.partials + (int64_t)tile_id * d.splits * (NT * MT);
+      switch (d.splits) {
+        case 2: sum_partials<2, NT * MT / 4, MT, TS, NTH, EH, DUAL, NB>(p0, tile, h); break;
+        case 3: sum_partials<3, NT * MT / 4, MT, TS, NTH, EH, DUAL, NB>(p0, tile, h); break;
+        case 4: sum_partials<4, NT * MT / 4, MT, TS, NTH, EH, DUAL, NB>(p0, tile, h); break;
+        case 5: sum_partials<5, NT * MT / 4, MT, TS, NTH, EH, DUAL, NB>(p0, tile, h); break;
+        case 6: sum_partials<6, NT * MT / 4, MT, TS, NTH, EH, DUAL, NB>(p0, tile, h); break;
+        case 7: sum_partials<7, NT * MT / 4, MT, TS, NTH, EH, DUAL, NB>(p0, tile, h); break;
+        default: sum_partials<8, NT * MT / 4, MT, TS, NTH, EH, DUAL, NB>(p0, tile, h); break;
+      }
+    }
+    __syncthreads();
+    run_epilogue(d, tile, TS, TCH, col0 + h * TCH, m0, mv, MT, s_scale, (float*)s_red, &s_flag, n_epi);
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -728,17 +799,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d, int grid_real
 }
 
 struct CfgInfo {
-  int nw, rb, pd, mt, kc;
+  int nw, rb, pd, mt, kc, eh;
 };
 // 0-2: 64-token tiles for a few dozen rows (weight streaming); 3: 4 waves (kept, not
-// planned: too few loads in flight); 4, 5: 128- and 256-token tiles for hundreds of rows.
-constexpr CfgInfo kCfgs[6] = {{8, 4, 4, 64, 512}, {8, 2, 4, 64, 512}, {8, 1, 8, 64, 512},
-                              {4, 1, 8, 64, 512}, {8, 2, 4, 128, 256}, {8, 1, 4, 256, 128}};
+// planned: too few loads in flight); 4, 5: 128- and 256-token tiles for hundreds of rows;
+// 6, 7: 256 weight rows x 192 / 160 tokens with the epilogue in two halves (every weight
+// byte read once for up to 256 rows, two 16-row blocks per wave).
+constexpr CfgInfo kCfgs[8] = {{8, 4, 4, 64, 512, 1},  {8, 2, 4, 64, 512, 1},  {8, 1, 8, 64, 512, 1},
+                              {4, 1, 8, 64, 512, 1},  {8, 2, 4, 128, 256, 1}, {8, 1, 4, 256, 128, 1},
+                              {8, 2, 4, 192, 128, 2}, {8, 2, 4, 160, 128, 2}};
 
-template <int NW, int RB, int PD, bool DUAL, int MT, int KC, int XB>
+template <int NW, int RB, int PD, bool DUAL, int MT, int KC, int XB, int EH = 1>
 void launch_cfg(const GemmDesc& d, int grid, hipStream_t s) {
   const int padded = (grid + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((gemm_bf16_kernel<NW, RB, PD, DUAL, MT, KC, XB>), dim3(padded), dim3(NW * 64), 0, s, d, grid);
+  hipLaunchKernelGGL((gemm_bf16_kernel<NW, RB, PD, DUAL, MT, KC, XB, EH>), dim3(padded), dim3(NW * 64), 0, s, d,
+                     grid);
 }
 
 }  // namespace
@@ -753,27 +828,31 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
     p.tile_cols = dual ? F32_NT / 2 : F32_NT;
     p.mt = F32_MT;
     p.n_tiles = (n + p.tile_cols - 1) / p.tile_cols;
+    p.w_tiles = p.n_tiles;
     p.m_tiles = (m + F32_MT - 1) / F32_MT;
     return p;
   }
   // Cost model (microseconds), fitted to measured launch times of every tile configuration
-  // and split count at the 8B- and 70B-shaped projections with 16..960 tokens (rms error
-  // ~15%).  Each workgroup needs most of a CU's LDS, so workgroups run in rounds of 256.
-  // Per workgroup: its weight slice streams at min(38 GB/s, 6.8 TB/s / resident
-  // workgroups) while its MFMAs run (4.0 TFLOP/s per CU with one 16-row block per wave,
-  // 12.7 with more: X comes from LDS once per block), plus its X slice from L2 at 75 GB/s,
-  // a fixed ~8 us (launch, pipeline fill, epilogue), and the write of its split-K partial.
+  // and split count at the 8B- and 70B-shaped projections with 16..960 tokens, each launch
+  // timed with cold caches (a 768 MB read first evicts the 256 MB Infinity Cache, as the
+  // rest of a step does); rms error ~12%, MFMA rates bounded by the chip's peak.  Each
+  // workgroup needs most of a CU's LDS, so workgroups run in rounds of 256.  Per
+  // workgroup: its weight slice streams at min(31 GB/s, 7.4 TB/s / resident workgroups)
+  // while its MFMAs run (~4.5 TFLOP/s per CU), plus its X slice from L2 at 49 GB/s, a
+  // fixed ~10 us (launch, pipeline fill, epilogue) and the write of its split-K partial.
   // Split-K adds a serial tail: the last workgroup of a tile reads every partial tile at
-  // ~60 GB/s.  The top-k epilogue costs ~1.1 us per 1000 (token, column) pairs of a tile.
-  constexpr double kBcu = 35.6e3, kBchip = 6.65e6, kBx = 75e3, kP1 = 4.0e6, kP2 = 12.7e6, kF0 = 8.4,
-                   kBfix = 59.6e3, kFsplit = 0.76, kTopk = 10.8e-4;  // bytes/us, flop/us, us
+  // ~64 GB/s, plus ~3.6 us.  The top-k epilogue costs ~1.2 us per 1000 (token, column)
+  // pairs of a tile.
+  constexpr double kBcu = 30.5e3, kBchip = 7.38e6, kBx = 48.7e3, kP1 = 4.61e6, kP2 = 4.45e6, kF0 = 10.0,
+                   kBfix = 64.4e3, kFsplit = 3.63, kTopk = 11.8e-4;  // bytes/us, flop/us, us
   double best = 1e30;
   int best_c = -1, best_s = 1;
-  for (int c : {0, 1, 2, 4, 5}) {
+  for (int c : {0, 1, 2, 4, 5, 6, 7}) {
     const CfgInfo& cf = kCfgs[c];
     const int nt = cf.nw * cf.rb * 16;
     const int tc = dual ? nt / 2 : nt;
-    if (epi_kind == EPI_QKV && tc % head_dim) continue;
+    if (epi_kind == EPI_QKV && (tc / cf.eh) % head_dim) continue;
+    if (dual && c == 6) continue;  // its gate/up instance spills registers
     const int m_tiles = (m + cf.mt - 1) / cf.mt;
     const int kchunks = (k + cf.kc - 1) / cf.kc;
     const int tiles = ((n + tc - 1) / tc) * m_tiles;
@@ -805,15 +884,17 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
   p.splits = best_s;
   p.kps = ((kchunks + best_s - 1) / best_s) * cf.kc;
   p.tile_rows = cf.nw * cf.rb * 16;
-  p.tile_cols = dual ? p.tile_rows / 2 : p.tile_rows;
+  const int wcols = dual ? p.tile_rows / 2 : p.tile_rows;  // output columns per weight tile
+  p.tile_cols = wcols / cf.eh;
   p.mt = cf.mt;
-  p.n_tiles = (n + p.tile_cols - 1) / p.tile_cols;
+  p.w_tiles = (n + wcols - 1) / wcols;
+  p.n_tiles = p.w_tiles * cf.eh;
   p.m_tiles = (m + cf.mt - 1) / cf.mt;
   return p;
 }
 
 void gemm_workspace(const GemmPlan& p, size_t* partial_floats, size_t* sumsq_floats, size_t* counter_ints) {
-  const size_t tiles = (size_t)p.n_tiles * p.m_tiles;
+  const size_t tiles = (size_t)p.w_tiles * p.m_tiles;
   if (p.splits > 1) {
     *partial_floats = tiles * p.splits * p.tile_rows * p.mt;
     *sumsq_floats = tiles * p.splits * p.mt;
@@ -832,7 +913,7 @@ int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s) {
   if (d.k % 32 || (d.x.ka % 8) || p.cfg < 0) return EAGLE_ERR_UNSUPPORTED;
   if (p.cfg != 100 && (d.x.a.dtype != EAGLE_BF16 || d.x.b.dtype != EAGLE_BF16)) return EAGLE_ERR_UNSUPPORTED;
   if (p.cfg == 100 && d.epi.kind == EPI_TOPK) return EAGLE_ERR_UNSUPPORTED;  // its LDS tile is too small
-  const int grid = p.n_tiles * p.m_tiles * p.splits;
+  const int grid = p.w_tiles * p.m_tiles * p.splits;
   if (grid <= 0) return EAGLE_OK;
   if (p.cfg == 100) {
     const int padded = (grid + kXcds - 1) / kXcds * kXcds;
@@ -846,6 +927,8 @@ int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s) {
       case 3: dual ? launch_cfg<4, 1, 8, true, 64, 512, 2>(d, grid, s) : launch_cfg<4, 1, 8, false, 64, 512, 2>(d, grid, s); break;
       case 4: dual ? launch_cfg<8, 2, 4, true, 128, 256, 2>(d, grid, s) : launch_cfg<8, 2, 4, false, 128, 256, 2>(d, grid, s); break;
       case 5: dual ? launch_cfg<8, 1, 4, true, 256, 128, 2>(d, grid, s) : launch_cfg<8, 1, 4, false, 256, 128, 2>(d, grid, s); break;
+      case 6: dual ? launch_cfg<8, 2, 4, true, 192, 128, 2, 2>(d, grid, s) : launch_cfg<8, 2, 4, false, 192, 128, 2, 2>(d, grid, s); break;
+      case 7: dual ? launch_cfg<8, 2, 4, true, 160, 128, 2, 2>(d, grid, s) : launch_cfg<8, 2, 4, false, 160, 128, 2, 2>(d, grid, s); break;
       default: return EAGLE_ERR_UNSUPPORTED;
     }
   }
