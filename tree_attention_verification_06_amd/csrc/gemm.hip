@@ -216,9 +216,23 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
       unsigned long long best = 0ull;
       if (t < mv && st < stripes) {
         const float sc = scale[t];
-        for (int r = st; r < tc; r += stripes) {
+        const int rlim = min(tc, d.n - col0);
+        int r = st;
+        if (!e.dbg_logits) {
+          // 8 rows per round: the LDS reads of a round are issued before any use
+          for (; r + 7 * stripes < rlim; r += 8 * stripes) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = tile[(r + u * stripes) * ts + t];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const unsigned long long key = argmax_key(sc * v[u], (uint32_t)(col0 + r + u * stripes));
+              best = key > best ? key : best;
+            }
+          }
+        }
+        for (; r < rlim; r += stripes) {
           const int c = col0 + r;
-          if (c >= d.n) break;
           const float v = sc * tile[r * ts + t];
           if (e.dbg_logits) e.dbg_logits[(int64_t)(m0 + t) * e.ld_logits + c] = v;
           const unsigned long long key = argmax_key(v, (uint32_t)c);
@@ -386,8 +400,14 @@ __device__ __forceinline__ bool block_in_half(int blk, int h, int* lb) {
 // the round trips to memory overlap.
 template <int S, int NF4, int MT_, int TS_, int NTH_, int EH, bool DUAL, int NB>
 __device__ __forceinline__ void sum_partials(const float* p0, float* tile, int h) {
-  constexpr int G = S <= 2 ? 4 : (S <= 4 ? 2 : 1);  // fragments per thread per pass
-  constexpr int NFH = NF4 / EH;                     // fragments of one half
+  constexpr int NFH = NF4 / EH;  // fragments of one half
+  // fragments per thread per pass: up to 32 loads of 16 bytes in flight per thread (the
+  // main loop's registers are free by now), so a tile usually takes a single round trip;
+  // tiles with two epilogue halves keep their accumulators live meanwhile and take 8
+  constexpr int LOADS = EH == 1 ? 32 : 8;
+  constexpr int GMAX = LOADS / S > 0 ? LOADS / S : 1;
+  constexpr int GNEED = (NFH + NTH_ - 1) / NTH_;
+  constexpr int G = GMAX < GNEED ? GMAX : GNEED;
   const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p0, (uint32_t)S * NF4 * 16);
   for (int f0 = threadIdx.x; f0 < NFH; f0 += NTH_ * G) {
     f32x4 a[S][G];
@@ -482,7 +502,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   // so the round trips hide under the main loop; the tail adds the parts in fixed order.
   constexpr int NPART = NTH / MT;
   float* s_np = (float*)s_red;  // [NPART][MT]; s_red is not used before the epilogue
-  if (d.x.norm == 2) {
+  // Up to 4 partials per thread stay in registers, unsummed, until after the main loop, so
+  // nothing waits for them here; more than that are summed (and waited for) right away.
+  const bool np_regs = d.x.norm == 2 && d.x.np <= 4 * NPART;
+  float np_a[4] = {0.f, 0.f, 0.f, 0.f};
+  if (np_regs) {
+    const int row = tid % MT, part = tid / MT;
+    const int m = min(m0 + row, d.m - 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = min(min(part, NPART - 1) + u * NPART, d.x.np - 1);
+      np_a[u] = d.x.ssq_in[(int64_t)p * d.m + m];
+    }
+  } else if (d.x.norm == 2) {
     const int row = tid % MT, part = tid / MT;
     if (part < NPART) {
       const int m = min(m0 + row, d.m - 1);
@@ -656,6 +688,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
 #pragma unroll
     for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     if (lane % LPR == 0) s_ssq[(wid + j * NW) * RPP + xl_row] = v;
+  }
+  if (np_regs) {
+    const int row = tid % MT, part = tid / MT;
+    if (part < NPART) {
+      float v = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v += (part + u * NPART < d.x.np) ? np_a[u] : 0.f;
+      s_np[part * MT + row] = v;
+    }
   }
   __syncthreads();
 
