@@ -69,6 +69,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// N independent sums over aligned groups of W lanes (W a power of two, <= 64), every lane
+// of a group ending with its group's sum.  The shuffle distance is the outer loop, so each
+// round issues the shuffles of all N values before waiting for any of them.
+template <int N, int W>
+__device__ __forceinline__ void group_sum_n(float (&v)[N]) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) {
+    float t[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) t[j] = __shfl_xor(v[j], o, 64);
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] += t[j];
+  }
+}
 
 // Per-launch HIP event timing (optional).
 struct Timer;

@@ -125,12 +125,13 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
             rv[u][q] = (e.kind == EPI_RESID && e.resid) ? load_elem(e.resid, e.resid_dtype, rrow * e.ld_resid + c) : 0.f;
           }
         }
+        float ss[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int t = t0 + u;
-          if (t >= mv) break;
+          ss[u] = 0.f;
+          if (t >= mv) continue;
           const int m = m0 + t;
-          float ss = 0.f;
 #pragma unroll
           for (int q = 0; q < CPL; ++q) {
             const int r = lane + 64 * q;
@@ -138,14 +139,16 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
             if (q < cpl && r < tc && c < d.n) {
               const float v = scale[t] * tile[r * ts + t] + rv[u][q];
               e.out[(int64_t)m * e.ld_out + c] = v;
-              ss += v * v;
+              ss[u] += v * v;
               if (e.xn_out) ((bf16*)e.xn_out)[(int64_t)m * e.ld_out + c] = f2bf(gv[q] * v);
             }
           }
-          if (e.ssq_out) {
-            ss = wave_sum(ss);
-            if (lane == 0) e.ssq_out[(int64_t)tile_i * d.m + m] = ss;
-          }
+        }
+        if (e.ssq_out) {
+          group_sum_n<U, 64>(ss);
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (lane == 0 && t0 + u < mv) e.ssq_out[(int64_t)tile_i * d.m + m0 + t0 + u] = ss[u];
         }
       }
       break;
@@ -682,12 +685,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   }
 
   // row sums of squares of this K range (norm == 1): the LPR lanes of a row are adjacent
+  if (d.x.norm == 1) {
+    group_sum_n<RPW, LPR>(ssq);
 #pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    float v = ssq[j];
-#pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    if (lane % LPR == 0) s_ssq[(wid + j * NW) * RPP + xl_row] = v;
+    for (int j = 0; j < RPW; ++j)
+      if (lane % LPR == 0) s_ssq[(wid + j * NW) * RPP + xl_row] = ssq[j];
   }
   if (np_regs) {
     const int row = tid % MT, part = tid / MT;
@@ -718,7 +720,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
         const int f = ((wid * RB + rb) * (MT / 16) + t) * 64 + lane;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[rb][t]), prs, f * 16, 0, kSc1);
       }
-    if (tid < MT) coherent_store(d.sumsq_part + ((int64_t)tile_id * d.splits + split) * MT + tid, s_ssq[tid]);
+    if (d.x.norm == 1 && tid < MT)
+      coherent_store(d.sumsq_part + ((int64_t)tile_id * d.splits + split) * MT + tid, s_ssq[tid]);
     wait_memory();
     __syncthreads();
     if (tid == 0) {
@@ -727,7 +730,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
     }
     __syncthreads();
     if (!s_flag) return;  // another split runs this tile's epilogue
-    if (tid < MT) {
+    if (d.x.norm == 1 && tid < MT) {
       float v = 0.f;
       for (int s = 0; s < d.splits; ++s) v += coherent_load(d.sumsq_part + ((int64_t)tile_id * d.splits + s) * MT + tid);
       s_ssq[tid] = v;
