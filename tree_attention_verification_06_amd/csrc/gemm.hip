@@ -90,9 +90,85 @@ __device__ __forceinline__ void rope_cs(int pos, double inv, float* c, float* s)
   sincosf((float)r, s, c);
 }
 
+// EPI_STORE_F32 / EPI_RESID over a finished tile (tc <= 64 * CPL columns): token-major, a
+// wave per token row and lanes along the columns (coalesced stores); the row's sum of
+// squares over this tile is a wave reduction.  A wave takes U consecutive rows at a time
+// and issues all their residual loads (U * CPL per lane) before any use, so one round trip
+// covers them.  Every load is unconditional (RT is the residual's element type; with no
+// residual, gain or row map the loads read a stand-in address inside the output and a
+// select drops the value): a load under a branch would be waited for at the join.
+template <int CPL, int U, typename RT>
+__device__ __forceinline__ void epi_store_rows(const GemmDesc& d, const float* tile, int ts, int tc, int col0, int m0,
+                                               int mv, const float* scale) {
+  const Epi& e = d.epi;
+  const int nw = blockDim.x / 64, w = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int tile_i = col0 / tc;
+  const bool has_res = e.kind == EPI_RESID && e.resid;
+  const bool has_idx = has_res && e.resid_idx;
+  const bool has_gain = e.xn_out && e.xn_gain;
+  const RT* rp = has_res ? (const RT*)e.resid : (const RT*)e.out;
+  const int64_t rld = has_res ? e.ld_resid : e.ld_out;
+  const int32_t* ip = has_idx ? e.resid_idx : (const int32_t*)e.out;
+  const bf16* gp = has_gain ? (const bf16*)e.xn_gain : (const bf16*)e.out;
+  float gv[CPL];
+#pragma unroll
+  for (int q = 0; q < CPL; ++q) {
+    const int c = min(col0 + lane + 64 * q, d.n - 1);
+    const float g = bf2f(gp[c]);
+    gv[q] = has_gain ? g : 1.f;
+  }
+  for (int t0 = w * U; t0 < mv; t0 += nw * U) {
+    int64_t rrow[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int m = m0 + min(t0 + u, mv - 1);
+      const int32_t im = ip[m];
+      rrow[u] = has_idx ? (int64_t)im : (int64_t)m;
+    }
+    float rv[U][CPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const int c = min(col0 + lane + 64 * q, d.n - 1);
+        const RT v = rp[rrow[u] * rld + c];
+        float f;
+        if constexpr (sizeof(RT) == 2) f = bf2f(v); else f = v;
+        rv[u][q] = has_res ? f : 0.f;
+      }
+    float ss[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u;
+      ss[u] = 0.f;
+      if (t >= mv) continue;
+      const int m = m0 + t;
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const int r = lane + 64 * q;
+        const int c = col0 + r;
+        if (r < tc && c < d.n) {
+          const float v = scale[t] * tile[r * ts + t] + rv[u][q];
+          e.out[(int64_t)m * e.ld_out + c] = v;
+          ss[u] += v * v;
+          if (e.xn_out) ((bf16*)e.xn_out)[(int64_t)m * e.ld_out + c] = f2bf(gv[q] * v);
+        }
+      }
+    }
+    if (e.ssq_out) {
+      group_sum_n<U, 64>(ss);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (lane == 0 && t0 + u < mv) e.ssq_out[(int64_t)tile_i * d.m + m0 + t0 + u] = ss[u];
+    }
+  }
+}
+
 // Fused epilogue over a finished fp32 tile in LDS: tile[r * ts + t] is output column
 // col0 + r (for dual tiles: gate columns r < tc, up columns r >= tc) of token m0 + t,
 // before the per-row norm scale scale[t].
+// CPLC: output columns per lane of the store epilogue, ceil(tc / 64) at most.
+template <int CPLC>
 __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int tc, int col0, int m0, int mv,
                              int mt, const float* scale, float* red_scratch, int* s_flag, int n_epi) {
   const Epi& e = d.epi;
@@ -100,57 +176,11 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
   switch (e.kind) {
     case EPI_STORE_F32:
     case EPI_RESID: {
-      // token-major: a wave per token row, lanes along the columns (coalesced stores); the
-      // row's sum of squares over this tile is a wave reduction.  The residual loads of U
-      // rows are issued together before any use, so their round trips overlap.
-      constexpr int U = 4, CPL = 8;  // rows per batch, max columns per lane (tc <= 512)
-      const int nw = nth / 64, w = tid / 64, lane = tid % 64;
-      const int tile_i = col0 / tc;
-      const int cpl = (tc + 63) / 64;
-      float gv[CPL];
-#pragma unroll
-      for (int q = 0; q < CPL; ++q) {
-        const int c = min(col0 + lane + 64 * min(q, cpl - 1), d.n - 1);
-        gv[q] = (e.xn_out && e.xn_gain) ? bf2f(((const bf16*)e.xn_gain)[c]) : 1.f;
-      }
-      for (int t0 = w * U; t0 < mv; t0 += nw * U) {
-        float rv[U][CPL];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int m = m0 + min(t0 + u, mv - 1);
-          const int64_t rrow = (e.kind == EPI_RESID && e.resid_idx) ? (int64_t)e.resid_idx[m] : (int64_t)m;
-#pragma unroll
-          for (int q = 0; q < CPL; ++q) {
-            const int c = min(col0 + lane + 64 * min(q, cpl - 1), d.n - 1);
-            rv[u][q] = (e.kind == EPI_RESID && e.resid) ? load_elem(e.resid, e.resid_dtype, rrow * e.ld_resid + c) : 0.f;
-          }
-        }
-        float ss[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int t = t0 + u;
-          ss[u] = 0.f;
-          if (t >= mv) continue;
-          const int m = m0 + t;
-#pragma unroll
-          for (int q = 0; q < CPL; ++q) {
-            const int r = lane + 64 * q;
-            const int c = col0 + r;
-            if (q < cpl && r < tc && c < d.n) {
-              const float v = scale[t] * tile[r * ts + t] + rv[u][q];
-              e.out[(int64_t)m * e.ld_out + c] = v;
-              ss[u] += v * v;
-              if (e.xn_out) ((bf16*)e.xn_out)[(int64_t)m * e.ld_out + c] = f2bf(gv[q] * v);
-            }
-          }
-        }
-        if (e.ssq_out) {
-          group_sum_n<U, 64>(ss);
-#pragma unroll
-          for (int u = 0; u < U; ++u)
-            if (lane == 0 && t0 + u < mv) e.ssq_out[(int64_t)tile_i * d.m + m0 + t0 + u] = ss[u];
-        }
-      }
+      constexpr int U = CPLC >= 16 ? 1 : 16 / CPLC;
+      if (e.kind == EPI_RESID && e.resid && e.resid_dtype == EAGLE_BF16)
+        epi_store_rows<CPLC, U, bf16>(d, tile, ts, tc, col0, m0, mv, scale);
+      else
+        epi_store_rows<CPLC, U, float>(d, tile, ts, tc, col0, m0, mv, scale);
       break;
     }
     case EPI_SILU: {
@@ -573,9 +603,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   uint4 xr[RPW];
   uint4 gr = make_uint4(0u, 0u, 0u, 0u);  // norm == 1: the 8 gain values of this lane's columns
   const bool stage_gain = d.x.norm == 1 && d.x.gain;
+  // the gain load is unconditional (a load under a branch is waited for at the join); with
+  // no gain it reads the weights (at least k elements) and the value is not used
+  const bf16* gain_src = stage_gain ? (const bf16*)d.x.gain : (const bf16*)d.w0;
   auto load_x = [&](int kc) {
     const int k = min(kc + xl_col, ke - 8);  // clamped: out-of-range lanes are zeroed at store
-    if (stage_gain) gr = *(const uint4*)((const bf16*)d.x.gain + k);
+    gr = *(const uint4*)(gain_src + k);
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
       const bool in_a = k < d.x.ka;
@@ -630,14 +663,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   // before merging the ring register, which serialises the stream.
   bf16x8_t wbuf[PD][RB];
   {
+    // the first X chunk is requested before the weight ring: loads return in order, so
+    // the chunk (and the barrier after it) waits for one round trip, not for the whole ring
     const int kc = chunk_k(0);
+    load_x(kc);
 #pragma unroll
     for (int s = 0; s < PD; ++s) {
       const int k = min(kc + s * 32, klast);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) wbuf[s][rb] = *(const bf16x8_t*)(wp[rb] + k);
     }
-    load_x(kc);
     store_x(0, kc, 1.f);
   }
   __syncthreads();
@@ -773,7 +808,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
       }
     }
     __syncthreads();
-    run_epilogue(d, tile, TS, TCH, col0 + h * TCH, m0, mv, MT, s_scale, (float*)s_red, &s_flag, n_epi);
+    run_epilogue<(TCH + 63) / 64>(d, tile, TS, TCH, col0 + h * TCH, m0, mv, MT, s_scale, (float*)s_red, &s_flag,
+                                  n_epi);
   }
 }
 
@@ -839,19 +875,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d, int grid_real
   __syncthreads();
   const int tc = d.dual ? F32_NT / 2 : F32_NT;
   const int c0 = d.dual ? col0 / 2 : col0;
-  run_epilogue(d, tile, TS, tc, c0, m0, mv, F32_MT, s_scale, (float*)s_red, &s_flag, grid_real);
+  run_epilogue<(F32_NT + 63) / 64>(d, tile, TS, tc, c0, m0, mv, F32_MT, s_scale, (float*)s_red, &s_flag, grid_real);
 }
 
 struct CfgInfo {
   int nw, rb, pd, mt, kc, eh;
 };
-// 0-2: 64-token tiles for a few dozen rows (weight streaming); 3: 4 waves (kept, not
-// planned: too few loads in flight); 4, 5: 128- and 256-token tiles for hundreds of rows;
-// 6, 7: 256 weight rows x 192 / 160 tokens with the epilogue in two halves (every weight
-// byte read once for up to 256 rows, two 16-row blocks per wave).
-constexpr CfgInfo kCfgs[8] = {{8, 4, 4, 64, 512, 1},  {8, 2, 4, 64, 512, 1},  {8, 1, 8, 64, 512, 1},
-                              {4, 1, 8, 64, 512, 1},  {8, 2, 4, 128, 256, 1}, {8, 1, 4, 256, 128, 1},
-                              {8, 2, 4, 192, 128, 2}, {8, 2, 4, 160, 128, 2}};
+// 0-2: 64-token tiles for a few dozen rows (weight streaming); 3, 4: 128- and 256-token
+// tiles for hundreds of rows; 5, 6: 256 weight rows x 192 / 160 tokens with the epilogue in
+// two halves (every weight byte read once for up to 256 rows, two 16-row blocks per wave).
+// Config 5 has no gate/up instance (it would spill registers).
+constexpr int kNumCfgs = 7;
+constexpr CfgInfo kCfgs[kNumCfgs] = {{8, 4, 4, 64, 512, 1},   {8, 2, 4, 64, 512, 1},   {8, 1, 8, 64, 512, 1},
+                                     {8, 2, 4, 128, 256, 1},  {8, 1, 4, 256, 128, 1},  {8, 2, 4, 192, 128, 2},
+                                     {8, 2, 4, 160, 128, 2}};
 
 template <int NW, int RB, int PD, bool DUAL, int MT, int KC, int XB, int EH = 1>
 void launch_cfg(const GemmDesc& d, int grid, hipStream_t s) {
@@ -891,12 +928,12 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
                    kBfix = 64.4e3, kFsplit = 3.63, kTopk = 11.8e-4;  // bytes/us, flop/us, us
   double best = 1e30;
   int best_c = -1, best_s = 1;
-  for (int c : {0, 1, 2, 4, 5, 6, 7}) {
+  for (int c = 0; c < kNumCfgs; ++c) {
     const CfgInfo& cf = kCfgs[c];
     const int nt = cf.nw * cf.rb * 16;
     const int tc = dual ? nt / 2 : nt;
     if (epi_kind == EPI_QKV && (tc / cf.eh) % head_dim) continue;
-    if (dual && c == 6) continue;  // its gate/up instance spills registers
+    if (dual && c == 5) continue;  // no gate/up instance
     const int m_tiles = (m + cf.mt - 1) / cf.mt;
     const int kchunks = (k + cf.kc - 1) / cf.kc;
     const int tiles = ((n + tc - 1) / tc) * m_tiles;
@@ -968,11 +1005,13 @@ int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s) {
       case 0: dual ? launch_cfg<8, 4, 4, true, 64, 512, 2>(d, grid, s) : launch_cfg<8, 4, 4, false, 64, 512, 2>(d, grid, s); break;
       case 1: dual ? launch_cfg<8, 2, 4, true, 64, 512, 2>(d, grid, s) : launch_cfg<8, 2, 4, false, 64, 512, 2>(d, grid, s); break;
       case 2: dual ? launch_cfg<8, 1, 8, true, 64, 512, 2>(d, grid, s) : launch_cfg<8, 1, 8, false, 64, 512, 2>(d, grid, s); break;
-      case 3: dual ? launch_cfg<4, 1, 8, true, 64, 512, 2>(d, grid, s) : launch_cfg<4, 1, 8, false, 64, 512, 2>(d, grid, s); break;
-      case 4: dual ? launch_cfg<8, 2, 4, true, 128, 256, 2>(d, grid, s) : launch_cfg<8, 2, 4, false, 128, 256, 2>(d, grid, s); break;
-      case 5: dual ? launch_cfg<8, 1, 4, true, 256, 128, 2>(d, grid, s) : launch_cfg<8, 1, 4, false, 256, 128, 2>(d, grid, s); break;
-      case 6: dual ? launch_cfg<8, 2, 4, true, 192, 128, 2, 2>(d, grid, s) : launch_cfg<8, 2, 4, false, 192, 128, 2, 2>(d, grid, s); break;
-      case 7: dual ? launch_cfg<8, 2, 4, true, 160, 128, 2, 2>(d, grid, s) : launch_cfg<8, 2, 4, false, 160, 128, 2, 2>(d, grid, s); break;
+      case 3: dual ? launch_cfg<8, 2, 4, true, 128, 256, 2>(d, grid, s) : launch_cfg<8, 2, 4, false, 128, 256, 2>(d, grid, s); break;
+      case 4: dual ? launch_cfg<8, 1, 4, true, 256, 128, 2>(d, grid, s) : launch_cfg<8, 1, 4, false, 256, 128, 2>(d, grid, s); break;
+      case 5:
+        if (dual) return EAGLE_ERR_UNSUPPORTED;
+        launch_cfg<8, 2, 4, false, 192, 128, 2, 2>(d, grid, s);
+        break;
+      case 6: dual ? launch_cfg<8, 2, 4, true, 160, 128, 2, 2>(d, grid, s) : launch_cfg<8, 2, 4, false, 160, 128, 2, 2>(d, grid, s); break;
       default: return EAGLE_ERR_UNSUPPORTED;
     }
   }
