@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-eagle-step", action="store_true",
                     help="skip the full EAGLE step (draft + verify + accept, batch 16)")
     ap.add_argument("--eagle-steps", type=int, default=20)
+    ap.add_argument("--lm-layout", choices=["packed", "row"], default="packed",
+                    help="LM-head weight layout: fragment-blocked (packed once at load) or row-major")
     ap.add_argument("--eagle-only", action="store_true",
                     help="run only the full EAGLE step (for profiling its kernels apart from the verify step)")
     return ap.parse_args()
@@ -56,9 +58,9 @@ def lm_head_bytes(dims, M):
     return dims.vocab * dims.hidden * es + M * dims.hidden * es + M * 8
 
 
-def measured_traffic(workload_name):
+def measured_traffic(workload_name, layout):
     """HBM bytes per LM-head launch from the committed counter summary, if it was taken on
-    the GEMM source as it is now (None otherwise)."""
+    the GEMM source as it is now and with the same LM-head weight layout (None otherwise)."""
     import hashlib
     import glob
     import re
@@ -71,7 +73,8 @@ def measured_traffic(workload_name):
         text = open(f).read()
         m1 = re.search(r"traffic_bytes_per_launch: (\d+)", text)
         m2 = re.search(r"gemm_source_sha256: ([0-9a-f]+)", text)
-        if m1 and m2 and m2.group(1) == sha:
+        m3 = re.search(r"lm_head_layout: (\S+)", text)
+        if m1 and m2 and m3 and m2.group(1) == sha and m3.group(1) == layout:
             return int(m1.group(1))
     return None
 
@@ -108,6 +111,19 @@ def draft_roofline_bytes_flops(dims, p, batch, prefix_len):
     return byts, flops
 
 
+def lm_layout_name(args):
+    return "fragment-blocked" if args.lm_layout == "packed" else "row-major"
+
+
+def lm_weights(weights, args):
+    """The weights with w_lm in the layout --lm-layout asks for (packing is a load-time step,
+    outside every timed region), and the layout code for the runners."""
+    if args.lm_layout == "row":
+        return weights, 0
+    from tree_attention_verification_06_amd.runner import with_packed_lm_head
+    return with_packed_lm_head(weights), 1
+
+
 def bench_eagle_step(args):
     """The full speculative step at the 8B shape with batch 16 (draft -> tree build -> verify
     of the 16 x 60 drafted nodes -> accept + commit), as a decode loop: each step's roots are
@@ -124,8 +140,9 @@ def bench_eagle_step(args):
     log(f"workload {wl.name}: generated in {time.perf_counter() - t0:.1f}s")
     t = upload(wl)
     dims, p, B = wl.dims, wl.draft, wl.batch
-    st = EagleStep(dims, p, t["weights"], t["draft_weights"], t["k_cache"], t["v_cache"], t["dk_cache"],
-                   t["dv_cache"], batch=B, max_prefix=wl.cache_cap)
+    weights, lm_layout = lm_weights(t["weights"], args)
+    st = EagleStep(dims, p, weights, t["draft_weights"], t["k_cache"], t["v_cache"], t["dk_cache"],
+                   t["dv_cache"], batch=B, max_prefix=wl.cache_cap, lm_layout=lm_layout)
     d, v = st.drafter, st.verifier
     prefix0 = t["prefix_len"].clone()
     feat = t["root_feature"].clone()
@@ -187,6 +204,7 @@ def bench_eagle_step(args):
     acc_mean = float(np.mean(acc))
     return {
         "workload": wl.name, "batch": B, "prefix": int(wl.prefix_len.max()),
+        "lm_head_layout": lm_layout_name(args),
         "draft": {"depth": p.depth, "top_k": p.top_k, "frontier": p.frontier, "max_nodes": p.max_nodes,
                   "conf_threshold": p.conf_threshold},
         "steps": n, "ms_per_step": round(ms_step, 4), "ms_draft": round(ms_draft, 4),
@@ -269,8 +287,9 @@ def main():
     M = wl.n_nodes
     max_nodes = max(len(p) for p in wl.parents)
     cap = wl.cache_cap
-    v = TreeVerifier(dims, t["weights"], t["k_cache"], t["v_cache"], batch=wl.batch, max_total_nodes=M,
-                     max_nodes=max_nodes, max_prefix=cap)
+    weights, lm_layout = lm_weights(t["weights"], args)
+    v = TreeVerifier(dims, weights, t["k_cache"], t["v_cache"], batch=wl.batch, max_total_nodes=M,
+                     max_nodes=max_nodes, max_prefix=cap, lm_layout=lm_layout)
     prefix0 = t["prefix_len"].clone()
 
     def step(timer=None):
@@ -350,7 +369,7 @@ def main():
         lm_avg = lm_ms / lm_n
         ach = lm_head_bytes(dims, M) / (lm_avg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name, lm_layout_name(args)),
                 "kernel": "gemm_bf16_kernel (LM head + fused row argmax)" if dims.dtype == "bf16" else
                 "gemm_f32_kernel (LM head + fused row argmax)",
                 "kernel_ms": round(lm_avg, 4), "bytes_per_launch": lm_head_bytes(dims, M)}
@@ -371,7 +390,8 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "tree_nodes": M, "max_tree_nodes": max_nodes,
                    "prefix": int(wl.prefix_len.max()), "hidden": dims.hidden, "q_heads": dims.n_q_heads,
                    "kv_heads": dims.n_kv_heads, "head_dim": dims.head_dim, "ffn": dims.ffn, "vocab": dims.vocab,
-                   "step": "tree_build + tree_verify + accept_commit"},
+                   "step": "tree_build + tree_verify + accept_commit",
+                   "lm_head_layout": lm_layout_name(args)},
         "accepted_tok_s": round(acc_per_step / (ms_per_step * 1e-3), 1),
         "accepted_per_step": acc_per_step,
         "accepted_tok_s_planted_depth3": round(planted / (ms_per_step * 1e-3), 1),

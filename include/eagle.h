@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define EAGLE_ABI_VERSION 1
+#define EAGLE_ABI_VERSION 2
 
 typedef enum {
   EAGLE_OK = 0,
@@ -87,7 +87,9 @@ typedef enum { EAGLE_BF16 = 0, EAGLE_F32 = 1 } eagle_dtype;
 typedef struct {
   int32_t hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
   float rope_theta, rms_eps;
-  int32_t dtype; /* eagle_dtype */
+  int32_t dtype;     /* eagle_dtype */
+  int32_t lm_layout; /* layout of w_lm: 0 row-major [V][H]; 1 fragment-blocked as written
+                        by eagle_pack_fragments (bf16 only).  Same arithmetic either way. */
 } eagle_dims;
 
 /* Weights of one decoder layer (element type dims.dtype). */
@@ -116,6 +118,20 @@ typedef struct {
   int32_t max_nodes;    /* final tree size per sequence, root included (2..128)       */
   float conf_threshold; /* a child is expandable iff its probability >= this, [0, 1]  */
 } eagle_draft_params;
+
+/* ---- weight packing ------------------------------------------------------
+ * A layout of this library (the pages prescribe none): a fragment-blocked copy of
+ * a row-major bf16 matrix W [rows][cols], cols a positive multiple of 32.  With
+ * nblk = ceil(rows / 16), the 8 elements of lane l (0..63) of 16-row block b at
+ * 32-column step s start at element ((s * nblk + b) * 64 + l) * 8 of out and hold
+ * W[16 b + l % 16][32 s + 8 (l / 16) .. 32 s + 8 (l / 16) + 7] (zeros for rows past
+ * the last).  These are the bf16 MFMA A operands in the order the GEMMs consume
+ * them; all blocks of one step are contiguous, so a GEMM whose workgroups advance
+ * through K together streams one compact region at a time.
+ * Inputs: w (device, 16-byte aligned); out (device, 16-byte aligned, nblk * 16 *
+ * cols elements, caller-owned, must not overlap w).  Asynchronous on stream.
+ * Errors: NULL or misaligned pointers, rows <= 0 or a bad cols -> EAGLE_ERR_ARG. */
+int eagle_pack_fragments(const void* w, int32_t rows, int32_t cols, void* out, void* stream);
 
 /* ---- tree encode -------------------------------------------------------
  * Method: "LLM parallel decoding EAGLE", How EAGLE works (tree attention: a

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert E.lib().eagle_abi_version() == 1
+    assert E.lib().eagle_abi_version() == 2
     assert E.status_str(0) == "ok"
     assert "workspace" in E.status_str(A.EAGLE_ERR_WORKSPACE)
 
@@ -53,8 +53,8 @@ def test_tree_build_host_errors():
     assert _tree_build(maxn=65, mw=1) == A.EAGLE_ERR_CAPACITY
 
 
-def _verify(dims, ws_bytes=1 << 40, **kw):
-    d = A.dims_struct(dims)
+def _verify(dims, ws_bytes=1 << 40, lm_layout=0, **kw):
+    d = A.dims_struct(dims, lm_layout)
     lw = A.EagleLayerW(4096, 4096, 4096, 4096, 4096, 4096, 4096)
     cl = A.EagleCacheLayout(1 << 20, 1 << 16, 128, 4096)
     a = dict(B=1, total=60, maxn=60, mw=1, max_prefix=2048, ws=ctypes.c_void_p(1 << 20))
@@ -75,6 +75,18 @@ def test_verify_host_errors():
     assert _verify(LLAMA8B, B=0) == A.EAGLE_ERR_ARG
     assert _verify(LLAMA8B, ws=ctypes.c_void_p((1 << 20) + 16)) == A.EAGLE_ERR_ARG  # misaligned workspace
     assert _verify(replace(TINY, head_dim=32)) == A.EAGLE_ERR_UNSUPPORTED
+    assert _verify(LLAMA8B, lm_layout=2) == A.EAGLE_ERR_ARG
+    assert _verify(TINY, lm_layout=1) == A.EAGLE_ERR_UNSUPPORTED  # fragment blocks are bf16 only
+
+
+def test_pack_fragments_host_errors():
+    pack = E.lib().eagle_pack_fragments
+    assert pack(None, 16, 32, FAKE, None) == A.EAGLE_ERR_ARG
+    assert pack(FAKE, 16, 32, None, None) == A.EAGLE_ERR_ARG
+    assert pack(FAKE, 0, 32, FAKE, None) == A.EAGLE_ERR_ARG
+    assert pack(FAKE, 16, 48, FAKE, None) == A.EAGLE_ERR_ARG    # columns not a multiple of 32
+    assert pack(FAKE, 16, 0, FAKE, None) == A.EAGLE_ERR_ARG
+    assert pack(ctypes.c_void_p(4096 + 8), 16, 32, FAKE, None) == A.EAGLE_ERR_ARG  # misaligned
 
 
 def test_workspace_size_query():

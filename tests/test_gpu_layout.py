@@ -1,0 +1,91 @@
+"""The fragment-blocked weight layout (eagle_pack_fragments): the packed bytes follow the
+layout's definition, and verification and draft expansion give bit-identical results with
+the LM head in either layout (the GEMM visits K in the same order for both)."""
+import numpy as np
+import pytest
+
+from tests._gpu import GpuRun, gpu_draft_outputs
+from workloads import DraftParams, make_workload
+from workloads.configs import mini_dims
+from workloads.device import upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def pack_reference(w):
+    """The layout as eagle.h defines it, written with numpy: lane l of 16-row block b at
+    32-column step s holds row 16 b + l % 16, columns 32 s + 8 (l / 16) .. + 7; the pieces
+    are ordered (s, b, l); rows past the last are zero."""
+    rows, cols = w.shape
+    nblk = (rows + 15) // 16
+    wp = np.zeros((nblk * 16, cols), dtype=w.dtype)
+    wp[:rows] = w
+    t = wp.reshape(nblk, 16, cols // 32, 4, 8)   # [b][r][s][q][e]: row 16 b + r, column 32 s + 8 q + e
+    return t.transpose(2, 0, 3, 1, 4).reshape(-1)  # [s][b][q][r][e]: lane l = 16 q + r
+
+
+@pytest.mark.parametrize("rows,cols", [(37, 96), (64, 32), (1, 64), (300, 4096)])
+def test_pack_fragments_matches_definition(rows, cols):
+    import torch
+    from tree_attention_verification_06_amd import eagle_pack_fragments
+    _log(f"pack {rows}x{cols}")
+    rng = np.random.default_rng(rows * 1000 + cols)
+    bits = rng.integers(0, 1 << 16, size=(rows, cols), dtype=np.uint16)
+    w = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    out = eagle_pack_fragments(w)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, pack_reference(bits))
+
+
+def _verify_pair(wl, **kw):
+    a = GpuRun(wl, **kw).run(accept=True).outputs()
+    b = GpuRun(wl, lm_layout=1, **kw).run(accept=True).outputs()
+    return a, b
+
+
+def test_verify_packed_lm_head_bit_identical_mini():
+    """Ragged batch, mini dims (vocab not a multiple of the 512-row tile): every output equal."""
+    wl = make_workload(3, seed=5, dims=mini_dims(), prefix=[1000, 37, 513, 2048])
+    _log(f"mini ragged: {wl.n_nodes} nodes, vocab {wl.dims.vocab}")
+    a, b = _verify_pair(wl)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_verify_packed_lm_head_bit_identical_8b_no_logits():
+    """The benchmark's launch configuration (8B layer, 60 nodes, P 2048, no debug logits, so the
+    argmax scan runs its unrolled path): the same argmax and max logit as the row-major run."""
+    wl = make_workload(2)
+    _log(f"{wl.name}: {wl.n_nodes} nodes")
+    a, b = _verify_pair(wl, want_logits=False)
+    for k in ("k_tree", "v_tree", "h", "attn", "maxlogit", "argmax"):
+        assert np.array_equal(a[k], b[k]), k
+    # and the same as a run that writes the logits (the argmax scan's other path)
+    c = GpuRun(wl, want_logits=True).run(accept=True).outputs()
+    for k in ("maxlogit", "argmax"):
+        assert np.array_equal(a[k], c[k]), k
+    assert np.array_equal(c["maxlogit"], c["logits"].max(axis=1))
+
+
+def test_draft_packed_lm_head_bit_identical():
+    from tree_attention_verification_06_amd.runner import TreeDrafter, with_packed_lm_head
+    params = DraftParams(depth=4, top_k=4, frontier=3, max_nodes=16)
+    wl = make_workload(5, seed=11, dims=mini_dims(), batch=3, prefix=[37, 100, 0], draft=params)
+    res = []
+    for layout in (0, 1):
+        t = upload(wl)
+        w = with_packed_lm_head(t["weights"]) if layout else t["weights"]
+        d = TreeDrafter(wl.dims, wl.draft, w, t["draft_weights"], t["dk_cache"], t["dv_cache"], batch=wl.batch,
+                        max_prefix=int(wl.prefix_len.max()), lm_layout=layout)
+        d.expand(t["root_feature"], t["root_token"], t["prefix_len"])
+        res.append(gpu_draft_outputs(d))
+    (t0, p0), (t1, p1) = res
+    for k in t0:
+        assert np.array_equal(t0[k], t1[k]), k
+    for k in p0:
+        assert np.array_equal(p0[k], p1[k]), k

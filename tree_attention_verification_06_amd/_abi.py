@@ -34,7 +34,8 @@ class EagleError(RuntimeError):
 class EagleDims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32), ("vocab", ctypes.c_int32),
-                ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("lm_layout", ctypes.c_int32)]
 
 
 class EagleLayerW(ctypes.Structure):
@@ -74,6 +75,7 @@ PROTOTYPES = {
                               _P, _P, _P, _P, _P, _P]),
     "eagle_workspace_size": (_S, [_I, ctypes.POINTER(EagleDims), _I, _I, _I, _I, ctypes.POINTER(EagleDraftParams)]),
     "eagle_workspace_init": (_I, [_P, _S, _P]),
+    "eagle_pack_fragments": (_I, [_P, _I, _I, _P, _P]),
     "eagle_timer_create": (_P, [_I]),
     "eagle_timer_destroy": (None, [_P]),
     "eagle_timer_collect": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
@@ -122,10 +124,11 @@ def _stream(stream):
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def dims_struct(dims):
-    """EagleDims from a workloads.LayerDims-like object."""
+def dims_struct(dims, lm_layout=0):
+    """EagleDims from a workloads.LayerDims-like object; lm_layout 1: w_lm is fragment-blocked."""
     return EagleDims(dims.hidden, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.ffn, dims.vocab,
-                     float(dims.rope_theta), float(dims.rms_eps), EAGLE_BF16 if dims.dtype == "bf16" else EAGLE_F32)
+                     float(dims.rope_theta), float(dims.rms_eps), EAGLE_BF16 if dims.dtype == "bf16" else EAGLE_F32,
+                     int(lm_layout))
 
 
 def layer_struct(w):
@@ -216,6 +219,20 @@ def eagle_workspace_size(which, dims, batch, total_nodes, max_nodes, max_prefix,
     params = draft_params_struct(params) if params is not None else None
     return int(lib().eagle_workspace_size(which, ctypes.byref(d), batch, total_nodes, max_nodes, max_prefix,
                                           ctypes.byref(params) if params is not None else None))
+
+
+def eagle_pack_fragments(w, out=None, stream=None):
+    """Fragment-blocked copy of a row-major bf16 matrix w [rows][cols] (eagle_pack_fragments);
+    out (allocated when None) holds ceil(rows / 16) * 16 * cols bf16 elements."""
+    import torch
+    rows, cols = w.shape
+    n = (rows + 15) // 16 * 16 * cols
+    if out is None:
+        out = torch.empty(n, dtype=torch.bfloat16, device=w.device)
+    if out.numel() < n or w.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or not w.is_contiguous():
+        raise EagleError(EAGLE_ERR_ARG, "eagle_pack_fragments")
+    _check(lib().eagle_pack_fragments(_p(w), rows, cols, _p(out), _stream(stream)), "eagle_pack_fragments")
+    return out
 
 
 def eagle_workspace_init(workspace, stream=None):

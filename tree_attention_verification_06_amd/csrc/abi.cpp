@@ -55,6 +55,8 @@ int check_dims(const eagle_dims* d) {
   }
   if ((d->ffn == 0) != (d->rms_eps == 0.f)) return EAGLE_ERR_UNSUPPORTED;
   if (d->rms_eps < 0.f || d->rope_theta < 0.f) return EAGLE_ERR_ARG;
+  if (d->lm_layout != 0 && d->lm_layout != 1) return EAGLE_ERR_ARG;
+  if (d->lm_layout == 1 && d->dtype != EAGLE_BF16) return EAGLE_ERR_UNSUPPORTED;
   return EAGLE_OK;
 }
 
@@ -336,6 +338,7 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
   {
     GemmDesc g = base_desc(d);
     g.w0 = w_lm;
+    g.w_layout = d->lm_layout;
     g.n = V;
     g.k = H;
     g.ldw = H;
@@ -474,6 +477,13 @@ size_t eagle_workspace_size(int32_t which, const eagle_dims* dims, int32_t batch
   if (which == 0) return verify_workspace(dims, batch, total_nodes, max_nodes, max_prefix);
   if (which == 1) return draft_workspace(dims, params, batch, max_prefix);
   return 0;
+}
+
+int eagle_pack_fragments(const void* w, int32_t rows, int32_t cols, void* out, void* stream) {
+  if (!w || !out || rows <= 0 || cols <= 0 || cols % 32) return EAGLE_ERR_ARG;
+  if (((uintptr_t)w | (uintptr_t)out) % 16) return EAGLE_ERR_ARG;
+  eagle::launch_pack_fragments(w, rows, cols, out, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
 }
 
 int eagle_workspace_init(void* workspace, size_t ws_bytes, void* stream) {

@@ -467,6 +467,7 @@ int check_draft(const eagle_dims* d, const eagle_draft_params* p, int B, int max
   if (1 + p->top_k + (p->depth - 1) * p->frontier * p->top_k > POOL_MAX) return EAGLE_ERR_UNSUPPORTED;
   if (p->frontier * p->top_k > 256) return EAGLE_ERR_UNSUPPORTED;
   if (!(p->conf_threshold >= 0.f && p->conf_threshold <= 1.f)) return EAGLE_ERR_ARG;
+  if (d->lm_layout != 0 && d->lm_layout != 1) return EAGLE_ERR_ARG;
   return EAGLE_OK;
 }
 
@@ -740,6 +741,7 @@ int draft_expand_impl(const eagle_dims* d, const eagle_draft_params* pr, const v
     {
       GemmDesc g{};
       g.w0 = w_lm;
+      g.w_layout = d->lm_layout;
       g.n = V;
       g.k = H;
       g.ldw = H;

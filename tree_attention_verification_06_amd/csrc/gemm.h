@@ -82,6 +82,7 @@ struct GemmDesc {
   const void* w1;  // second weight block (dual = 1: tile = gate columns + matching up columns)
   int dual;
   int dtype;       // EAGLE_BF16: MFMA path; EAGLE_F32: VALU path
+  int w_layout;    // 0: row-major [n][ldw]; 1: fragment-blocked (eagle_pack_fragments; bf16 only)
   int n;           // output columns (rows of each weight block)
   int k;
   int64_t ldw;
@@ -114,5 +115,7 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
 // Workspace floats for partials / sum-of-squares and ints for counters of one GEMM.
 void gemm_workspace(const GemmPlan& p, size_t* partial_floats, size_t* sumsq_floats, size_t* counter_ints);
 int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s);
+// Fragment-blocked copy of a row-major bf16 matrix (layout in eagle.h, eagle_pack_fragments).
+void launch_pack_fragments(const void* w, int rows, int cols, void* out, hipStream_t s);
 
 }  // namespace eagle

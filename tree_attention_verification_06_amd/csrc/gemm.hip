@@ -527,6 +527,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   // workgroups read different columns (spreads requests over HBM channels); the token
   // tiles of one weight tile run side by side on one XCD and keep the same order, so
   // the weight lines the first one fetches are still in that XCD's L2 for the others
+  // (the same order for both weight layouts, so they give bit-identical results)
   const int nchunk = (ke - kb + KC - 1) / KC;
   const int c0 = (nt_i * 5 + split * 3) % nchunk;
 
@@ -577,12 +578,24 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
     wblk = (const bf16*)d.w0;
     wrow0 = col0 + wid * RB * 16;
   }
+  // wp[rb]: this lane's 8 elements of block rb at K step 0; wstep: elements between
+  // consecutive 32-column steps (the address of column k is wp + (k / 32) * wstep)
   const bf16* wp[RB];
+  int64_t wstep;
+  if (d.w_layout) {
+    const int nblk = (d.n + 15) / 16;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = min(wrow0 + rb * 16 + lr, d.n - 1);
-    wp[rb] = wblk + (int64_t)row * d.ldw + lq * 8;
+    for (int rb = 0; rb < RB; ++rb) wp[rb] = wblk + (int64_t)min(wrow0 / 16 + rb, nblk - 1) * 512 + lane * 8;
+    wstep = (int64_t)nblk * 512;
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = min(wrow0 + rb * 16 + lr, d.n - 1);
+      wp[rb] = wblk + (int64_t)row * d.ldw + lq * 8;
+    }
+    wstep = 32;
   }
+  auto wload = [&](int rb, int k) { return *(const bf16x8_t*)(wp[rb] + (int64_t)(k >> 5) * wstep); };
 
   // X rows staged by this lane: r = (wid + j * NW) * RPP + lane / LPR, 8 columns at
   // (lane % LPR) * 8 of each chunk
@@ -671,7 +684,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
     for (int s = 0; s < PD; ++s) {
       const int k = min(kc + s * 32, klast);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) wbuf[s][rb] = *(const bf16x8_t*)(wp[rb] + k);
+      for (int rb = 0; rb < RB; ++rb) wbuf[s][rb] = wload(rb, k);
     }
     store_x(0, kc, 1.f);
   }
@@ -694,7 +707,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
       int kn = (s + PD < NSTEP) ? kc + (s + PD) * 32 : (more ? kcn + (s + PD - NSTEP) * 32 : klast);
       kn = min(kn, klast);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) wbuf[s % PD][rb] = *(const bf16x8_t*)(wp[rb] + kn);
+      for (int rb = 0; rb < RB; ++rb) wbuf[s % PD][rb] = wload(rb, kn);
       // keep the prefetch of step s + PD ahead of the math of step s (the scheduler
       // would otherwise sink the loads next to their use)
       __builtin_amdgcn_sched_barrier(0);
@@ -994,6 +1007,7 @@ int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s) {
   if (d.k % 32 || (d.x.ka % 8) || p.cfg < 0) return EAGLE_ERR_UNSUPPORTED;
   if (p.cfg != 100 && (d.x.a.dtype != EAGLE_BF16 || d.x.b.dtype != EAGLE_BF16)) return EAGLE_ERR_UNSUPPORTED;
   if (p.cfg == 100 && d.epi.kind == EPI_TOPK) return EAGLE_ERR_UNSUPPORTED;  // its LDS tile is too small
+  if (p.cfg == 100 && d.w_layout) return EAGLE_ERR_UNSUPPORTED;              // fragment blocks are bf16
   const int grid = p.w_tiles * p.m_tiles * p.splits;
   if (grid <= 0) return EAGLE_OK;
   if (p.cfg == 100) {
@@ -1016,6 +1030,31 @@ int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s) {
     }
   }
   return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
+}
+
+namespace {
+// One 16-byte fragment piece per thread: piece f = (step s, block b, lane l) in that order.
+__global__ __launch_bounds__(256) void pack_fragments_kernel(const bf16* __restrict__ w, int rows, int cols,
+                                                              bf16* __restrict__ out, int64_t pieces) {
+  const int nblk = (rows + 15) / 16;
+  for (int64_t f = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; f < pieces; f += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(f % 64);
+    const int64_t sb = f / 64;
+    const int b = (int)(sb % nblk);
+    const int s = (int)(sb / nblk);
+    const int row = b * 16 + l % 16, col = s * 32 + (l / 16) * 8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < rows) v = *(const uint4*)(w + (int64_t)row * cols + col);
+    *(uint4*)(out + f * 8) = v;
+  }
+}
+}  // namespace
+
+void launch_pack_fragments(const void* w, int rows, int cols, void* out, hipStream_t s) {
+  const int64_t pieces = (int64_t)((rows + 15) / 16) * (cols / 32) * 64;
+  const int grid = (int)std::min<int64_t>((pieces + 255) / 256, 8192);
+  hipLaunchKernelGGL(pack_fragments_kernel, dim3(grid), dim3(256), 0, s, (const bf16*)w, rows, cols, (bf16*)out,
+                     pieces);
 }
 
 }  // namespace eagle

@@ -9,11 +9,22 @@ import torch
 from . import _abi as A
 
 
+def with_packed_lm_head(weights):
+    """A shallow copy of a weights dict whose w_lm is the fragment-blocked copy written by
+    eagle_pack_fragments (pass lm_layout=1 to the runners with it).  A load-time step: the
+    packed copy takes as much device memory as w_lm."""
+    w = dict(weights)
+    w["w_lm"] = A.eagle_pack_fragments(weights["w_lm"])
+    return w
+
+
 class TreeVerifier:
+    """lm_layout: 0 if weights["w_lm"] is row-major [vocab][hidden], 1 if fragment-blocked."""
+
     def __init__(self, dims, weights, k_cache, v_cache, *, batch, max_total_nodes, max_nodes, max_prefix,
-                 max_accept=None, device="cuda"):
+                 max_accept=None, device="cuda", lm_layout=0):
         self.dims = dims
-        self.dstruct = A.dims_struct(dims)
+        self.dstruct = A.dims_struct(dims, lm_layout)
         self.lstruct = A.layer_struct(weights)
         self.w = weights
         self.k_cache = k_cache
@@ -83,13 +94,14 @@ class TreeDrafter:
 
     weights: the target's tensors (final_ln, w_lm, embed); draft_weights: w_fc and the
     draft decoder layer.  Trees come out compacted (tree_off, parent, tokens, cum) in
-    arrays of batch * max_nodes entries, padded past tree_off[batch]."""
+    arrays of batch * max_nodes entries, padded past tree_off[batch].  lm_layout: the
+    layout of weights["w_lm"] (0 row-major, 1 fragment-blocked)."""
 
     def __init__(self, dims, params, weights, draft_weights, dk_cache, dv_cache, *, batch, max_prefix,
-                 device="cuda"):
+                 device="cuda", lm_layout=0):
         self.dims = dims
         self.params = A.draft_params_struct(params)
-        self.dstruct = A.dims_struct(dims)
+        self.dstruct = A.dims_struct(dims, lm_layout)
         self.lstruct = A.layer_struct(draft_weights)
         self.w = weights
         self.dw = draft_weights
@@ -142,13 +154,13 @@ class EagleStep:
     step's roots are the accepted bonus tokens and their features."""
 
     def __init__(self, dims, params, weights, draft_weights, k_cache, v_cache, dk_cache, dv_cache, *, batch,
-                 max_prefix, device="cuda"):
+                 max_prefix, device="cuda", lm_layout=0):
         self.drafter = TreeDrafter(dims, params, weights, draft_weights, dk_cache, dv_cache, batch=batch,
-                                   max_prefix=max_prefix, device=device)
+                                   max_prefix=max_prefix, device=device, lm_layout=lm_layout)
         M = self.drafter.max_nodes
         self.total = batch * M
         self.verifier = TreeVerifier(dims, weights, k_cache, v_cache, batch=batch, max_total_nodes=self.total,
-                                     max_nodes=M, max_prefix=max_prefix, device=device)
+                                     max_nodes=M, max_prefix=max_prefix, device=device, lm_layout=lm_layout)
 
     def step(self, root_feature, root_token, prefix_len, timer=None):
         d, v = self.drafter, self.verifier
