@@ -41,8 +41,9 @@ def parse():
     ap.add_argument("--no-eagle-step", action="store_true",
                     help="skip the full EAGLE step (draft + verify + accept, batch 16)")
     ap.add_argument("--eagle-steps", type=int, default=20)
-    ap.add_argument("--lm-layout", choices=["packed", "row"], default="packed",
-                    help="LM-head weight layout: fragment-blocked (packed once at load) or row-major")
+    ap.add_argument("--weight-layout", choices=["packed", "row"], default="packed",
+                    help="weight matrices (LM head, layer, draft): fragment-blocked (packed once at load) "
+                         "or row-major")
     ap.add_argument("--eagle-only", action="store_true",
                     help="run only the full EAGLE step (for profiling its kernels apart from the verify step)")
     return ap.parse_args()
@@ -73,7 +74,7 @@ def measured_traffic(workload_name, layout):
         text = open(f).read()
         m1 = re.search(r"traffic_bytes_per_launch: (\d+)", text)
         m2 = re.search(r"gemm_source_sha256: ([0-9a-f]+)", text)
-        m3 = re.search(r"lm_head_layout: (\S+)", text)
+        m3 = re.search(r"weight_layout: (\S+)", text)
         if m1 and m2 and m3 and m2.group(1) == sha and m3.group(1) == layout:
             return int(m1.group(1))
     return None
@@ -111,17 +112,17 @@ def draft_roofline_bytes_flops(dims, p, batch, prefix_len):
     return byts, flops
 
 
-def lm_layout_name(args):
-    return "fragment-blocked" if args.lm_layout == "packed" else "row-major"
+def layout_name(args):
+    return "fragment-blocked" if args.weight_layout == "packed" else "row-major"
 
 
-def lm_weights(weights, args):
-    """The weights with w_lm in the layout --lm-layout asks for (packing is a load-time step,
-    outside every timed region), and the layout code for the runners."""
-    if args.lm_layout == "row":
+def laid_out(weights, args):
+    """The weights with every matrix in the layout --weight-layout asks for (packing is a
+    load-time step, outside every timed region), and the layout code for the runners."""
+    if args.weight_layout == "row":
         return weights, 0
-    from tree_attention_verification_06_amd.runner import with_packed_lm_head
-    return with_packed_lm_head(weights), 1
+    from tree_attention_verification_06_amd.runner import with_packed_weights
+    return with_packed_weights(weights), 1
 
 
 def bench_eagle_step(args):
@@ -140,9 +141,10 @@ def bench_eagle_step(args):
     log(f"workload {wl.name}: generated in {time.perf_counter() - t0:.1f}s")
     t = upload(wl)
     dims, p, B = wl.dims, wl.draft, wl.batch
-    weights, lm_layout = lm_weights(t["weights"], args)
-    st = EagleStep(dims, p, weights, t["draft_weights"], t["k_cache"], t["v_cache"], t["dk_cache"],
-                   t["dv_cache"], batch=B, max_prefix=wl.cache_cap, lm_layout=lm_layout)
+    weights, layout = laid_out(t["weights"], args)
+    draft_weights, _ = laid_out(t["draft_weights"], args)
+    st = EagleStep(dims, p, weights, draft_weights, t["k_cache"], t["v_cache"], t["dk_cache"],
+                   t["dv_cache"], batch=B, max_prefix=wl.cache_cap, lm_layout=layout, weight_layout=layout)
     d, v = st.drafter, st.verifier
     prefix0 = t["prefix_len"].clone()
     feat = t["root_feature"].clone()
@@ -204,7 +206,7 @@ def bench_eagle_step(args):
     acc_mean = float(np.mean(acc))
     return {
         "workload": wl.name, "batch": B, "prefix": int(wl.prefix_len.max()),
-        "lm_head_layout": lm_layout_name(args),
+        "weight_layout": layout_name(args),
         "draft": {"depth": p.depth, "top_k": p.top_k, "frontier": p.frontier, "max_nodes": p.max_nodes,
                   "conf_threshold": p.conf_threshold},
         "steps": n, "ms_per_step": round(ms_step, 4), "ms_draft": round(ms_draft, 4),
@@ -287,9 +289,9 @@ def main():
     M = wl.n_nodes
     max_nodes = max(len(p) for p in wl.parents)
     cap = wl.cache_cap
-    weights, lm_layout = lm_weights(t["weights"], args)
+    weights, layout = laid_out(t["weights"], args)
     v = TreeVerifier(dims, weights, t["k_cache"], t["v_cache"], batch=wl.batch, max_total_nodes=M,
-                     max_nodes=max_nodes, max_prefix=cap, lm_layout=lm_layout)
+                     max_nodes=max_nodes, max_prefix=cap, lm_layout=layout, weight_layout=layout)
     prefix0 = t["prefix_len"].clone()
 
     def step(timer=None):
@@ -369,7 +371,7 @@ def main():
         lm_avg = lm_ms / lm_n
         ach = lm_head_bytes(dims, M) / (lm_avg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name, lm_layout_name(args)),
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name, layout_name(args)),
                 "kernel": "gemm_bf16_kernel (LM head + fused row argmax)" if dims.dtype == "bf16" else
                 "gemm_f32_kernel (LM head + fused row argmax)",
                 "kernel_ms": round(lm_avg, 4), "bytes_per_launch": lm_head_bytes(dims, M)}
@@ -391,7 +393,7 @@ def main():
                    "prefix": int(wl.prefix_len.max()), "hidden": dims.hidden, "q_heads": dims.n_q_heads,
                    "kv_heads": dims.n_kv_heads, "head_dim": dims.head_dim, "ffn": dims.ffn, "vocab": dims.vocab,
                    "step": "tree_build + tree_verify + accept_commit",
-                   "lm_head_layout": lm_layout_name(args)},
+                   "weight_layout": layout_name(args)},
         "accepted_tok_s": round(acc_per_step / (ms_per_step * 1e-3), 1),
         "accepted_per_step": acc_per_step,
         "accepted_tok_s_planted_depth3": round(planted / (ms_per_step * 1e-3), 1),

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define EAGLE_ABI_VERSION 2
+#define EAGLE_ABI_VERSION 3
 
 typedef enum {
   EAGLE_OK = 0,
@@ -92,7 +92,10 @@ typedef struct {
                         by eagle_pack_fragments (bf16 only).  Same arithmetic either way. */
 } eagle_dims;
 
-/* Weights of one decoder layer (element type dims.dtype). */
+/* Weights of one decoder layer (element type dims.dtype).  The matrices are [rows][cols]
+ * as listed, row-major when layout == 0, or each in the fragment-blocked layout written by
+ * eagle_pack_fragments when layout == 1 (bf16 only; the same arithmetic either way).  For
+ * a draft layer, layout also applies to its w_fc. */
 typedef struct {
   const void* ln_attn; /* [H] RMSNorm gain before attention (NULL if rms_eps == 0) */
   const void* w_qkv;   /* [(Hq + 2 Hkv) D][H]: q rows (head-major), then k rows, then v rows */
@@ -101,6 +104,7 @@ typedef struct {
   const void* w_gate;  /* [F][H] */
   const void* w_up;    /* [F][H] */
   const void* w_down;  /* [H][F] */
+  int32_t layout;      /* 0 row-major, 1 fragment-blocked */
 } eagle_layer_w;
 
 /* KV cache geometry, in elements: element (b, h, t, d) is at

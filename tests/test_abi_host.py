@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert E.lib().eagle_abi_version() == 2
+    assert E.lib().eagle_abi_version() == 3
     assert E.status_str(0) == "ok"
     assert "workspace" in E.status_str(A.EAGLE_ERR_WORKSPACE)
 
@@ -53,9 +53,9 @@ def test_tree_build_host_errors():
     assert _tree_build(maxn=65, mw=1) == A.EAGLE_ERR_CAPACITY
 
 
-def _verify(dims, ws_bytes=1 << 40, lm_layout=0, **kw):
+def _verify(dims, ws_bytes=1 << 40, lm_layout=0, layer_layout=0, **kw):
     d = A.dims_struct(dims, lm_layout)
-    lw = A.EagleLayerW(4096, 4096, 4096, 4096, 4096, 4096, 4096)
+    lw = A.EagleLayerW(4096, 4096, 4096, 4096, 4096, 4096, 4096, layer_layout)
     cl = A.EagleCacheLayout(1 << 20, 1 << 16, 128, 4096)
     a = dict(B=1, total=60, maxn=60, mw=1, max_prefix=2048, ws=ctypes.c_void_p(1 << 20))
     a.update(kw)
@@ -77,6 +77,8 @@ def test_verify_host_errors():
     assert _verify(replace(TINY, head_dim=32)) == A.EAGLE_ERR_UNSUPPORTED
     assert _verify(LLAMA8B, lm_layout=2) == A.EAGLE_ERR_ARG
     assert _verify(TINY, lm_layout=1) == A.EAGLE_ERR_UNSUPPORTED  # fragment blocks are bf16 only
+    assert _verify(LLAMA8B, layer_layout=2) == A.EAGLE_ERR_ARG
+    assert _verify(TINY, layer_layout=1) == A.EAGLE_ERR_UNSUPPORTED
 
 
 def test_pack_fragments_host_errors():

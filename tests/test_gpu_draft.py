@@ -112,15 +112,18 @@ def test_draft_unsupported_params_rejected():
                              d.tree_off, d.parent, d.tokens, d.cum, d.workspace, max_prefix=d.max_prefix)
 
 
-def _step_check(wl, seqs, label):
+def _step_check(wl, seqs, label, layout=0):
     """Full step on the GPU (draft -> encode -> verify -> accept + commit, no host sync), then
-    the oracle's verification of the GPU-drafted trees of sequences ``seqs``."""
+    the oracle's verification of the GPU-drafted trees of sequences ``seqs``.  layout 1: every
+    weight matrix fragment-blocked."""
     import torch
-    from tree_attention_verification_06_amd.runner import EagleStep
+    from tree_attention_verification_06_amd.runner import EagleStep, with_packed_weights
     t = upload(wl)
     k_before = wl.k_cache.copy()
-    st = EagleStep(wl.dims, wl.draft, t["weights"], t["draft_weights"], t["k_cache"], t["v_cache"], t["dk_cache"],
-                   t["dv_cache"], batch=wl.batch, max_prefix=int(wl.prefix_len.max()))
+    w = with_packed_weights(t["weights"]) if layout else t["weights"]
+    dw = with_packed_weights(t["draft_weights"]) if layout else t["draft_weights"]
+    st = EagleStep(wl.dims, wl.draft, w, dw, t["k_cache"], t["v_cache"], t["dk_cache"], t["dv_cache"],
+                   batch=wl.batch, max_prefix=int(wl.prefix_len.max()), lm_layout=layout, weight_layout=layout)
     st.step(t["root_feature"], t["root_token"], t["prefix_len"])
     torch.cuda.synchronize()
     d, v = st.drafter, st.verifier
@@ -174,14 +177,15 @@ def test_full_step_mini_with_pruning():
 
 
 def test_full_eagle_step_llama8b_b16():
-    """Full EAGLE step at the 8B shape, batch 16, prefix 2048, depth 6, top-10, 60-node trees.
-    The GPU runs all 16 sequences; the oracle (teacher-forced draft and verification) checks a
-    sample of them one by one; selection, rerank and acceptance are checked on all 16."""
+    """Full EAGLE step at the 8B shape, batch 16, prefix 2048, depth 6, top-10, 60-node trees,
+    with the weights fragment-blocked as the benchmark runs it.  The GPU runs all 16 sequences;
+    the oracle (teacher-forced draft and verification) checks a sample of them one by one;
+    selection, rerank and acceptance are checked on all 16."""
     t0 = time.time()
     wl = make_workload(5)
     _log(f"cfg {wl.name}: generated in {time.time() - t0:.1f}s")
     sample = [0, 9]
-    acc = _step_check(wl, sample, wl.name)
+    acc = _step_check(wl, sample, wl.name, layout=1)
     _log(f"  step checked {time.time() - t0:.1f}s, accept lengths {acc.tolist()}")
     # teacher-forced draft numerics on the sample (re-drafts: the step consumed prefix_len)
     t, d, tree, pool = _draft(wl)

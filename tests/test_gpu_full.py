@@ -43,10 +43,10 @@ def _run_full(cfg, prefix=None):
 
 
 def test_full_llama8b_layer_60_nodes_prefix_2048():
-    """Row-major LM head against the oracle, then the fragment-blocked LM head (the layout the
+    """Row-major weights against the oracle, then fragment-blocked weights (the layout the
     benchmark runs): the same arithmetic in the same order, so every output is bit-identical."""
     wl, g, out, ref = _run_full(2)
-    p = GpuRun(wl, lm_layout=1).run(accept=True).outputs()
+    p = GpuRun(wl, layout=1).run(accept=True).outputs()
     check_verify(p, ref, wl.dims, label=wl.name + " packed")
     for k in ("k_tree", "v_tree", "h", "attn", "logits", "maxlogit", "argmax"):
         assert np.array_equal(out[k], p[k]), k

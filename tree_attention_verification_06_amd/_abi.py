@@ -41,7 +41,7 @@ class EagleDims(ctypes.Structure):
 class EagleLayerW(ctypes.Structure):
     _fields_ = [("ln_attn", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p), ("w_o", ctypes.c_void_p),
                 ("ln_mlp", ctypes.c_void_p), ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
-                ("w_down", ctypes.c_void_p)]
+                ("w_down", ctypes.c_void_p), ("layout", ctypes.c_int32)]
 
 
 class EagleCacheLayout(ctypes.Structure):
@@ -131,10 +131,12 @@ def dims_struct(dims, lm_layout=0):
                      int(lm_layout))
 
 
-def layer_struct(w):
-    """EagleLayerW from a dict of device tensors (missing entries -> NULL)."""
+def layer_struct(w, layout=0):
+    """EagleLayerW from a dict of device tensors (missing entries -> NULL); layout 1: the
+    matrices are fragment-blocked (eagle_pack_fragments)."""
     g = lambda k: w[k].data_ptr() if w.get(k) is not None else None  # noqa: E731
-    return EagleLayerW(g("ln_attn"), g("w_qkv"), g("w_o"), g("ln_mlp"), g("w_gate"), g("w_up"), g("w_down"))
+    return EagleLayerW(g("ln_attn"), g("w_qkv"), g("w_o"), g("ln_mlp"), g("w_gate"), g("w_up"), g("w_down"),
+                       int(layout))
 
 
 def cache_struct(cache):

@@ -147,6 +147,8 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
   if (!x_in && (!embed || !tokens)) return EAGLE_ERR_ARG;
   const bool norm = d->rms_eps > 0.f;
   if (!lw->w_qkv || !lw->w_o) return EAGLE_ERR_ARG;
+  if (lw->layout != 0 && lw->layout != 1) return EAGLE_ERR_ARG;
+  if (lw->layout == 1 && d->dtype != EAGLE_BF16) return EAGLE_ERR_UNSUPPORTED;
   if (norm && (!lw->ln_attn || !lw->ln_mlp || !lw->w_gate || !lw->w_up || !lw->w_down || !final_ln))
     return EAGLE_ERR_ARG;
   if (((uintptr_t)ws) & 255) return EAGLE_ERR_ARG;
@@ -185,6 +187,7 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
   {
     GemmDesc g = base_desc(d);
     g.w0 = lw->w_qkv;
+    g.w_layout = lw->layout;
     g.n = (Hq + 2 * Hkv) * D;
     g.k = H;
     g.ldw = H;
@@ -249,6 +252,7 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
   {
     GemmDesc g = base_desc(d);
     g.w0 = lw->w_o;
+    g.w_layout = lw->layout;
     g.n = H;
     g.k = Hq * D;
     g.ldw = Hq * D;
@@ -279,6 +283,7 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     GemmDesc g = base_desc(d);
     g.w0 = lw->w_gate;
     g.w1 = lw->w_up;
+    g.w_layout = lw->layout;
     g.dual = 1;
     g.n = F;
     g.k = H;
@@ -310,6 +315,7 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     // 5. down projection + residual -> h_out (and bf16(final gain * h) + row sums of squares)
     GemmDesc g2 = base_desc(d);
     g2.w0 = lw->w_down;
+    g2.w_layout = lw->layout;
     g2.n = H;
     g2.k = F;
     g2.ldw = F;

@@ -533,6 +533,7 @@ int draft_expand_impl(const eagle_dims* d, const eagle_draft_params* pr, const v
     return EAGLE_ERR_ARG;
   if (!lw->ln_attn || !lw->w_qkv || !lw->w_o || !lw->ln_mlp || !lw->w_gate || !lw->w_up || !lw->w_down)
     return EAGLE_ERR_ARG;
+  if (lw->layout != 0 && lw->layout != 1) return EAGLE_ERR_ARG;
   if (((uintptr_t)ws) & 255) return EAGLE_ERR_ARG;
   if (cache->token_stride % 8 || cache->head_stride % 8 || cache->batch_stride % 8 || cache->capacity < 0)
     return EAGLE_ERR_ARG;
@@ -596,6 +597,7 @@ int draft_expand_impl(const eagle_dims* d, const eagle_draft_params* pr, const v
     {
       GemmDesc g{};
       g.w0 = w_fc;
+      g.w_layout = lw->layout;
       g.n = H;
       g.k = 2 * H;
       g.ldw = 2 * H;
@@ -615,6 +617,7 @@ int draft_expand_impl(const eagle_dims* d, const eagle_draft_params* pr, const v
     {
       GemmDesc g{};
       g.w0 = lw->w_qkv;
+      g.w_layout = lw->layout;
       g.n = (Hq + 2 * Hkv) * Dh;
       g.k = H;
       g.ldw = H;
@@ -674,6 +677,7 @@ int draft_expand_impl(const eagle_dims* d, const eagle_draft_params* pr, const v
     {
       GemmDesc g{};
       g.w0 = lw->w_o;
+      g.w_layout = lw->layout;
       g.n = H;
       g.k = Hq * Dh;
       g.ldw = Hq * Dh;
@@ -697,6 +701,7 @@ int draft_expand_impl(const eagle_dims* d, const eagle_draft_params* pr, const v
       GemmDesc g{};
       g.w0 = lw->w_gate;
       g.w1 = lw->w_up;
+      g.w_layout = lw->layout;
       g.dual = 1;
       g.n = Fm;
       g.k = H;
@@ -719,6 +724,7 @@ int draft_expand_impl(const eagle_dims* d, const eagle_draft_params* pr, const v
     {
       GemmDesc g{};
       g.w0 = lw->w_down;
+      g.w_layout = lw->layout;
       g.n = H;
       g.k = Fm;
       g.ldw = Fm;

@@ -9,23 +9,38 @@ import torch
 from . import _abi as A
 
 
-def with_packed_lm_head(weights):
-    """A shallow copy of a weights dict whose w_lm is the fragment-blocked copy written by
-    eagle_pack_fragments (pass lm_layout=1 to the runners with it).  A load-time step: the
-    packed copy takes as much device memory as w_lm."""
+LAYER_MATRICES = ("w_qkv", "w_o", "w_gate", "w_up", "w_down", "w_fc")
+
+
+def with_packed_weights(weights, *, lm_head=True, layer=True):
+    """A shallow copy of a weights dict with w_lm (lm_head) and the layer matrices present
+    (layer: w_qkv, w_o, w_gate, w_up, w_down, w_fc) replaced by fragment-blocked copies
+    written by eagle_pack_fragments; pass lm_layout=1 / weight_layout=1 to the runners with
+    it.  A load-time step: each packed copy takes as much device memory as its source."""
     w = dict(weights)
-    w["w_lm"] = A.eagle_pack_fragments(weights["w_lm"])
+    if lm_head and w.get("w_lm") is not None:
+        w["w_lm"] = A.eagle_pack_fragments(weights["w_lm"])
+    if layer:
+        for k in LAYER_MATRICES:
+            if w.get(k) is not None:
+                w[k] = A.eagle_pack_fragments(weights[k])
     return w
 
 
+def with_packed_lm_head(weights):
+    """with_packed_weights for w_lm alone."""
+    return with_packed_weights(weights, layer=False)
+
+
 class TreeVerifier:
-    """lm_layout: 0 if weights["w_lm"] is row-major [vocab][hidden], 1 if fragment-blocked."""
+    """lm_layout: 0 if weights["w_lm"] is row-major [vocab][hidden], 1 if fragment-blocked;
+    weight_layout: the same for the layer matrices."""
 
     def __init__(self, dims, weights, k_cache, v_cache, *, batch, max_total_nodes, max_nodes, max_prefix,
-                 max_accept=None, device="cuda", lm_layout=0):
+                 max_accept=None, device="cuda", lm_layout=0, weight_layout=0):
         self.dims = dims
         self.dstruct = A.dims_struct(dims, lm_layout)
-        self.lstruct = A.layer_struct(weights)
+        self.lstruct = A.layer_struct(weights, weight_layout)
         self.w = weights
         self.k_cache = k_cache
         self.v_cache = v_cache
@@ -95,14 +110,15 @@ class TreeDrafter:
     weights: the target's tensors (final_ln, w_lm, embed); draft_weights: w_fc and the
     draft decoder layer.  Trees come out compacted (tree_off, parent, tokens, cum) in
     arrays of batch * max_nodes entries, padded past tree_off[batch].  lm_layout: the
-    layout of weights["w_lm"] (0 row-major, 1 fragment-blocked)."""
+    layout of weights["w_lm"] (0 row-major, 1 fragment-blocked); weight_layout: the same
+    for the draft matrices (w_fc and the draft layer)."""
 
     def __init__(self, dims, params, weights, draft_weights, dk_cache, dv_cache, *, batch, max_prefix,
-                 device="cuda", lm_layout=0):
+                 device="cuda", lm_layout=0, weight_layout=0):
         self.dims = dims
         self.params = A.draft_params_struct(params)
         self.dstruct = A.dims_struct(dims, lm_layout)
-        self.lstruct = A.layer_struct(draft_weights)
+        self.lstruct = A.layer_struct(draft_weights, weight_layout)
         self.w = weights
         self.dw = draft_weights
         self.dk_cache = dk_cache
@@ -154,13 +170,15 @@ class EagleStep:
     step's roots are the accepted bonus tokens and their features."""
 
     def __init__(self, dims, params, weights, draft_weights, k_cache, v_cache, dk_cache, dv_cache, *, batch,
-                 max_prefix, device="cuda", lm_layout=0):
+                 max_prefix, device="cuda", lm_layout=0, weight_layout=0):
         self.drafter = TreeDrafter(dims, params, weights, draft_weights, dk_cache, dv_cache, batch=batch,
-                                   max_prefix=max_prefix, device=device, lm_layout=lm_layout)
+                                   max_prefix=max_prefix, device=device, lm_layout=lm_layout,
+                                   weight_layout=weight_layout)
         M = self.drafter.max_nodes
         self.total = batch * M
         self.verifier = TreeVerifier(dims, weights, k_cache, v_cache, batch=batch, max_total_nodes=self.total,
-                                     max_nodes=M, max_prefix=max_prefix, device=device, lm_layout=lm_layout)
+                                     max_nodes=M, max_prefix=max_prefix, device=device, lm_layout=lm_layout,
+                                     weight_layout=weight_layout)
 
     def step(self, root_feature, root_token, prefix_len, timer=None):
         d, v = self.drafter, self.verifier
