@@ -164,6 +164,99 @@ __device__ __forceinline__ void epi_store_rows(const GemmDesc& d, const float* t
   }
 }
 
+// EPI_TOPK with per-thread candidate lists of KL entries (KL >= k): the branch-free sorted
+// insertion costs KL compare-and-swap steps per column, so the list is no longer than needed.
+template <int KL>
+__device__ __forceinline__ void epi_topk(const GemmDesc& d, const float* tile, int ts, int tc, int col0, int m0, int mv,
+                                         int mt, const float* scale) {
+  const Epi& e = d.epi;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  // Per token: this tile's top-k (value desc, index asc) and (max, sum exp(v - max)).
+  // Thread (token t = tid % mt, part = tid / mt) scans columns part, part + P, ...
+  // (P = nth / mt parts per token): a wave reads one column for 64 consecutive tokens,
+  // which is conflict-free in the column-major tile.  Each thread keeps its best
+  // candidates as a sorted register list (branch-free insertion, static indices); the
+  // lists and partial (max, sum) pairs of a token are then merged through LDS.
+  const int K = e.topk;
+  const int tile_i = col0 / tc;
+  const int P = nth / mt;  // parts per token; threads past P * mt (mt not dividing nth) sit out
+  const int t = tid % mt, part = tid / mt;
+  const bool active = part < P;
+  const int ncol = min(tc, d.n - col0);
+  unsigned long long lst[KL];
+#pragma unroll
+  for (int q = 0; q < KL; ++q) lst[q] = 0ull;
+  float mx = -INFINITY, se = 0.f;
+  if (active && t < mv) {
+    const float sc = scale[t];
+    int r0 = part;
+    for (; r0 + 3 * P < ncol; r0 += 4 * P) {  // 4 LDS reads in flight per round
+      float v4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v4[u] = tile[(r0 + u * P) * ts + t];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) mx = fmaxf(mx, sc * v4[u]);
+    }
+    for (; r0 < ncol; r0 += P) mx = fmaxf(mx, sc * tile[r0 * ts + t]);
+    for (int r = part; r < ncol; r += P) {
+      const float v = sc * tile[r * ts + t];
+      se += __expf(v - mx);
+      unsigned long long key = argmax_key(v, (uint32_t)(col0 + r));
+#pragma unroll
+      for (int q = 0; q < KL; ++q) {
+        const unsigned long long hi = key > lst[q] ? key : lst[q];
+        key = key > lst[q] ? lst[q] : key;
+        lst[q] = hi;
+      }
+    }
+  }
+  __syncthreads();  // every read of the tile is done: its LDS is reused below
+  unsigned long long* sl = (unsigned long long*)tile;          // [P][mt][KL]
+  float* sm = (float*)(sl + (size_t)P * mt * KL);             // [P][mt][2]
+  if (active) {
+#pragma unroll
+    for (int q = 0; q < KL; ++q) sl[((size_t)part * mt + t) * KL + q] = lst[q];
+    sm[(part * mt + t) * 2] = mx;
+    sm[(part * mt + t) * 2 + 1] = se;
+  }
+  __syncthreads();
+  if (part == 0 && t < mv) {
+    float M = -INFINITY;
+    for (int p2 = 0; p2 < P; ++p2) M = fmaxf(M, sm[(p2 * mt + t) * 2]);
+    float S = 0.f;
+    for (int p2 = 0; p2 < P; ++p2) {
+      const float m2 = sm[(p2 * mt + t) * 2];
+      if (m2 > -INFINITY) S += sm[(p2 * mt + t) * 2 + 1] * __expf(m2 - M);
+    }
+    const int64_t ob = (int64_t)tile_i * d.m + m0 + t;  // tile-major: coalesced per workgroup
+    e.lse_part[ob * 2] = M;
+    e.lse_part[ob * 2 + 1] = S;
+    // P-way merge of the sorted lists (keys are unique: one per column)
+    int head[8];
+#pragma unroll
+    for (int p2 = 0; p2 < 8; ++p2) head[p2] = 0;
+    for (int q = 0; q < K; ++q) {
+      unsigned long long best = 0ull;
+      int bp = 0;
+#pragma unroll
+      for (int p2 = 0; p2 < 8; ++p2) {
+        if (p2 < P && head[p2] < KL) {
+          const unsigned long long c = sl[((size_t)p2 * mt + t) * KL + head[p2]];
+          if (c > best) {
+            best = c;
+            bp = p2;
+          }
+        }
+      }
+#pragma unroll
+      for (int p2 = 0; p2 < 8; ++p2) head[p2] += (p2 == bp && best != 0ull);
+      const bool valid = best != 0ull;
+      e.topk_val[ob * K + q] = valid ? ord2f((uint32_t)(best >> 32)) : -INFINITY;
+      e.topk_idx[ob * K + q] = valid ? (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull)) : -1;
+    }
+  }
+}
+
 // Fused epilogue over a finished fp32 tile in LDS: tile[r * ts + t] is output column
 // col0 + r (for dual tiles: gate columns r < tc, up columns r >= tc) of token m0 + t,
 // before the per-row norm scale scale[t].
@@ -304,83 +397,10 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
       break;
     }
     case EPI_TOPK: {
-      // Per token: this tile's top-k (value desc, index asc) and (max, sum exp(v - max)).
-      // Thread (token t = tid % mt, part = tid / mt) scans columns part, part + P, ...
-      // (P = nth / mt parts per token): a wave reads one column for 64 consecutive tokens,
-      // which is conflict-free in the column-major tile.  Each thread keeps its best
-      // candidates as a sorted register list (branch-free insertion, static indices); the
-      // lists and partial (max, sum) pairs of a token are then merged through LDS.
-      constexpr int KMAX = 16;
-      const int K = e.topk;
-      const int tile_i = col0 / tc;
-      const int P = nth / mt;  // parts per token; threads past P * mt (mt not dividing nth) sit out
-      const int t = tid % mt, part = tid / mt;
-      const bool active = part < P;
-      const int ncol = min(tc, d.n - col0);
-      unsigned long long lst[KMAX];
-#pragma unroll
-      for (int q = 0; q < KMAX; ++q) lst[q] = 0ull;
-      float mx = -INFINITY, se = 0.f;
-      if (active && t < mv) {
-        const float sc = scale[t];
-        for (int r = part; r < ncol; r += P) mx = fmaxf(mx, sc * tile[r * ts + t]);
-        for (int r = part; r < ncol; r += P) {
-          const float v = sc * tile[r * ts + t];
-          se += __expf(v - mx);
-          unsigned long long key = argmax_key(v, (uint32_t)(col0 + r));
-#pragma unroll
-          for (int q = 0; q < KMAX; ++q) {
-            const unsigned long long hi = key > lst[q] ? key : lst[q];
-            key = key > lst[q] ? lst[q] : key;
-            lst[q] = hi;
-          }
-        }
-      }
-      __syncthreads();  // every read of the tile is done: its LDS is reused below
-      unsigned long long* sl = (unsigned long long*)tile;          // [P][mt][KMAX]
-      float* sm = (float*)(sl + (size_t)P * mt * KMAX);             // [P][mt][2]
-      if (active) {
-#pragma unroll
-        for (int q = 0; q < KMAX; ++q) sl[((size_t)part * mt + t) * KMAX + q] = lst[q];
-        sm[(part * mt + t) * 2] = mx;
-        sm[(part * mt + t) * 2 + 1] = se;
-      }
-      __syncthreads();
-      if (part == 0 && t < mv) {
-        float M = -INFINITY;
-        for (int p2 = 0; p2 < P; ++p2) M = fmaxf(M, sm[(p2 * mt + t) * 2]);
-        float S = 0.f;
-        for (int p2 = 0; p2 < P; ++p2) {
-          const float m2 = sm[(p2 * mt + t) * 2];
-          if (m2 > -INFINITY) S += sm[(p2 * mt + t) * 2 + 1] * __expf(m2 - M);
-        }
-        const int64_t ob = (int64_t)tile_i * d.m + m0 + t;  // tile-major: coalesced per workgroup
-        e.lse_part[ob * 2] = M;
-        e.lse_part[ob * 2 + 1] = S;
-        // P-way merge of the sorted lists (keys are unique: one per column)
-        int head[8];
-#pragma unroll
-        for (int p2 = 0; p2 < 8; ++p2) head[p2] = 0;
-        for (int q = 0; q < K; ++q) {
-          unsigned long long best = 0ull;
-          int bp = 0;
-#pragma unroll
-          for (int p2 = 0; p2 < 8; ++p2) {
-            if (p2 < P && head[p2] < KMAX) {
-              const unsigned long long c = sl[((size_t)p2 * mt + t) * KMAX + head[p2]];
-              if (c > best) {
-                best = c;
-                bp = p2;
-              }
-            }
-          }
-#pragma unroll
-          for (int p2 = 0; p2 < 8; ++p2) head[p2] += (p2 == bp && best != 0ull);
-          const bool valid = best != 0ull;
-          e.topk_val[ob * K + q] = valid ? ord2f((uint32_t)(best >> 32)) : -INFINITY;
-          e.topk_idx[ob * K + q] = valid ? (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull)) : -1;
-        }
-      }
+      if (e.topk <= 12)
+        epi_topk<12>(d, tile, ts, tc, col0, m0, mv, mt, scale);
+      else
+        epi_topk<16>(d, tile, ts, tc, col0, m0, mv, mt, scale);
       break;
     }
     default:
