@@ -236,6 +236,8 @@ __global__ __launch_bounds__(256) void draft_prep_kernel(DraftState s) {
 // Each thread keeps a sorted list of its best KMAX candidates (branch-free insertion,
 // static indices); each wave then selects its top K from its lanes' lists, and one
 // thread merges the four wave lists.
+// KL: length of the per-thread candidate lists (>= K): the sorted insertion costs KL steps.
+template <int KL>
 __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
   const int r = blockIdx.x;
   const int b = r / s.FL, j = r % s.FL;
@@ -246,31 +248,61 @@ __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
   const int Rl = s.B * s.FL;
   const float* lp = s.tk_lse + (int64_t)r * 2;
   const int64_t ls = (int64_t)Rl * 2;
+  // both passes over the tiles issue 4 loads per thread per round (clamped, unconditional)
+  const int nth = blockDim.x;
   float mx = -INFINITY;
-  for (int t = tid; t < s.n_tk; t += blockDim.x) mx = fmaxf(mx, lp[t * ls]);
+  for (int t0 = tid; t0 < s.n_tk; t0 += 4 * nth) {
+    float m4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m4[u] = lp[min(t0 + u * nth, s.n_tk - 1) * ls];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mx = fmaxf(mx, m4[u]);  // clamped repeats change no maximum
+  }
   mx = wave_max(mx);
   if (lane == 0) fred[w] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
   __syncthreads();
   float se = 0.f;
-  for (int t = tid; t < s.n_tk; t += blockDim.x) se += lp[t * ls + 1] * __expf(lp[t * ls] - mx);
+  for (int t0 = tid; t0 < s.n_tk; t0 += 4 * nth) {
+    float m4[4], s4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t o = (int64_t)min(t0 + u * nth, s.n_tk - 1) * ls;
+      m4[u] = lp[o];
+      s4[u] = lp[o + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (t0 + u * nth < s.n_tk) se += s4[u] * __expf(m4[u] - mx);
+  }
   se = wave_sum(se);
   if (lane == 0) fred[w] = se;
   __syncthreads();
   const float lse = mx + __logf((fred[0] + fred[1]) + (fred[2] + fred[3]));
 
-  unsigned long long lst[KMAX];
+  unsigned long long lst[KL];
 #pragma unroll
-  for (int i = 0; i < KMAX; ++i) lst[i] = 0ull;
-  // thread tid scans tiles tid, tid + 256, ... (the K candidates of a (tile, row) are adjacent)
+  for (int i = 0; i < KL; ++i) lst[i] = 0ull;
+  // thread tid scans tiles tid, tid + 256, ... (the K candidates of a (tile, row) are
+  // adjacent); a tile's K candidates are loaded together (unconditional, clamped loads),
+  // so each tile costs one round trip
   for (int t = tid; t < s.n_tk; t += blockDim.x) {
-    for (int q = 0; q < s.K; ++q) {
-      const int64_t o = ((int64_t)t * Rl + r) * s.K + q;
-      const int id = s.tk_idx[o];
-      unsigned long long key = id < 0 ? 0ull : argmax_key(s.tk_val[o], (uint32_t)id);
+    const int64_t o0 = ((int64_t)t * Rl + r) * s.K;
+    float vv[KL];
+    int ii[KL];
 #pragma unroll
-      for (int i = 0; i < KMAX; ++i) {
+    for (int q = 0; q < KL; ++q) {
+      const int64_t o = o0 + min(q, s.K - 1);
+      vv[q] = s.tk_val[o];
+      ii[q] = s.tk_idx[o];
+    }
+#pragma unroll
+    for (int q = 0; q < KL; ++q) {
+      if (q >= s.K) break;
+      unsigned long long key = ii[q] < 0 ? 0ull : argmax_key(vv[q], (uint32_t)ii[q]);
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
         const unsigned long long hi = key > lst[i] ? key : lst[i];
         key = key > lst[i] ? lst[i] : key;
         lst[i] = hi;
@@ -289,8 +321,8 @@ __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
     }
     if (best != 0ull && lst[0] == best) {
 #pragma unroll
-      for (int i = 0; i < KMAX - 1; ++i) lst[i] = lst[i + 1];
-      lst[KMAX - 1] = 0ull;
+      for (int i = 0; i < KL - 1; ++i) lst[i] = lst[i + 1];
+      lst[KL - 1] = 0ull;
     }
     if (lane == 0) wtop[w][q] = best;
   }
@@ -767,7 +799,10 @@ int draft_expand_impl(const eagle_dims* d, const eagle_draft_params* pr, const v
       if ((rc = gemm(g, L.p_lm[i], ST_LM_HEAD))) return rc;
     }
     timer_begin(timer, ST_DRAFT_TOPK, s);
-    hipLaunchKernelGGL(draft_topk_merge_kernel, dim3(Rl), dim3(256), 0, s, st);
+    if (pr->top_k <= 12)
+      hipLaunchKernelGGL(draft_topk_merge_kernel<12>, dim3(Rl), dim3(256), 0, s, st);
+    else
+      hipLaunchKernelGGL(draft_topk_merge_kernel<16>, dim3(Rl), dim3(256), 0, s, st);
     timer_end(timer, s);
     timer_begin(timer, ST_DRAFT_SELECT, s);
     hipLaunchKernelGGL(draft_select_kernel, dim3(B), dim3(256), 0, s, st);
