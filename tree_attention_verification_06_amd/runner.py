@@ -27,10 +27,6 @@ def with_packed_weights(weights, *, lm_head=True, layer=True):
     return w
 
 
-def with_packed_lm_head(weights):
-    """with_packed_weights for w_lm alone."""
-    return with_packed_weights(weights, layer=False)
-
 
 class TreeVerifier:
     """lm_layout: 0 if weights["w_lm"] is row-major [vocab][hidden], 1 if fragment-blocked;
