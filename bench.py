@@ -202,6 +202,7 @@ def bench_eagle_step(args):
     diag.close()
     dbytes, dflops = draft_roofline_bytes_flops(dims, p, B, wl.prefix_len)
     d_roof_ms = max(dbytes / (HBM_PEAK_GBS * 1e9), dflops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    eagle3 = bench_eagle3(args, wl, st, t, prefix0, feat, tok)
     nodes = B * p.max_nodes
     acc_mean = float(np.mean(acc))
     return {
@@ -216,9 +217,60 @@ def bench_eagle_step(args):
         "draft_roofline": {"bound": "hbm", "algorithmic_bytes": dbytes, "algorithmic_flops": dflops,
                            "t_roof_ms": round(d_roof_ms, 4), "frac": round(d_roof_ms / ms_draft, 4)},
         "draft_stage_ms": stages,
+        "eagle3": eagle3,
         "data": "synthetic: random-init draft head and target layer N(0,0.02), root features N(0,1), "
                 "draft KV prefix N(0,1); the roots of each step are the previous step's bonus tokens",
     }
+
+
+def bench_eagle3(args, wl, st, t, prefix0, feat, tok):
+    """EAGLE-3 draft input at the same shape: the root features are W_fuse [f_low; f_mid; f_high]
+    (eagle_fuse_features, K = 3H) instead of the top feature.  Times the fusion alone (HIP
+    events around n launches; HBM roofline of its weight stream) and whole EAGLE-3 steps
+    (fuse -> draft -> encode -> verify -> accept).  The one-layer target cannot produce three
+    feature levels, so every step fuses the same seeded synthetic low/mid/high features."""
+    import torch
+    import tree_attention_verification_06_amd as E
+    from workloads.configs import eagle3_inputs
+    n = args.eagle_steps
+    dims, B, H = wl.dims, wl.batch, wl.dims.hidden
+    w_np, f_np = eagle3_inputs(wl)
+    w_fuse = torch.from_numpy(w_np.view(np.int16)).cuda().view(torch.bfloat16)
+    feats = torch.from_numpy(f_np.view(np.int16)).cuda().view(torch.bfloat16)
+    layout = 1 if args.weight_layout == "packed" else 0
+    if layout:
+        w_fuse = E.eagle_pack_fragments(w_fuse)
+    root = torch.zeros(B, H, dtype=torch.float32, device="cuda")
+    ws = torch.empty(E.eagle_workspace_size(2, dims, B, 0, 0, 0), dtype=torch.uint8, device="cuda")
+    E.eagle_workspace_init(ws)
+
+    def fuse():
+        E.eagle_fuse_features(dims, w_fuse, feats, root, ws, w_layout=layout)
+    for _ in range(3):
+        fuse()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        fuse()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_fuse = e0.elapsed_time(e1) / n
+    t["prefix_len"].copy_(prefix0)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        fuse()
+        st.step(root, tok, t["prefix_len"])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / n
+    fbytes = H * 3 * H * 2 + B * 3 * H * 2 + B * H * 4
+    return {"fuse": f"W_fuse [{H}][{3 * H}] on [f_low; f_mid; f_high] of {B} sequences",
+            "ms_fuse": round(ms_fuse, 4), "ms_per_step": round(ms_step, 4),
+            "fuse_roofline": {"bound": "hbm", "algorithmic_bytes": fbytes,
+                              "frac": round(fbytes / (ms_fuse * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}}
 
 
 def cpu_baseline(wl, sample_nodes, min_seconds=10.0, max_steps=100):

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define EAGLE_ABI_VERSION 3
+#define EAGLE_ABI_VERSION 4
 
 typedef enum {
   EAGLE_OK = 0,
@@ -122,6 +122,23 @@ typedef struct {
   int32_t max_nodes;    /* final tree size per sequence, root included (2..128)       */
   float conf_threshold; /* a child is expandable iff its probability >= this, [0, 1]  */
 } eagle_draft_params;
+
+/* ---- EAGLE-3 draft input ----------------------------------------------------
+ * Method: "LLM parallel decoding EAGLE" (EAGLE vs EAGLE-2 table and FAQ: EAGLE-3 feeds
+ * the draft a fusion of the target's low-, mid- and high-level features rather than its
+ * top feature) and the "yuhuili" author page (EAGLE-3).  The pages give no formula; the
+ * reading here is one linear map with no bias:
+ *   root_feature[b] = W_fuse [f_low[b]; f_mid[b]; f_high[b]]
+ * after which eagle_draft_expand runs unchanged on root_feature (its FC takes
+ * [root_feature; E[root token]] at the first level).
+ * Inputs: w_fuse [H][3H] bf16, row-major (w_layout 0) or fragment-blocked (w_layout 1,
+ * eagle_pack_fragments); feats [batch][3H] bf16, the three features of each sequence
+ * concatenated.  Output: root_feature [batch][H] f32 (fp32 accumulation).
+ * Workspace: eagle_workspace_size(2, dims, batch, 0, 0, 0, NULL) bytes, zero-filled once.
+ * Errors: NULL pointers, batch < 1, w_layout not 0/1, misaligned workspace -> ARG;
+ * dims not bf16 or hidden not a multiple of 64 -> UNSUPPORTED; small workspace -> WORKSPACE. */
+int eagle_fuse_features(const eagle_dims* dims, const void* w_fuse, int32_t w_layout, const void* feats,
+                        int32_t batch, float* root_feature, void* workspace, size_t ws_bytes, void* stream);
 
 /* ---- weight packing ------------------------------------------------------
  * A layout of this library (the pages prescribe none): a fragment-blocked copy of
@@ -278,8 +295,8 @@ int eagle_draft_pool(const eagle_dims* dims, const eagle_draft_params* params, i
 
 /* ---- workspace -------------------------------------------------------------
  * Bytes of workspace a call needs.  which: 0 = eagle_tree_verify, 1 =
- * eagle_draft_expand.  params is used only for which == 1.  Returns 0 for
- * unsupported arguments. */
+ * eagle_draft_expand, 2 = eagle_fuse_features.  params is used only for
+ * which == 1.  Returns 0 for unsupported arguments. */
 size_t eagle_workspace_size(int32_t which, const eagle_dims* dims, int32_t batch, int32_t total_nodes,
                             int32_t max_nodes, int32_t max_prefix, const eagle_draft_params* params);
 

@@ -38,6 +38,17 @@ import numpy as np
 from .layer import as_f64, layer_rows, lm_head_logits
 
 
+def fuse_features(w_fuse, low, mid, high):
+    """EAGLE-3 draft input: the root feature is a fusion of the target's low-, mid- and
+    high-level features instead of its top feature ("LLM parallel decoding EAGLE" page,
+    EAGLE vs EAGLE-2 table and FAQ; "yuhuili" page, EAGLE-3).  The pages give no formula;
+    reading: one linear map without bias, W_fuse [H][3H] applied to [f_low; f_mid; f_high]
+    in that order.  Returns [B][H] in fp64; the draft expansion then takes it as the root
+    feature unchanged."""
+    x = np.concatenate([as_f64(low), as_f64(mid), as_f64(high)], axis=-1)
+    return x @ as_f64(w_fuse).T
+
+
 def log_softmax(z):
     m = z.max(axis=-1, keepdims=True)
     return z - m - np.log(np.exp(z - m).sum(axis=-1, keepdims=True))

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert E.lib().eagle_abi_version() == 3
+    assert E.lib().eagle_abi_version() == 4
     assert E.status_str(0) == "ok"
     assert "workspace" in E.status_str(A.EAGLE_ERR_WORKSPACE)
 
@@ -121,3 +121,25 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(A, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         A.lib()
+
+
+def test_fuse_features_host_errors():
+    from dataclasses import replace
+    L = E.lib()
+    ws_bytes = A.eagle_workspace_size(2, LLAMA8B, 16, 0, 0, 0)
+    assert ws_bytes > 0
+    assert A.eagle_workspace_size(2, TINY, 16, 0, 0, 0) == 0  # fp32 dims: unsupported
+    d = A.dims_struct(LLAMA8B)
+    ws = ctypes.c_void_p(1 << 20)
+
+    def fuse(dims=d, w=FAKE, layout=0, x=FAKE, b=16, out=FAKE, w_s=ws, nbytes=ws_bytes):
+        return L.eagle_fuse_features(ctypes.byref(dims), w, layout, x, b, out, w_s, nbytes, None)
+    assert fuse(w=None) == A.EAGLE_ERR_ARG
+    assert fuse(out=None) == A.EAGLE_ERR_ARG
+    assert fuse(b=0) == A.EAGLE_ERR_ARG
+    assert fuse(layout=2) == A.EAGLE_ERR_ARG
+    assert fuse(w_s=ctypes.c_void_p((1 << 20) + 16)) == A.EAGLE_ERR_ARG  # misaligned workspace
+    assert fuse(nbytes=ws_bytes - 1) == A.EAGLE_ERR_WORKSPACE
+    assert fuse(dims=A.dims_struct(TINY)) == A.EAGLE_ERR_UNSUPPORTED
+    assert fuse(dims=A.dims_struct(replace(LLAMA8B, hidden=4000))) == A.EAGLE_ERR_UNSUPPORTED
+

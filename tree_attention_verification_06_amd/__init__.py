@@ -3,15 +3,16 @@
 The C ABI (include/eagle.h) has four calls on the hot path: eagle_tree_build,
 eagle_tree_verify, eagle_accept_commit and eagle_draft_expand (plus
 eagle_draft_pool, which reads back the draft's candidate pool, and
-eagle_pack_fragments, a load-time weight layout for the LM head).  This package
+eagle_pack_fragments, a load-time weight layout, and eagle_fuse_features, the EAGLE-3 draft
+input).  This package
 re-exports them with the same names (argument marshalling only) and a small
 convenience runner.  The library must be built first (__graft_entry__.build());
 importing works without it, calling does not.
 """
 from ._abi import (EAGLE_BF16, EAGLE_F32, EAGLE_OK, EagleError, Timer, eagle_accept_commit, eagle_draft_expand,
-                   eagle_draft_pool, eagle_pack_fragments, eagle_tree_build, eagle_tree_verify, eagle_workspace_init, eagle_workspace_size,
+                   eagle_draft_pool, eagle_fuse_features, eagle_pack_fragments, eagle_tree_build, eagle_tree_verify, eagle_workspace_init, eagle_workspace_size,
                    lib, status_str, EagleDraftParams, STAGES, LIB_PATH)
 
 __all__ = ["EAGLE_BF16", "EAGLE_F32", "EAGLE_OK", "EagleError", "Timer", "eagle_accept_commit",
-           "eagle_draft_expand", "eagle_draft_pool", "eagle_pack_fragments", "eagle_tree_build", "eagle_tree_verify", "eagle_workspace_init",
+           "eagle_draft_expand", "eagle_draft_pool", "eagle_fuse_features", "eagle_pack_fragments", "eagle_tree_build", "eagle_tree_verify", "eagle_workspace_init",
            "eagle_workspace_size", "lib", "status_str", "EagleDraftParams", "STAGES", "LIB_PATH"]

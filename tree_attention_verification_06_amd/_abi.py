@@ -76,6 +76,7 @@ PROTOTYPES = {
     "eagle_workspace_size": (_S, [_I, ctypes.POINTER(EagleDims), _I, _I, _I, _I, ctypes.POINTER(EagleDraftParams)]),
     "eagle_workspace_init": (_I, [_P, _S, _P]),
     "eagle_pack_fragments": (_I, [_P, _I, _I, _P, _P]),
+    "eagle_fuse_features": (_I, [ctypes.POINTER(EagleDims), _P, _I, _P, _I, _P, _P, _S, _P]),
     "eagle_timer_create": (_P, [_I]),
     "eagle_timer_destroy": (None, [_P]),
     "eagle_timer_collect": (_I, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
@@ -235,6 +236,15 @@ def eagle_pack_fragments(w, out=None, stream=None):
         raise EagleError(EAGLE_ERR_ARG, "eagle_pack_fragments")
     _check(lib().eagle_pack_fragments(_p(w), rows, cols, _p(out), _stream(stream)), "eagle_pack_fragments")
     return out
+
+
+def eagle_fuse_features(dims, w_fuse, feats, root_feature, workspace, *, w_layout=0, stream=None):
+    """EAGLE-3 draft input (eagle_fuse_features): root_feature [B][H] f32 = W_fuse [B][3H] feats."""
+    d = dims if isinstance(dims, EagleDims) else dims_struct(dims)
+    B = feats.shape[0]
+    _check(lib().eagle_fuse_features(ctypes.byref(d), _p(w_fuse), int(w_layout), _p(feats), B, _p(root_feature),
+                                     _p(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "eagle_fuse_features")
 
 
 def eagle_workspace_init(workspace, stream=None):

@@ -128,6 +128,29 @@ XSeg seg(const void* p, int dtype, int64_t ld, const int32_t* idx = nullptr) {
   return s;
 }
 
+// Workspace of eagle_fuse_features: the split-K partials, sums of squares and counters of
+// its one GEMM (H outputs over K = 3H for `batch` rows).
+struct FuseLayout {
+  GemmPlan plan;
+  size_t part, ssq, counters, total;
+};
+FuseLayout fuse_layout(const eagle_dims* d, int B) {
+  FuseLayout L{};
+  if (!d || d->dtype != EAGLE_BF16 || B < 1 || d->hidden <= 0 || d->hidden % 64) return L;
+  L.plan = plan_gemm(EAGLE_BF16, d->hidden, 3 * d->hidden, B, 0, EPI_STORE_F32, d->head_dim);
+  size_t pf, sf, ci;
+  gemm_workspace(L.plan, &pf, &sf, &ci);
+  size_t off = 0;
+  L.part = off;
+  off += align256(std::max<size_t>(pf * 4, 1));
+  L.ssq = off;
+  off += align256(std::max<size_t>(sf * 4, 1));
+  L.counters = off;
+  off += align256(std::max<size_t>(ci * 4, 1));
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 // Verification of every node of every tree: one decoder layer + LM head with a fused argmax.
@@ -482,7 +505,38 @@ size_t eagle_workspace_size(int32_t which, const eagle_dims* dims, int32_t batch
                             int32_t max_nodes, int32_t max_prefix, const eagle_draft_params* params) {
   if (which == 0) return verify_workspace(dims, batch, total_nodes, max_nodes, max_prefix);
   if (which == 1) return draft_workspace(dims, params, batch, max_prefix);
+  if (which == 2) return fuse_layout(dims, batch).total;
   return 0;
+}
+
+int eagle_fuse_features(const eagle_dims* dims, const void* w_fuse, int32_t w_layout, const void* feats,
+                        int32_t batch, float* root_feature, void* workspace, size_t ws_bytes, void* stream) {
+  if (!dims || !w_fuse || !feats || !root_feature || !workspace || batch < 1) return EAGLE_ERR_ARG;
+  if (w_layout != 0 && w_layout != 1) return EAGLE_ERR_ARG;
+  if (((uintptr_t)workspace) & 255) return EAGLE_ERR_ARG;
+  if (dims->dtype != EAGLE_BF16 || dims->hidden <= 0 || dims->hidden % 64) return EAGLE_ERR_UNSUPPORTED;
+  const FuseLayout L = fuse_layout(dims, batch);
+  if (ws_bytes < L.total) return EAGLE_ERR_WORKSPACE;
+  const int H = dims->hidden;
+  char* w = (char*)workspace;
+  GemmDesc g{};
+  g.dtype = EAGLE_BF16;
+  g.w0 = w_fuse;
+  g.w_layout = w_layout;
+  g.n = H;
+  g.k = 3 * H;
+  g.ldw = 3 * H;
+  g.m = batch;
+  g.x.a = seg(feats, EAGLE_BF16, 3 * H);
+  g.x.b = g.x.a;
+  g.x.ka = 3 * H;
+  g.epi.kind = EPI_STORE_F32;
+  g.epi.out = root_feature;
+  g.epi.ld_out = H;
+  g.partials = (float*)(w + L.part);
+  g.sumsq_part = (float*)(w + L.ssq);
+  g.counters = (int*)(w + L.counters);
+  return launch_gemm(g, L.plan, (hipStream_t)stream);
 }
 
 int eagle_pack_fragments(const void* w, int32_t rows, int32_t cols, void* out, void* stream) {

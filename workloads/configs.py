@@ -74,7 +74,7 @@ CONFIGS = {
 TID = dict(x=1, k_prefix=2, v_prefix=3, tokens=4, w_qkv=10, w_o=11, w_gate=12, w_up=13, w_down=14,
            w_lm=15, embed=16, w_fc=17, ln_attn=18, ln_mlp=19, final_ln=20,
            d_w_qkv=30, d_w_o=31, d_w_gate=32, d_w_up=33, d_w_down=34, d_ln_attn=35, d_ln_mlp=36,
-           d_k_prefix=37, d_v_prefix=38, root_feature=39, root_token=40, tree=41)
+           d_k_prefix=37, d_v_prefix=38, root_feature=39, root_token=40, tree=41, w_fuse=42, fuse_feats=43)
 
 _ROWS_PER_CHUNK = 2048
 
@@ -244,6 +244,16 @@ def make_workload(cfg_id, seed=None, *, dims: LayerDims = None, batch=None, pref
         wl.root_feature = normal_tensor(seed, TID["root_feature"], (B, H), 1.0, "f32")
         wl.root_token = np.random.default_rng([seed, TID["root_token"]]).integers(0, V, size=B).astype(np.int32)
     return wl
+
+
+def eagle3_inputs(wl: Workload):
+    """Seeded EAGLE-3 draft inputs for a draft workload: the fusion matrix W_fuse [H][3H]
+    (N(0, 0.02)) and each sequence's low-, mid- and high-level target features [B][3H]
+    (N(0, 1)), both stored as bf16 bits."""
+    H, B = wl.dims.hidden, wl.batch
+    w_fuse = normal_tensor(wl.seed, TID["w_fuse"], (H, 3 * H), 0.02, "bf16")
+    feats = normal_tensor(wl.seed, TID["fuse_feats"], (B, 3 * H), 1.0, "bf16")
+    return w_fuse, feats
 
 
 def with_trees(wl: Workload, parents, tokens=None, x_seed_tid=None):
