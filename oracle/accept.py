@@ -47,6 +47,50 @@ def accept_sequence(parent, tokens, g, depth):
     return L, path, out, int(g[leaf]), leaf
 
 
+def sample_accept_sequence(parent, tokens, logits, temperature, u, gumbel):
+    """Acceptance when the target samples at temperature T > 0 ("Speculative decoding with
+    EAGLE", Deep dive and FAQ: accepted tokens must agree with the target's own choice, here
+    its own sample, so the output distribution is unchanged).  The pages give no procedure;
+    the reading is speculative sampling with deterministic candidates, walked from the root:
+      at node n, p = softmax(logits[n] / T); its children c (in index order) are tried in
+      turn: c is accepted iff u[c] * r < p(tokens[c]), where r is the probability mass left
+      after removing the tokens of the children already rejected (r = 1 at first); accepted
+      -> continue at c; all rejected (or a leaf) -> the bonus token is drawn from p with the
+      rejected tokens removed, as argmax_v (log p(v) + gumbel[n][v]) over the tokens left.
+    Each emitted token is then distributed exactly as the target's p at its position:
+    P(accept the i-th child) = p(x_i) and P(bonus = y) = p(y) for y outside the children's
+    tokens (sibling tokens are distinct).  u [n] uniforms in [0, 1) (u[c] decides node c),
+    gumbel [n][V] standard Gumbel noise, logits [n][V]; all consumed as given (inputs).
+    Returns (L, path root..leaf, out_tokens [L + 1], next_token, leaf)."""
+    n = len(parent)
+    children = [[] for _ in range(n)]
+    for j in range(1, n):
+        children[int(parent[j])].append(j)
+    node, path = 0, [0]
+    while True:
+        z = np.asarray(logits[node], dtype=np.float64) / float(temperature)
+        m = z.max()
+        logp = z - (m + np.log(np.exp(z - m).sum()))
+        rejected, r, nxt = [], 1.0, None
+        for c in children[node]:
+            x = int(tokens[c])
+            px = float(np.exp(logp[x]))
+            if float(u[c]) * r < px:
+                nxt = c
+                break
+            rejected.append(x)
+            r -= px
+        if nxt is None:
+            score = logp + np.asarray(gumbel[node], dtype=np.float64)
+            score[rejected] = -np.inf
+            bonus = int(np.argmax(score))
+            break
+        node = nxt
+        path.append(node)
+    out = [int(tokens[p]) for p in path[1:]] + [bonus]
+    return len(path) - 1, path, out, bonus, node
+
+
 def accept_batch(parents, tokens, g, encs):
     """accept_sequence for each tree of a batch (node arrays concatenated)."""
     sizes = [len(p) for p in parents]
