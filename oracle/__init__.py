@@ -34,13 +34,15 @@ decoding).
 from .tree import tree_encode, pack_ancestors, encode_batch, TreeEncoding
 from .layer import (as_f64, rms_norm, rope_rotate_half, attend, layer_rows, verify_forward,
                     lm_head_logits, lm_head_argmax, silu)
-from .accept import accept_sequence, accept_batch, commit_sequence, sample_accept_sequence
+from .accept import (accept_sequence, accept_batch, commit_sequence, sample_accept_sequence, sample_summaries,
+                     sample_accept_from_summaries)
 from .draft import draft_expand, draft_select_level, draft_rerank, fuse_features
 
 __all__ = [
     "tree_encode", "pack_ancestors", "encode_batch", "TreeEncoding",
     "as_f64", "rms_norm", "rope_rotate_half", "attend", "layer_rows", "verify_forward",
     "lm_head_logits", "lm_head_argmax", "silu",
-    "accept_sequence", "accept_batch", "commit_sequence", "sample_accept_sequence",
+    "accept_sequence", "accept_batch", "commit_sequence", "sample_accept_sequence", "sample_summaries",
+    "sample_accept_from_summaries",
     "draft_expand", "draft_select_level", "draft_rerank", "fuse_features",
 ]

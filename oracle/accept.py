@@ -47,7 +47,7 @@ def accept_sequence(parent, tokens, g, depth):
     return L, path, out, int(g[leaf]), leaf
 
 
-def sample_accept_sequence(parent, tokens, logits, temperature, u, gumbel):
+def sample_accept_sequence(parent, tokens, logits, temperature, u, gumbel, trace=None):
     """Acceptance when the target samples at temperature T > 0 ("Speculative decoding with
     EAGLE", Deep dive and FAQ: accepted tokens must agree with the target's own choice, here
     its own sample, so the output distribution is unchanged).  The pages give no procedure;
@@ -61,7 +61,9 @@ def sample_accept_sequence(parent, tokens, logits, temperature, u, gumbel):
     P(accept the i-th child) = p(x_i) and P(bonus = y) = p(y) for y outside the children's
     tokens (sibling tokens are distinct).  u [n] uniforms in [0, 1) (u[c] decides node c),
     gumbel [n][V] standard Gumbel noise, logits [n][V]; all consumed as given (inputs).
-    Returns (L, path root..leaf, out_tokens [L + 1], next_token, leaf)."""
+    Only one bonus is drawn per call, at a node fixed by u alone, so every node may be given
+    the same noise row.  trace (a list, optional) receives (c, u[c] * r, p(tokens[c])) for
+    every child tried.  Returns (L, path root..leaf, out_tokens [L + 1], next_token, leaf)."""
     n = len(parent)
     children = [[] for _ in range(n)]
     for j in range(1, n):
@@ -75,6 +77,8 @@ def sample_accept_sequence(parent, tokens, logits, temperature, u, gumbel):
         for c in children[node]:
             x = int(tokens[c])
             px = float(np.exp(logp[x]))
+            if trace is not None:
+                trace.append((c, float(u[c]) * r, px))
             if float(u[c]) * r < px:
                 nxt = c
                 break
@@ -84,6 +88,76 @@ def sample_accept_sequence(parent, tokens, logits, temperature, u, gumbel):
             score = logp + np.asarray(gumbel[node], dtype=np.float64)
             score[rejected] = -np.inf
             bonus = int(np.argmax(score))
+            break
+        node = nxt
+        path.append(node)
+    out = [int(tokens[p]) for p in path[1:]] + [bonus]
+    return len(path) - 1, path, out, bonus, node
+
+
+def sample_summaries(parent, tokens, logits, temperature, gumbel_row):
+    """Per-node summaries of the target's logits that the walk of sample_accept_sequence needs,
+    with z = logits / T (fp64), for one tree sharing the noise row gumbel_row [V]:
+      child_logit[c] = z[parent(c)][tokens[c]] for every non-root node c (NaN at the root);
+      over the tokens that are not the token of a child of n ("the rest" of node n):
+      rest_lse[n] = log sum exp z[n], rest_token[n] = argmax (z[n] + gumbel_row) (first
+      index on ties).
+    The vocabulary of node n splits into its child tokens and the rest, so its log-normaliser
+    is the log-sum-exp of rest_lse[n] and its children's child_logit; a walk that stops at n
+    has rejected every child, so its bonus argmax over the non-rejected tokens is
+    rest_token[n].  Sibling tokens must be distinct (else ValueError)."""
+    n = len(parent)
+    z = np.asarray(logits, dtype=np.float64) / float(temperature)
+    V = z.shape[1]
+    g = np.asarray(gumbel_row, dtype=np.float64)
+    child_logit = np.full(n, np.nan)
+    kids = [[] for _ in range(n)]
+    for c in range(1, n):
+        kids[int(parent[c])].append(int(tokens[c]))
+        child_logit[c] = z[int(parent[c]), int(tokens[c])]
+    rest_lse = np.zeros(n)
+    rest_token = np.zeros(n, dtype=np.int64)
+    for node in range(n):
+        if len(set(kids[node])) != len(kids[node]):
+            raise ValueError(f"node {node}: two children with the same token")
+        rest = np.ones(V, dtype=bool)
+        rest[kids[node]] = False
+        zr = z[node][rest]
+        m = zr.max()
+        rest_lse[node] = m + np.log(np.exp(zr - m).sum())
+        score = z[node] + g
+        score[~rest] = -np.inf
+        rest_token[node] = int(np.argmax(score))
+    return child_logit, rest_lse, rest_token
+
+
+def sample_accept_from_summaries(parent, tokens, child_logit, rest_lse, rest_token, u, trace=None):
+    """The walk of sample_accept_sequence on the summaries of sample_summaries (fp64): at node
+    n the log-normaliser is logsumexp(rest_lse[n], child_logit of n's children); children are
+    tried in index order, c accepted iff u[c] * r < exp(child_logit[c] - that), r -= that
+    probability on rejection; the walk stops at the first node whose children are all
+    rejected (or a leaf), with the bonus rest_token[n].  trace as in sample_accept_sequence.
+    Returns (L, path, out_tokens, next_token, leaf)."""
+    n = len(parent)
+    children = [[] for _ in range(n)]
+    for j in range(1, n):
+        children[int(parent[j])].append(j)
+    node, path = 0, [0]
+    while True:
+        terms = [float(rest_lse[node])] + [float(child_logit[c]) for c in children[node]]
+        m = max(terms)
+        lse = m + np.log(sum(np.exp(t - m) for t in terms))
+        r, nxt = 1.0, None
+        for c in children[node]:
+            px = float(np.exp(float(child_logit[c]) - lse))
+            if trace is not None:
+                trace.append((c, float(u[c]) * r, px))
+            if float(u[c]) * r < px:
+                nxt = c
+                break
+            r -= px
+        if nxt is None:
+            bonus = int(rest_token[node])
             break
         node = nxt
         path.append(node)

@@ -74,7 +74,7 @@ CONFIGS = {
 TID = dict(x=1, k_prefix=2, v_prefix=3, tokens=4, w_qkv=10, w_o=11, w_gate=12, w_up=13, w_down=14,
            w_lm=15, embed=16, w_fc=17, ln_attn=18, ln_mlp=19, final_ln=20,
            d_w_qkv=30, d_w_o=31, d_w_gate=32, d_w_up=33, d_w_down=34, d_ln_attn=35, d_ln_mlp=36,
-           d_k_prefix=37, d_v_prefix=38, root_feature=39, root_token=40, tree=41, w_fuse=42, fuse_feats=43)
+           d_k_prefix=37, d_v_prefix=38, root_feature=39, root_token=40, tree=41, w_fuse=42, fuse_feats=43, gumbel=44, accept_u=45)
 
 _ROWS_PER_CHUNK = 2048
 
@@ -254,6 +254,22 @@ def eagle3_inputs(wl: Workload):
     w_fuse = normal_tensor(wl.seed, TID["w_fuse"], (H, 3 * H), 0.02, "bf16")
     feats = normal_tensor(wl.seed, TID["fuse_feats"], (B, 3 * H), 1.0, "bf16")
     return w_fuse, feats
+
+
+def sample_inputs(wl: Workload, draw=0, n_nodes=None):
+    """Seeded random inputs of acceptance at temperature T > 0 for a workload with trees:
+    one row of standard Gumbel noise per tree, gumbel [B][V] = -log(-log U) with U uniform
+    on the open interval (0, 1) (float64, stored as float32), and one acceptance uniform per
+    node, u [sum N] in [0, 1) (float32).  ``draw`` selects an independent set; ``n_nodes``
+    overrides sum N (e.g. batch * max_nodes for trees a draft step will build)."""
+    B, V = wl.batch, wl.dims.vocab
+    n = wl.n_nodes if n_nodes is None else int(n_nodes)
+    rng = np.random.default_rng([wl.seed, TID["gumbel"], draw])
+    U = rng.random((B, V))
+    U = np.where(U > 0.0, U, np.nextafter(0.0, 1.0))
+    gumbel = (-np.log(-np.log(U))).astype(np.float32)
+    u = np.random.default_rng([wl.seed, TID["accept_u"], draw]).random(n).astype(np.float32)
+    return gumbel, u
 
 
 def with_trees(wl: Workload, parents, tokens=None, x_seed_tid=None):
