@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--weight-layout", choices=["packed", "row"], default="packed",
                     help="weight matrices (LM head, layer, draft): fragment-blocked (packed once at load) "
                          "or row-major")
+    ap.add_argument("--temperature", type=float, default=1.0,
+                    help="temperature of the sampling-acceptance measurements (T > 0)")
     ap.add_argument("--eagle-only", action="store_true",
                     help="run only the full EAGLE step (for profiling its kernels apart from the verify step)")
     return ap.parse_args()
@@ -144,7 +146,8 @@ def bench_eagle_step(args):
     weights, layout = laid_out(t["weights"], args)
     draft_weights, _ = laid_out(t["draft_weights"], args)
     st = EagleStep(dims, p, weights, draft_weights, t["k_cache"], t["v_cache"], t["dk_cache"],
-                   t["dv_cache"], batch=B, max_prefix=wl.cache_cap, lm_layout=layout, weight_layout=layout)
+                   t["dv_cache"], batch=B, max_prefix=wl.cache_cap, lm_layout=layout, weight_layout=layout,
+                   sample=True)
     d, v = st.drafter, st.verifier
     prefix0 = t["prefix_len"].clone()
     feat = t["root_feature"].clone()
@@ -203,6 +206,7 @@ def bench_eagle_step(args):
     dbytes, dflops = draft_roofline_bytes_flops(dims, p, B, wl.prefix_len)
     d_roof_ms = max(dbytes / (HBM_PEAK_GBS * 1e9), dflops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
     eagle3 = bench_eagle3(args, wl, st, t, prefix0, feat, tok)
+    sampling = bench_sampling(args, wl, st, t, prefix0, feat, tok)
     nodes = B * p.max_nodes
     acc_mean = float(np.mean(acc))
     return {
@@ -218,8 +222,96 @@ def bench_eagle_step(args):
                            "t_roof_ms": round(d_roof_ms, 4), "frac": round(d_roof_ms / ms_draft, 4)},
         "draft_stage_ms": stages,
         "eagle3": eagle3,
+        "sampling": sampling,
         "data": "synthetic: random-init draft head and target layer N(0,0.02), root features N(0,1), "
                 "draft KV prefix N(0,1); the roots of each step are the previous step's bonus tokens",
+    }
+
+
+def bench_sampling(args, wl, st, t, prefix0, feat, tok):
+    """Acceptance at temperature T > 0 at the same shape (16 trees of up to 60 drafted nodes):
+    the sampling verification alone (encode + eagle_tree_verify_sample on fixed drafted trees;
+    its LM head reads one noise row of V floats per tree on top of the weights) and whole
+    sampling steps (draft -> encode -> verify_sample -> accept_sample, decode loop).  The
+    noise rows and acceptance uniforms are seeded inputs, resident before the timed region
+    and reused by every step."""
+    import torch
+    import tree_attention_verification_06_amd as E
+    from workloads.configs import sample_inputs
+
+    n = args.eagle_steps
+    T = args.temperature
+    d, v = st.drafter, st.verifier
+    gumbel, u = sample_inputs(wl, 0, n_nodes=st.total)
+    g_t = torch.from_numpy(gumbel).cuda()
+    u_t = torch.from_numpy(u).cuda()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # verification alone, on the trees of one draft expansion
+    t["prefix_len"].copy_(prefix0)
+    d.expand(feat, tok, t["prefix_len"])
+    tokens_fixed = d.tokens.clone()
+    plen = t["prefix_len"].clone()
+
+    def verify_only(k, timer=None):
+        for _ in range(k):
+            v.encode(d.tree_off, d.parent, plen, st.total)
+            v.verify_sample(d.tree_off, tokens_fixed, d.parent, plen, st.total, T, g_t, timer=timer)
+
+    verify_only(3)
+    torch.cuda.synchronize()
+    lm = E.Timer(capacity=4 * (n + 1), stages=["lm_head"])
+    e0.record(stream)
+    verify_only(n, lm)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_verify = e0.elapsed_time(e1) / n
+    lm_ms, lm_n = lm.collect().get("lm_head", (0.0, 0))
+    lm.close()
+    diag = E.Timer(capacity=64)
+    verify_only(3, diag)
+    torch.cuda.synchronize()
+    stages = {k: round(ms / 3, 5) for k, (ms, c) in diag.collect().items()}
+    diag.close()
+
+    # whole sampling steps
+    f, tk = feat.clone(), tok.clone()
+
+    def run(k, count=False):
+        nonlocal f, tk
+        acc = []
+        for _ in range(k):
+            nf, nt = st.step_sample(f, tk, t["prefix_len"], T, g_t, u_t)
+            f, tk = nf.clone(), nt.clone()
+            if count:
+                acc.append(int((v.accept_len + 1).sum().item()))
+        return acc
+
+    t["prefix_len"].copy_(prefix0)
+    run(3)
+    t["prefix_len"].copy_(prefix0)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    run(n)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / n
+    st_code = int(v.status.item())
+    if st_code != 0:
+        raise RuntimeError(f"device status {st_code} ({E.status_str(st_code)})")
+    t["prefix_len"].copy_(prefix0)
+    acc = run(min(n, 10), count=True)
+    acc_mean = float(np.mean(acc))
+    nodes = st.total
+    return {
+        "temperature": T, "ms_verify": round(ms_verify, 4),
+        "verify_nodes_s": round(nodes / (ms_verify * 1e-3), 1),
+        "lm_head_ms": round(lm_ms / max(lm_n, 1), 4),
+        "verify_stage_ms": stages,
+        "ms_per_step": round(ms_step, 4),
+        "accepted_per_step": acc_mean, "accepted_tok_s": round(acc_mean / (ms_step * 1e-3), 1),
+        "noise_bytes_per_step": int(gumbel.nbytes),
+        "data": "seeded Gumbel noise rows [B][V] and acceptance uniforms, fixed across steps",
     }
 
 

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define EAGLE_ABI_VERSION 4
+#define EAGLE_ABI_VERSION 5
 
 typedef enum {
   EAGLE_OK = 0,
@@ -234,6 +234,64 @@ int eagle_accept_commit(int32_t batch, const int32_t* tree_off, int32_t max_node
                         float* next_feature, int32_t max_accept, int32_t* accept_len, int32_t* path,
                         int32_t* out_tokens, int32_t* next_token, int32_t* dev_status, void* stream);
 
+/* ---- verification and acceptance at temperature T > 0 ---------------------
+ * Method: "Speculative decoding with EAGLE", Deep dive and FAQ (the accepted
+ * tokens follow the target's own distribution, so decoding is lossless).  The
+ * pages give no sampling procedure; the reading implemented is speculative
+ * sampling with the tree's tokens as deterministic candidates, walked from the
+ * root: at node n with p = softmax(logits_n / T), its children c are tried in
+ * index order; c is accepted iff u[c] * r < p(tokens[c]), r being the mass left
+ * once the tokens of the rejected elder siblings are removed (r = 1 at first);
+ * on acceptance the walk moves to c.  When every child of n is rejected (or n is
+ * a leaf) the bonus token is drawn from p without n's child tokens by the
+ * Gumbel-max rule, argmax_v (log p(v) + gumbel[b][v]).  Each emitted token is
+ * then distributed as the target's p at its position.  Exactly one bonus is
+ * drawn per sequence and where it is drawn depends on u only, so the noise row
+ * gumbel[b] is shared by every node of tree b.  Sibling tokens must be distinct.
+ *
+ * eagle_tree_verify_sample: the decoder layer of eagle_tree_verify (same
+ * arguments, plus parent [total_nodes] local parents and tokens required), then
+ * the LM head summarised per node n (v = logits_n / T):
+ *   child_logit[c] = v_{parent(c)}[tokens[c]] for every non-root node c (the
+ *   root's entry is not written);
+ *   rest_lse[n] = log sum_v exp(v) over the tokens that are not a child token of n;
+ *   rest_token[n] = argmax over the same tokens of v + gumbel[b][token] (ties:
+ *   the lower id), b the tree of n.
+ * The [total_nodes][vocab] logits are never written.  gumbel [B][V] f32 standard
+ * Gumbel noise (device).  temperature > 0 and finite 1/T, else EAGLE_ERR_ARG.
+ * Rows past tree_off[B] are computed and meaningless.  Workspace:
+ * eagle_workspace_size(3, ...). */
+int eagle_tree_verify_sample(const eagle_dims* dims, const eagle_layer_w* layer, const void* final_ln,
+                             const void* w_lm, int32_t batch, const int32_t* tree_off, int32_t total_nodes,
+                             int32_t max_nodes, const void* x_in, const void* embed, const int32_t* tokens,
+                             const int32_t* parent, const uint64_t* anc, int32_t mask_words, const int32_t* pos,
+                             const int32_t* prefix_len, int32_t max_prefix, const void* k_cache,
+                             const void* v_cache, const eagle_cache_layout* cache, float temperature,
+                             const float* gumbel, void* k_tree, void* v_tree, float* h_out, float* child_logit,
+                             float* rest_lse, int32_t* rest_token, void* workspace, size_t ws_bytes,
+                             eagle_timer* timer, void* stream);
+
+/* eagle_accept_commit_sample: the walk above per tree b from the outputs of
+ * eagle_tree_verify_sample: the log-normaliser of node n is the log-sum-exp of
+ * rest_lse[n] and the child_logit of its children; p(tokens[c]) =
+ * exp(child_logit[c] - that); the bonus of the node where the walk stops is
+ * rest_token[n].  u [total_nodes] uniforms in [0, 1), u[c] decides node c.
+ * Outputs and commit exactly as eagle_accept_commit (path root..leaf,
+ * out_tokens = accepted tokens then the bonus, next_token = the bonus,
+ * next_feature = h_nodes[leaf]).  Host errors as eagle_accept_commit, and
+ * max_nodes > 128 -> EAGLE_ERR_CAPACITY.  Device errors: a tree of more than 128
+ * nodes -> EAGLE_ERR_CAPACITY; parent[0] != -1, parent[i] outside [0, i) or two
+ * siblings with the same token -> EAGLE_ERR_TREE; L > max_accept or no cache
+ * room -> EAGLE_ERR_CAPACITY; such a sequence gets accept_len -1 and no commit. */
+int eagle_accept_commit_sample(int32_t batch, const int32_t* tree_off, int32_t max_nodes, const int32_t* parent,
+                               const int32_t* tokens, const float* child_logit, const float* rest_lse,
+                               const int32_t* rest_token, const float* u, const void* k_tree, const void* v_tree,
+                               void* k_cache, void* v_cache, const eagle_cache_layout* cache, int32_t n_kv_heads,
+                               int32_t head_dim, int32_t dtype, int32_t* prefix_len, const float* h_nodes,
+                               int32_t hidden, float* next_feature, int32_t max_accept, int32_t* accept_len,
+                               int32_t* path, int32_t* out_tokens, int32_t* next_token, int32_t* dev_status,
+                               void* stream);
+
 /* ---- draft-head tree expansion -------------------------------------------
  * Method: "Speculative decoding with EAGLE", Technical insight (feature-level
  * draft head fed the true previous-token embedding; reuses the target LM
@@ -295,7 +353,7 @@ int eagle_draft_pool(const eagle_dims* dims, const eagle_draft_params* params, i
 
 /* ---- workspace -------------------------------------------------------------
  * Bytes of workspace a call needs.  which: 0 = eagle_tree_verify, 1 =
- * eagle_draft_expand, 2 = eagle_fuse_features.  params is used only for
+ * eagle_draft_expand, 2 = eagle_fuse_features, 3 = eagle_tree_verify_sample.  params is used only for
  * which == 1.  Returns 0 for unsupported arguments. */
 size_t eagle_workspace_size(int32_t which, const eagle_dims* dims, int32_t batch, int32_t total_nodes,
                             int32_t max_nodes, int32_t max_prefix, const eagle_draft_params* params);

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert E.lib().eagle_abi_version() == 4
+    assert E.lib().eagle_abi_version() == 5
     assert E.status_str(0) == "ok"
     assert "workspace" in E.status_str(A.EAGLE_ERR_WORKSPACE)
 
@@ -143,3 +143,50 @@ def test_fuse_features_host_errors():
     assert fuse(dims=A.dims_struct(TINY)) == A.EAGLE_ERR_UNSUPPORTED
     assert fuse(dims=A.dims_struct(replace(LLAMA8B, hidden=4000))) == A.EAGLE_ERR_UNSUPPORTED
 
+
+
+def test_verify_sample_host_errors():
+    from dataclasses import replace
+    L = E.lib()
+    d = A.dims_struct(LLAMA8B)
+    lw = A.EagleLayerW(4096, 4096, 4096, 4096, 4096, 4096, 4096, 0)
+    cl = A.EagleCacheLayout(1 << 20, 1 << 16, 128, 4096)
+    ws_bytes = A.eagle_workspace_size(3, LLAMA8B, 1, 60, 60, 2048)
+    assert ws_bytes > A.eagle_workspace_size(0, LLAMA8B, 1, 60, 60, 2048) > 0
+    ws = ctypes.c_void_p(1 << 20)
+
+    def call(dims=d, temperature=1.0, gumbel=FAKE, tokens=FAKE, parent=FAKE, out=FAKE, nbytes=ws_bytes):
+        return L.eagle_tree_verify_sample(ctypes.byref(dims), ctypes.byref(lw), FAKE, FAKE, 1, FAKE, 60, 60, FAKE,
+                                          None, tokens, parent, FAKE, 1, FAKE, FAKE, 2048, FAKE, FAKE,
+                                          ctypes.byref(cl), temperature, gumbel, FAKE, FAKE, FAKE, out, FAKE, FAKE,
+                                          ws, nbytes, None, None)
+    assert call(temperature=0.0) == A.EAGLE_ERR_ARG
+    assert call(temperature=-1.0) == A.EAGLE_ERR_ARG
+    assert call(temperature=float("nan")) == A.EAGLE_ERR_ARG
+    assert call(temperature=1e-45) == A.EAGLE_ERR_ARG  # 1/T overflows
+    assert call(gumbel=None) == A.EAGLE_ERR_ARG
+    assert call(tokens=None) == A.EAGLE_ERR_ARG
+    assert call(parent=None) == A.EAGLE_ERR_ARG
+    assert call(out=None) == A.EAGLE_ERR_ARG
+    assert call(nbytes=ws_bytes - 1) == A.EAGLE_ERR_WORKSPACE
+    assert call(dims=A.dims_struct(replace(LLAMA8B, head_dim=96))) == A.EAGLE_ERR_UNSUPPORTED
+
+
+def test_accept_sample_host_errors():
+    cl = A.EagleCacheLayout(1 << 20, 1 << 16, 128, 4096)
+    f = E.lib().eagle_accept_commit_sample
+
+    def call(**kw):
+        a = dict(B=1, maxn=60, hkv=8, hd=128, dtype=0, max_accept=16, tree_off=FAKE, u=FAKE, cl=FAKE)
+        a.update(kw)
+        return f(a["B"], a["tree_off"], a["maxn"], FAKE, FAKE, a["cl"], FAKE, FAKE, a["u"], FAKE, FAKE, FAKE, FAKE,
+                 ctypes.byref(cl), a["hkv"], a["hd"], a["dtype"], FAKE, None, 4096, None, a["max_accept"], FAKE,
+                 FAKE, FAKE, FAKE, None, None)
+    assert call(B=0) == A.EAGLE_ERR_ARG
+    assert call(tree_off=None) == A.EAGLE_ERR_ARG
+    assert call(u=None) == A.EAGLE_ERR_ARG
+    assert call(cl=None) == A.EAGLE_ERR_ARG
+    assert call(maxn=129) == A.EAGLE_ERR_CAPACITY
+    assert call(dtype=5) == A.EAGLE_ERR_UNSUPPORTED
+    assert call(max_accept=500) == A.EAGLE_ERR_ARG
+    assert call(hd=4) == A.EAGLE_ERR_UNSUPPORTED

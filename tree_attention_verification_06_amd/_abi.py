@@ -68,6 +68,13 @@ PROTOTYPES = {
     "eagle_accept_commit": (_I, [_I, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
                                  ctypes.POINTER(EagleCacheLayout), _I, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P,
                                  _P, _P]),
+    "eagle_tree_verify_sample": (_I, [ctypes.POINTER(EagleDims), ctypes.POINTER(EagleLayerW), _P, _P, _I, _P, _I,
+                                      _I, _P, _P, _P, _P, _P, _I, _P, _P, _I, _P, _P,
+                                      ctypes.POINTER(EagleCacheLayout), ctypes.c_float, _P, _P, _P, _P, _P, _P, _P,
+                                      _P, _S, _P, _P]),
+    "eagle_accept_commit_sample": (_I, [_I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                        ctypes.POINTER(EagleCacheLayout), _I, _I, _I, _P, _P, _I, _P, _I, _P, _P,
+                                        _P, _P, _P, _P]),
     "eagle_draft_expand": (_I, [ctypes.POINTER(EagleDims), ctypes.POINTER(EagleDraftParams), _P,
                                 ctypes.POINTER(EagleLayerW), _P, _P, _P, _I, _P, _P, _P, _P,
                                 ctypes.POINTER(EagleCacheLayout), _P, _I, _P, _P, _P, _P, _P, _S, _P, _P]),
@@ -189,6 +196,38 @@ def eagle_accept_commit(tree_off, parent, tokens, argmax, anc, mask_words, depth
                                    hidden, _p(next_feature), max_accept, _p(accept_len), _p(path), _p(out_tokens),
                                    _p(next_token), _p(dev_status), _stream(stream))
     _check(st, "eagle_accept_commit")
+
+
+def eagle_tree_verify_sample(dims, layer, final_ln, w_lm, tree_off, x_in, embed, tokens, parent, anc, mask_words,
+                             pos, prefix_len, k_cache, v_cache, temperature, gumbel, k_tree, v_tree, h_out,
+                             child_logit, rest_lse, rest_token, workspace, *, total_nodes, max_nodes, max_prefix,
+                             timer=None, stream=None):
+    d = dims_struct(dims) if not isinstance(dims, EagleDims) else dims
+    lw = layer_struct(layer) if not isinstance(layer, EagleLayerW) else layer
+    cl = cache_struct(k_cache)
+    B = tree_off.numel() - 1
+    st = lib().eagle_tree_verify_sample(ctypes.byref(d), ctypes.byref(lw), _p(final_ln), _p(w_lm), B, _p(tree_off),
+                                        total_nodes, max_nodes, _p(x_in), _p(embed), _p(tokens), _p(parent),
+                                        _p(anc), mask_words, _p(pos), _p(prefix_len), max_prefix, _p(k_cache),
+                                        _p(v_cache), ctypes.byref(cl), float(temperature), _p(gumbel), _p(k_tree),
+                                        _p(v_tree), _p(h_out), _p(child_logit), _p(rest_lse), _p(rest_token),
+                                        _p(workspace), workspace.numel() * workspace.element_size(), _t(timer),
+                                        _stream(stream))
+    _check(st, "eagle_tree_verify_sample")
+
+
+def eagle_accept_commit_sample(tree_off, parent, tokens, child_logit, rest_lse, rest_token, u, k_tree, v_tree,
+                               k_cache, v_cache, prefix_len, h_nodes, next_feature, accept_len, path, out_tokens,
+                               next_token, dev_status=None, *, max_nodes, max_accept, n_kv_heads, head_dim, dtype,
+                               hidden, stream=None):
+    cl = cache_struct(k_cache)
+    B = tree_off.numel() - 1
+    st = lib().eagle_accept_commit_sample(B, _p(tree_off), max_nodes, _p(parent), _p(tokens), _p(child_logit),
+                                          _p(rest_lse), _p(rest_token), _p(u), _p(k_tree), _p(v_tree), _p(k_cache),
+                                          _p(v_cache), ctypes.byref(cl), n_kv_heads, head_dim, dtype, _p(prefix_len),
+                                          _p(h_nodes), hidden, _p(next_feature), max_accept, _p(accept_len),
+                                          _p(path), _p(out_tokens), _p(next_token), _p(dev_status), _stream(stream))
+    _check(st, "eagle_accept_commit_sample")
 
 
 def eagle_draft_expand(dims, params, w_fc, draft_layer, final_ln, w_lm, embed, root_feature, root_token, dk_cache,

@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "attn.h"
@@ -62,12 +63,14 @@ int check_dims(const eagle_dims* d) {
 
 struct VerifyLayout {
   size_t q, attn, y, act, attn_part, gemm_part, gemm_ssq, counters, keys, done, total;
+  size_t gparent, row_tree, samp_part;  // sampling LM head only
   size_t y16, h16, ssq_y, ssq_h;  // bf16 path: gain-scaled bf16 copies and row sum-of-squares partials
   GemmPlan p_qkv, p_o, p_gu, p_down, p_lm;
   AttnPlan pa;
 };
 
-VerifyLayout plan_verify(const eagle_dims* d, int B, int total_nodes, int max_nodes, int max_prefix) {
+VerifyLayout plan_verify(const eagle_dims* d, int B, int total_nodes, int max_nodes, int max_prefix,
+                         bool sample = false) {
   VerifyLayout L{};
   const int es = elem_size(d->dtype);
   const int M = total_nodes;
@@ -78,7 +81,7 @@ VerifyLayout plan_verify(const eagle_dims* d, int B, int total_nodes, int max_no
     L.p_gu = plan_gemm(d->dtype, F, H, M, 1, EPI_SILU, D);
     L.p_down = plan_gemm(d->dtype, H, F, M, 0, EPI_RESID, D);
   }
-  L.p_lm = plan_gemm(d->dtype, V, H, M, 0, EPI_ARGMAX, D);
+  L.p_lm = plan_gemm(d->dtype, V, H, M, 0, sample ? EPI_SAMPLE : EPI_ARGMAX, D);
   L.pa = plan_attn(d->dtype, B, Hq, Hkv, D, max_nodes, max_prefix);
   size_t pf = 0, sf = 0, ci = 0;
   for (const GemmPlan* p : {&L.p_qkv, &L.p_o, &L.p_gu, &L.p_down, &L.p_lm}) {
@@ -109,6 +112,11 @@ VerifyLayout plan_verify(const eagle_dims* d, int B, int total_nodes, int max_no
   L.h16 = take((size_t)M * H * 2);
   L.ssq_y = take((size_t)std::max(L.p_o.n_tiles, 1) * M * 4);
   L.ssq_h = take((size_t)std::max(F > 0 ? L.p_down.n_tiles : L.p_o.n_tiles, 1) * M * 4);
+  if (sample) {
+    L.gparent = take((size_t)M * 4);
+    L.row_tree = take((size_t)M * 4);
+    L.samp_part = take((size_t)M * L.p_lm.n_tiles * 16);
+  }
   L.total = off;
   return L;
 }
@@ -153,18 +161,36 @@ FuseLayout fuse_layout(const eagle_dims* d, int B) {
 
 }  // namespace
 
-// Verification of every node of every tree: one decoder layer + LM head with a fused argmax.
+// Outputs of verification at temperature T > 0 (eagle_tree_verify_sample).
+struct SampleOut {
+  const int32_t* parent;
+  float temperature;
+  const float* gumbel;
+  float* child_logit;
+  float* rest_lse;
+  int32_t* rest_token;
+};
+
+// Verification of every node of every tree: one decoder layer + LM head with a fused
+// argmax, or (so != nullptr) with the sampling epilogue and its per-row merge.
 int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_ln, const void* w_lm, int B,
                 const int32_t* tree_off, int total_nodes, int max_nodes, const void* x_in, const void* embed,
                 const int32_t* tokens, const uint64_t* anc, int mw, const int32_t* pos, const int32_t* prefix_len,
                 int max_prefix, const void* k_cache, const void* v_cache, const eagle_cache_layout* cache,
                 void* k_tree, void* v_tree, float* h_out, int32_t* argmax, float* maxlogit, float* dbg_attn,
-                float* dbg_logits, void* ws, size_t ws_bytes, eagle_timer* timer, hipStream_t s) {
+                float* dbg_logits, void* ws, size_t ws_bytes, eagle_timer* timer, hipStream_t s,
+                const SampleOut* so = nullptr) {
   int rc = check_dims(d);
   if (rc) return rc;
   if (!lw || !w_lm || !tree_off || !anc || !pos || !prefix_len || !k_cache || !v_cache || !cache || !k_tree ||
-      !v_tree || !h_out || !argmax || !ws)
+      !v_tree || !h_out || !ws)
     return EAGLE_ERR_ARG;
+  if (!so && !argmax) return EAGLE_ERR_ARG;
+  if (so) {
+    if (!so->parent || !tokens || !so->gumbel || !so->child_logit || !so->rest_lse || !so->rest_token)
+      return EAGLE_ERR_ARG;
+    if (!(so->temperature > 0.f) || !std::isfinite(1.f / so->temperature)) return EAGLE_ERR_ARG;
+  }
   if (B < 1 || total_nodes < 1 || max_nodes < 1 || max_nodes > 64 * mw || mw < 1 || mw > 2 || max_prefix < 0)
     return EAGLE_ERR_ARG;
   if (!x_in && (!embed || !tokens)) return EAGLE_ERR_ARG;
@@ -177,7 +203,7 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
   if (((uintptr_t)ws) & 255) return EAGLE_ERR_ARG;
   if (cache->token_stride % 8 || cache->head_stride % 8 || cache->batch_stride % 8 || cache->capacity < 0)
     return EAGLE_ERR_ARG;
-  const VerifyLayout L = plan_verify(d, B, total_nodes, max_nodes, max_prefix);
+  const VerifyLayout L = plan_verify(d, B, total_nodes, max_nodes, max_prefix, so != nullptr);
   if (ws_bytes < L.total) return EAGLE_ERR_WORKSPACE;
   char* w = (char*)ws;
   const int dt = d->dtype;
@@ -206,6 +232,16 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     g.counters = counters;
   };
 
+  int32_t* gparent = so ? (int32_t*)(w + L.gparent) : nullptr;
+  int32_t* row_tree = so ? (int32_t*)(w + L.row_tree) : nullptr;
+  float4* samp_part = so ? (float4*)(w + L.samp_part) : nullptr;
+  if (so) {
+    // 0. each row's global parent row and sequence, for the sampling LM head
+    timer_begin(timer, ST_OTHER, s);
+    rc = launch_sample_prep(tree_off, so->parent, B, M, gparent, row_tree, s);
+    timer_end(timer, s);
+    if (rc) return rc;
+  }
   // 1. RMSNorm -> QKV projection -> rotary at pos -> q (workspace), k_tree, v_tree
   {
     GemmDesc g = base_desc(d);
@@ -386,25 +422,90 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     g.x.b = g.x.a;
     g.x.ka = H;
     g.x.eps = d->rms_eps;
-    g.epi.kind = EPI_ARGMAX;
-    g.epi.keys = keys;
-    g.epi.dbg_logits = dbg_logits;
-    g.epi.ld_logits = V;
-    g.epi.argmax_out = argmax;
-    g.epi.max_out = maxlogit;
-    g.epi.done = done;
+    if (so) {
+      g.epi.kind = EPI_SAMPLE;
+      g.epi.noise = so->gumbel;
+      g.epi.ld_noise = V;
+      g.epi.row_group = row_tree;
+      g.epi.inv_t = 1.f / so->temperature;
+      g.epi.gparent = gparent;
+      g.epi.ctoken = tokens;
+      g.epi.max_nodes = max_nodes;
+      g.epi.child_logit = so->child_logit;
+      g.epi.samp_part = samp_part;
+      g.epi.n_part = L.p_lm.n_tiles;
+    } else {
+      g.epi.kind = EPI_ARGMAX;
+      g.epi.keys = keys;
+      g.epi.dbg_logits = dbg_logits;
+      g.epi.ld_logits = V;
+      g.epi.argmax_out = argmax;
+      g.epi.max_out = maxlogit;
+      g.epi.done = done;
+    }
     common(g);
     timer_begin(timer, ST_LM_HEAD, s);
     rc = launch_gemm(g, L.p_lm, s);
     timer_end(timer, s);
     if (rc) return rc;
   }
+  if (so) {
+    // 7. per row: log-normaliser and best noisy token of the non-child tokens
+    timer_begin(timer, ST_OTHER, s);
+    rc = launch_sample_merge(samp_part, L.p_lm.n_tiles, M, so->rest_lse, so->rest_token, s);
+    timer_end(timer, s);
+    if (rc) return rc;
+  }
   return EAGLE_OK;
 }
 
-size_t verify_workspace(const eagle_dims* d, int B, int total_nodes, int max_nodes, int max_prefix) {
+size_t verify_workspace(const eagle_dims* d, int B, int total_nodes, int max_nodes, int max_prefix,
+                        bool sample = false) {
   if (check_dims(d) || B < 1 || total_nodes < 1 || max_nodes < 1) return 0;
-  return plan_verify(d, B, total_nodes, max_nodes, max_prefix).total;
+  return plan_verify(d, B, total_nodes, max_nodes, max_prefix, sample).total;
+}
+
+// Checks the arguments both acceptance rules share and fills the commit half of a.
+int commit_args(AcceptArgs& a, int batch, const int32_t* tree_off, int max_nodes, const int32_t* parent,
+                const int32_t* tokens, const void* k_tree, const void* v_tree, void* k_cache, void* v_cache,
+                const eagle_cache_layout* cache, int n_kv_heads, int head_dim, int dtype, int32_t* prefix_len,
+                const float* h_nodes, int hidden, float* next_feature, int max_accept, int32_t* accept_len,
+                int32_t* path, int32_t* out_tokens, int32_t* next_token, int32_t* dev_status) {
+  if (batch < 1 || max_nodes < 1 || !tree_off || !parent || !tokens || !k_tree || !v_tree || !k_cache || !v_cache ||
+      !cache || !prefix_len || !accept_len || !path || !out_tokens || !next_token)
+    return EAGLE_ERR_ARG;
+  if (max_accept < 0 || max_accept > 127) return EAGLE_ERR_ARG;
+  if (dtype != EAGLE_BF16 && dtype != EAGLE_F32) return EAGLE_ERR_UNSUPPORTED;
+  const int es = elem_size(dtype);
+  if (n_kv_heads < 1 || head_dim < 1 || (head_dim * es) % 16) return EAGLE_ERR_UNSUPPORTED;
+  if ((cache->token_stride * es) % 16 || (cache->head_stride * es) % 16 || (cache->batch_stride * es) % 16)
+    return EAGLE_ERR_ARG;
+  if (next_feature && (!h_nodes || hidden < 1 || hidden % 4)) return EAGLE_ERR_ARG;
+  a.tree_off = tree_off;
+  a.parent = parent;
+  a.tokens = tokens;
+  a.k_tree = k_tree;
+  a.v_tree = v_tree;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cb = cache->batch_stride;
+  a.ch = cache->head_stride;
+  a.ct = cache->token_stride;
+  a.capacity = cache->capacity;
+  a.hkv = n_kv_heads;
+  a.hd = head_dim;
+  a.elem = es;
+  a.prefix_len = prefix_len;
+  a.h_nodes = h_nodes;
+  a.hidden = hidden;
+  a.next_feature = next_feature;
+  a.max_accept = max_accept;
+  a.accept_len = accept_len;
+  a.path = path;
+  a.out_tokens = out_tokens;
+  a.next_token = next_token;
+  a.status = dev_status;
+  return EAGLE_OK;
 }
 
 }  // namespace eagle
@@ -458,47 +559,55 @@ int eagle_accept_commit(int32_t batch, const int32_t* tree_off, int32_t max_node
                         int32_t* prefix_len, const float* h_nodes, int32_t hidden, float* next_feature,
                         int32_t max_accept, int32_t* accept_len, int32_t* path, int32_t* out_tokens,
                         int32_t* next_token, int32_t* dev_status, void* stream) {
-  if (batch < 1 || max_nodes < 1 || !tree_off || !parent || !tokens || !argmax || !anc || !depth || !k_tree ||
-      !v_tree || !k_cache || !v_cache || !cache || !prefix_len || !accept_len || !path || !out_tokens || !next_token)
-    return EAGLE_ERR_ARG;
+  if (!argmax || !anc || !depth) return EAGLE_ERR_ARG;
   if (mask_words < 1 || mask_words > 2 || max_nodes > 64 * mask_words) return EAGLE_ERR_CAPACITY;
-  if (max_accept < 0 || max_accept > 127) return EAGLE_ERR_ARG;
-  if (dtype != EAGLE_BF16 && dtype != EAGLE_F32) return EAGLE_ERR_UNSUPPORTED;
-  const int es = elem_size(dtype);
-  if (n_kv_heads < 1 || head_dim < 1 || (head_dim * es) % 16) return EAGLE_ERR_UNSUPPORTED;
-  if ((cache->token_stride * es) % 16 || (cache->head_stride * es) % 16 || (cache->batch_stride * es) % 16)
-    return EAGLE_ERR_ARG;
-  if (next_feature && (!h_nodes || hidden < 1 || hidden % 4)) return EAGLE_ERR_ARG;
   AcceptArgs a{};
-  a.tree_off = tree_off;
-  a.parent = parent;
-  a.tokens = tokens;
+  const int rc = commit_args(a, batch, tree_off, max_nodes, parent, tokens, k_tree, v_tree, k_cache, v_cache, cache,
+                             n_kv_heads, head_dim, dtype, prefix_len, h_nodes, hidden, next_feature, max_accept,
+                             accept_len, path, out_tokens, next_token, dev_status);
+  if (rc) return rc;
   a.argmax = argmax;
   a.anc = anc;
   a.mw = mask_words;
   a.depth = depth;
-  a.k_tree = k_tree;
-  a.v_tree = v_tree;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.cb = cache->batch_stride;
-  a.ch = cache->head_stride;
-  a.ct = cache->token_stride;
-  a.capacity = cache->capacity;
-  a.hkv = n_kv_heads;
-  a.hd = head_dim;
-  a.elem = es;
-  a.prefix_len = prefix_len;
-  a.h_nodes = h_nodes;
-  a.hidden = hidden;
-  a.next_feature = next_feature;
-  a.max_accept = max_accept;
-  a.accept_len = accept_len;
-  a.path = path;
-  a.out_tokens = out_tokens;
-  a.next_token = next_token;
-  a.status = dev_status;
   return launch_accept_commit(a, batch, (hipStream_t)stream);
+}
+
+int eagle_accept_commit_sample(int32_t batch, const int32_t* tree_off, int32_t max_nodes, const int32_t* parent,
+                               const int32_t* tokens, const float* child_logit, const float* rest_lse,
+                               const int32_t* rest_token, const float* u, const void* k_tree, const void* v_tree,
+                               void* k_cache, void* v_cache, const eagle_cache_layout* cache, int32_t n_kv_heads,
+                               int32_t head_dim, int32_t dtype, int32_t* prefix_len, const float* h_nodes,
+                               int32_t hidden, float* next_feature, int32_t max_accept, int32_t* accept_len,
+                               int32_t* path, int32_t* out_tokens, int32_t* next_token, int32_t* dev_status,
+                               void* stream) {
+  if (!child_logit || !rest_lse || !rest_token || !u) return EAGLE_ERR_ARG;
+  if (max_nodes > 128) return EAGLE_ERR_CAPACITY;
+  AcceptArgs a{};
+  const int rc = commit_args(a, batch, tree_off, max_nodes, parent, tokens, k_tree, v_tree, k_cache, v_cache, cache,
+                             n_kv_heads, head_dim, dtype, prefix_len, h_nodes, hidden, next_feature, max_accept,
+                             accept_len, path, out_tokens, next_token, dev_status);
+  if (rc) return rc;
+  a.child_logit = child_logit;
+  a.rest_lse = rest_lse;
+  a.rest_token = rest_token;
+  a.u = u;
+  return launch_accept_sample(a, batch, (hipStream_t)stream);
+}
+
+int eagle_tree_verify_sample(const eagle_dims* dims, const eagle_layer_w* layer, const void* final_ln,
+                             const void* w_lm, int32_t batch, const int32_t* tree_off, int32_t total_nodes,
+                             int32_t max_nodes, const void* x_in, const void* embed, const int32_t* tokens,
+                             const int32_t* parent, const uint64_t* anc, int32_t mask_words, const int32_t* pos,
+                             const int32_t* prefix_len, int32_t max_prefix, const void* k_cache,
+                             const void* v_cache, const eagle_cache_layout* cache, float temperature,
+                             const float* gumbel, void* k_tree, void* v_tree, float* h_out, float* child_logit,
+                             float* rest_lse, int32_t* rest_token, void* workspace, size_t ws_bytes,
+                             eagle_timer* timer, void* stream) {
+  SampleOut so{parent, temperature, gumbel, child_logit, rest_lse, rest_token};
+  return verify_impl(dims, layer, final_ln, w_lm, batch, tree_off, total_nodes, max_nodes, x_in, embed, tokens, anc,
+                     mask_words, pos, prefix_len, max_prefix, k_cache, v_cache, cache, k_tree, v_tree, h_out,
+                     nullptr, nullptr, nullptr, nullptr, workspace, ws_bytes, timer, (hipStream_t)stream, &so);
 }
 
 size_t eagle_workspace_size(int32_t which, const eagle_dims* dims, int32_t batch, int32_t total_nodes,
@@ -506,6 +615,7 @@ size_t eagle_workspace_size(int32_t which, const eagle_dims* dims, int32_t batch
   if (which == 0) return verify_workspace(dims, batch, total_nodes, max_nodes, max_prefix);
   if (which == 1) return draft_workspace(dims, params, batch, max_prefix);
   if (which == 2) return fuse_layout(dims, batch).total;
+  if (which == 3) return verify_workspace(dims, batch, total_nodes, max_nodes, max_prefix, true);
   return 0;
 }
 

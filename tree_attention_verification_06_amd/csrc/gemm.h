@@ -33,7 +33,7 @@ struct XSrc {
   int np;
 };
 
-enum EpiKind { EPI_STORE_F32 = 0, EPI_QKV = 1, EPI_RESID = 2, EPI_SILU = 3, EPI_ARGMAX = 4, EPI_TOPK = 5 };
+enum EpiKind { EPI_STORE_F32 = 0, EPI_QKV = 1, EPI_RESID = 2, EPI_SILU = 3, EPI_ARGMAX = 4, EPI_TOPK = 5, EPI_SAMPLE = 6 };
 
 struct Epi {
   int kind;
@@ -75,6 +75,24 @@ struct Epi {
   int32_t* topk_idx; // [n_tiles][m][topk]
   float* lse_part;   // [n_tiles][m][2]
   int topk;
+  // EPI_SAMPLE: tempered logits v = inv_t * logit.  For every row c with a parent row
+  // gparent[c] (-1: none) in the tile, the tile's value at (gparent[c], ctoken[c]), if
+  // that column is in the tile, goes to child_logit[c] and is then left out; over the
+  // remaining columns each (row, tile) gets (max v, sum exp(v - max)) and the largest
+  // key of v + noise, written as one float4 (max, sum, key low word, key high word) to
+  // samp_part[row * n_part + tile].  A child row lies at most max_nodes - 1 rows after
+  // its parent.  Row m uses the noise row row_group[m] (< 0: row 0): noise of column c
+  // is noise[row_group[m] * ld_noise + c].
+  const float* noise;
+  int64_t ld_noise;
+  const int32_t* row_group;
+  float inv_t;
+  const int32_t* gparent;
+  const int32_t* ctoken;
+  int max_nodes;
+  float* child_logit;
+  float4* samp_part;
+  int n_part;
 };
 
 struct GemmDesc {

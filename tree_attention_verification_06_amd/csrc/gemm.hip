@@ -257,11 +257,102 @@ __device__ __forceinline__ void epi_topk(const GemmDesc& d, const float* tile, i
   }
 }
 
+// Sampling epilogue (EPI_SAMPLE).  First the tempered logits of the child tokens that
+// fall in this tile are read out and masked (sibling tokens are distinct, so every
+// thread touches its own tile entries); then thread (token t = tid % mt, part = tid / mt)
+// summarises its columns part, part + P, ... of the remaining logits as (max,
+// sum exp(v - max)) and the largest key of v + noise.  The noise reads go out in
+// batches of NQ before any is used; the per-part results are merged through LDS.
+__device__ __forceinline__ void epi_sample(const GemmDesc& d, float* tile, int ts, int tc, int col0, int m0, int mv,
+                                           int mt, const float* scale) {
+  constexpr int NQ = 32;
+  const Epi& e = d.epi;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  const int ncol = min(tc, d.n - col0);
+  // children of rows m0 .. m0 + mv - 1 are among rows m0 + 1 .. m0 + mv + max_nodes - 2
+  const int c_end = min(d.m, m0 + mv + e.max_nodes - 1);
+  for (int c = m0 + 1 + tid; c < c_end; c += nth) {
+    const int gp = e.gparent[c] - m0;
+    const int tk = e.ctoken[c] - col0;
+    if (gp >= 0 && gp < mv && tk >= 0 && tk < ncol) {
+      float* at = tile + tk * ts + gp;
+      e.child_logit[c] = (scale[gp] * e.inv_t) * *at;
+      *at = -INFINITY;
+    }
+  }
+  __syncthreads();
+  const int tile_i = col0 / tc;
+  const int P = nth / mt;  // parts per token; threads past P * mt sit out
+  const int t = tid % mt, part = tid / mt;
+  const bool active = part < P && t < mv;
+  float mx = -INFINITY, se = 0.f;
+  unsigned long long best = 0ull;
+  if (active) {
+    const float sc = scale[t] * e.inv_t;
+    const int grp = e.row_group[m0 + t];
+    const float* nz = e.noise + (int64_t)(grp < 0 ? 0 : grp) * e.ld_noise + col0;
+    int r0 = part;
+    for (; r0 + 3 * P < ncol; r0 += 4 * P) {
+      float v4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v4[u] = tile[(r0 + u * P) * ts + t];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) mx = fmaxf(mx, sc * v4[u]);
+    }
+    for (; r0 < ncol; r0 += P) mx = fmaxf(mx, sc * tile[r0 * ts + t]);
+    const float mref = mx == -INFINITY ? 0.f : mx;  // a part whose columns are all masked adds 0
+    for (int base = part; base < ncol; base += NQ * P) {
+      float g[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) g[q] = nz[min(base + q * P, ncol - 1)];  // in-range stand-in past the end
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int r = base + q * P;
+        const bool in = r < ncol;
+        const int rc = in ? r : ncol - 1;
+        const float v = sc * tile[rc * ts + t];
+        se += in ? __expf(v - mref) : 0.f;
+        const unsigned long long key = in ? argmax_key(v + g[q], (uint32_t)(col0 + r)) : 0ull;
+        best = key > best ? key : best;
+      }
+    }
+  }
+  __syncthreads();  // every read of the tile is done: its LDS is reused below
+  float* s_mx = tile;                          // [P][mt] each
+  float* s_se = s_mx + P * mt;
+  uint32_t* s_klo = (uint32_t*)(s_se + P * mt);
+  uint32_t* s_khi = s_klo + P * mt;
+  if (part < P) {
+    s_mx[part * mt + t] = mx;
+    s_se[part * mt + t] = se;
+    s_klo[part * mt + t] = (uint32_t)best;
+    s_khi[part * mt + t] = (uint32_t)(best >> 32);
+  }
+  __syncthreads();
+  if (part == 0 && t < mv) {
+    float M = -INFINITY;
+    unsigned long long K = 0ull;
+    for (int p2 = 0; p2 < P; ++p2) {
+      M = fmaxf(M, s_mx[p2 * mt + t]);
+      const unsigned long long k2 =
+          ((unsigned long long)s_khi[p2 * mt + t] << 32) | (unsigned long long)s_klo[p2 * mt + t];
+      K = k2 > K ? k2 : K;
+    }
+    float S = 0.f;
+    for (int p2 = 0; p2 < P; ++p2) {
+      const float m2 = s_mx[p2 * mt + t];
+      if (m2 > -INFINITY) S += s_se[p2 * mt + t] * __expf(m2 - M);
+    }
+    e.samp_part[(int64_t)(m0 + t) * e.n_part + tile_i] =
+        make_float4(M, S, __uint_as_float((uint32_t)K), __uint_as_float((uint32_t)(K >> 32)));
+  }
+}
+
 // Fused epilogue over a finished fp32 tile in LDS: tile[r * ts + t] is output column
 // col0 + r (for dual tiles: gate columns r < tc, up columns r >= tc) of token m0 + t,
 // before the per-row norm scale scale[t].
 // CPLC: output columns per lane of the store epilogue, ceil(tc / 64) at most.
-template <int CPLC>
+template <int CPLC, bool WITH_SAMPLE>
 __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int tc, int col0, int m0, int mv,
                              int mt, const float* scale, float* red_scratch, int* s_flag, int n_epi) {
   const Epi& e = d.epi;
@@ -396,6 +487,9 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
       }
       break;
     }
+    case EPI_SAMPLE:
+      if constexpr (WITH_SAMPLE) epi_sample(d, const_cast<float*>(tile), ts, tc, col0, m0, mv, mt, scale);
+      break;
     case EPI_TOPK: {
       if (e.topk <= 12)
         epi_topk<12>(d, tile, ts, tc, col0, m0, mv, mt, scale);
@@ -499,7 +593,9 @@ __device__ __forceinline__ void sum_partials(const float* p0, float* tile, int h
 // tiles (MT 128 / 256) use shorter K chunks so that the X chunks and the output tile both
 // fit the 160 KB of LDS; each weight byte is then streamed once per MT tokens instead of
 // once per 64.
-template <int NW, int RB, int PD, bool DUAL, int MT, int KC, int XB, int EH>
+// SAMPLE: the instance for the sampling epilogue only (the other epilogues' code and its
+// registers stay out of it, and it stays out of theirs).
+template <int NW, int RB, int PD, bool DUAL, int MT, int KC, int XB, int EH, bool SAMPLE>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid_real) {
   constexpr int NT = NW * RB * 16;        // weight rows per tile (both blocks when DUAL)
   constexpr int TC = DUAL ? NT / 2 : NT;  // output columns per tile
@@ -841,8 +937,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
       }
     }
     __syncthreads();
-    run_epilogue<(TCH + 63) / 64>(d, tile, TS, TCH, col0 + h * TCH, m0, mv, MT, s_scale, (float*)s_red, &s_flag,
-                                  n_epi);
+    if constexpr (SAMPLE)
+      epi_sample(d, tile, TS, TCH, col0 + h * TCH, m0, mv, MT, s_scale);
+    else
+      run_epilogue<(TCH + 63) / 64, false>(d, tile, TS, TCH, col0 + h * TCH, m0, mv, MT, s_scale, (float*)s_red,
+                                           &s_flag, n_epi);
   }
 }
 
@@ -908,7 +1007,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d, int grid_real
   __syncthreads();
   const int tc = d.dual ? F32_NT / 2 : F32_NT;
   const int c0 = d.dual ? col0 / 2 : col0;
-  run_epilogue<(F32_NT + 63) / 64>(d, tile, TS, tc, c0, m0, mv, F32_MT, s_scale, (float*)s_red, &s_flag, grid_real);
+  run_epilogue<(F32_NT + 63) / 64, true>(d, tile, TS, tc, c0, m0, mv, F32_MT, s_scale, (float*)s_red, &s_flag,
+                                         grid_real);
 }
 
 struct CfgInfo {
@@ -926,8 +1026,15 @@ constexpr CfgInfo kCfgs[kNumCfgs] = {{8, 4, 4, 64, 512, 1},   {8, 2, 4, 64, 512,
 template <int NW, int RB, int PD, bool DUAL, int MT, int KC, int XB, int EH = 1>
 void launch_cfg(const GemmDesc& d, int grid, hipStream_t s) {
   const int padded = (grid + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((gemm_bf16_kernel<NW, RB, PD, DUAL, MT, KC, XB, EH>), dim3(padded), dim3(NW * 64), 0, s, d,
-                     grid);
+  if constexpr (!DUAL) {
+    if (d.epi.kind == EPI_SAMPLE) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<NW, RB, PD, false, MT, KC, XB, EH, true>), dim3(padded), dim3(NW * 64), 0,
+                         s, d, grid);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<NW, RB, PD, DUAL, MT, KC, XB, EH, false>), dim3(padded), dim3(NW * 64), 0, s,
+                     d, grid);
 }
 
 }  // namespace
@@ -1028,6 +1135,7 @@ int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s) {
   if (p.cfg != 100 && (d.x.a.dtype != EAGLE_BF16 || d.x.b.dtype != EAGLE_BF16)) return EAGLE_ERR_UNSUPPORTED;
   if (p.cfg == 100 && d.epi.kind == EPI_TOPK) return EAGLE_ERR_UNSUPPORTED;  // its LDS tile is too small
   if (p.cfg == 100 && d.w_layout) return EAGLE_ERR_UNSUPPORTED;              // fragment blocks are bf16
+  if (d.dual && d.epi.kind == EPI_SAMPLE) return EAGLE_ERR_UNSUPPORTED;
   const int grid = p.w_tiles * p.m_tiles * p.splits;
   if (grid <= 0) return EAGLE_OK;
   if (p.cfg == 100) {

@@ -30,10 +30,22 @@ struct AcceptArgs {
   int32_t* out_tokens;
   int32_t* next_token;
   int32_t* status;
+  // acceptance at temperature T > 0 (argmax, anc, mw and depth unused): per node the
+  // tempered logit of its token under its parent, the log-normaliser and best noisy
+  // token of its non-child tokens, and its acceptance uniform
+  const float* child_logit;
+  const float* rest_lse;
+  const int32_t* rest_token;
+  const float* u;
 };
 
 int launch_tree_build(int batch, const int32_t* tree_off, const int32_t* parent, const int32_t* prefix_len, int mw,
                       uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* status, hipStream_t s);
 int launch_accept_commit(const AcceptArgs& a, int batch, hipStream_t s);
+int launch_sample_prep(const int32_t* tree_off, const int32_t* parent, int batch, int total, int32_t* gparent,
+                       int32_t* row_tree, hipStream_t s);
+int launch_sample_merge(const float4* part, int n_part, int rows, float* rest_lse, int32_t* rest_token,
+                        hipStream_t s);
+int launch_accept_sample(const AcceptArgs& a, int batch, hipStream_t s);
 
 }  // namespace eagle

@@ -1,4 +1,4 @@
-// Tree encode and greedy accept + KV commit (gfx950).
+// Tree encode, acceptance (greedy, and sampling at T > 0) + KV commit (gfx950).
 //
 // Both are integer work on at most 128 nodes per tree, so each tree gets one
 // workgroup and each node one lane: ancestor words are built by walking the parent
@@ -51,6 +51,64 @@ __global__ __launch_bounds__(128) void tree_build_kernel(const int32_t* tree_off
     for (int w = 0; w < mw; ++w) anc[(int64_t)(off + i) * mw + w] = words[w];
     depth[off + i] = d;
     pos[off + i] = P + d;
+  }
+}
+
+// Outputs and commit of sequence b, shared by both acceptance rules: path and
+// out_tokens for the accepted path s_path[0..L] (LDS) and the bonus token, then the K/V
+// rows of the path into cache slots P..P+L (16-byte copies; rows are hd * elem bytes,
+// a multiple of 16), the leaf's feature into next_feature, and prefix_len[b] = P + L + 1.
+// Every thread of the workgroup calls it.
+__device__ void commit_path(const AcceptArgs& a, int b, int off, const int* s_path, const int* s_tok, int L, int leaf,
+                            int bonus, int P) {
+  const int tid = threadIdx.x;
+  const int stride = a.max_accept + 1;
+  for (int d = tid; d < stride; d += blockDim.x) {
+    a.path[(int64_t)b * stride + d] = d <= L ? s_path[d] : -1;
+    int t = -1;
+    if (d < L) t = s_tok[s_path[d + 1]];
+    else if (d == L) t = bonus;
+    a.out_tokens[(int64_t)b * stride + d] = t;
+  }
+  if (tid == 0) {
+    a.accept_len[b] = L;
+    a.next_token[b] = bonus;
+  }
+  const int row_bytes = a.hd * a.elem;
+  const int chunks = row_bytes / 16;
+  const int per_node = a.hkv * chunks;
+  const int total = (L + 1) * per_node;
+  for (int i = tid; i < 2 * total; i += blockDim.x) {
+    const int which = i / total;  // 0: K, 1: V
+    const int r = i % total;
+    const int d = r / per_node;
+    const int h = (r % per_node) / chunks;
+    const int ch = r % chunks;
+    const char* src = (const char*)(which ? a.v_tree : a.k_tree) +
+                      ((int64_t)(off + s_path[d]) * a.hkv + h) * row_bytes + ch * 16;
+    char* dst = (char*)(which ? a.v_cache : a.k_cache) +
+                ((int64_t)b * a.cb + (int64_t)h * a.ch + (int64_t)(P + d) * a.ct) * a.elem + ch * 16;
+    *(uint4*)dst = *(const uint4*)src;
+  }
+  if (a.next_feature) {
+    for (int i = tid * 4; i < a.hidden; i += blockDim.x * 4)
+      *(float4*)(a.next_feature + (int64_t)b * a.hidden + i) =
+          *(const float4*)(a.h_nodes + (int64_t)(off + leaf) * a.hidden + i);
+  }
+  if (tid == 0) a.prefix_len[b] = P + L + 1;
+}
+
+// A sequence that cannot be accepted: accept_len and next_token -1, path and
+// out_tokens all -1, nothing committed.
+__device__ void reject_sequence(const AcceptArgs& a, int b) {
+  const int stride = a.max_accept + 1;
+  if (threadIdx.x == 0) {
+    a.accept_len[b] = -1;
+    a.next_token[b] = -1;
+  }
+  for (int d = threadIdx.x; d < stride; d += blockDim.x) {
+    a.path[(int64_t)b * stride + d] = -1;
+    a.out_tokens[(int64_t)b * stride + d] = -1;
   }
 }
 
@@ -125,16 +183,8 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptArgs a) {
   }
   __syncthreads();
   const int L = s_L, leaf = s_leaf, P = s_P;
-  const int stride = a.max_accept + 1;
   if (!s_ok) {
-    if (tid == 0) {
-      a.accept_len[b] = -1;
-      a.next_token[b] = -1;
-    }
-    for (int d = tid; d < stride; d += blockDim.x) {
-      a.path[(int64_t)b * stride + d] = -1;
-      a.out_tokens[(int64_t)b * stride + d] = -1;
-    }
+    reject_sequence(a, b);
     return;
   }
   // path: ancestors of the leaf have increasing index and depth, so node j on the path
@@ -144,42 +194,190 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptArgs a) {
     if (((s_anc[leaf][j >> 6] >> (j & 63)) & 1ull) && dj >= 0 && dj <= L) s_path[dj] = j;
   }
   __syncthreads();
-  const int bonus = s_am[leaf];
-  for (int d = tid; d < stride; d += blockDim.x) {
-    a.path[(int64_t)b * stride + d] = d <= L ? s_path[d] : -1;
-    int t = -1;
-    if (d < L) t = s_tok[s_path[d + 1]];
-    else if (d == L) t = bonus;
-    a.out_tokens[(int64_t)b * stride + d] = t;
+  commit_path(a, b, off, s_path, s_tok, L, leaf, s_am[leaf], P);
+}
+
+
+// ---- acceptance at temperature T > 0 ----------------------------------------------
+
+// Global parent row of every row (-1: a root, a padding row past tree_off[B] or a
+// malformed parent) and the sequence each row belongs to (-1: padding).  Workgroup b
+// < batch handles tree b, workgroup `batch` the padding rows.
+__global__ __launch_bounds__(128) void sample_prep_kernel(const int32_t* tree_off, const int32_t* parent, int batch,
+                                                          int total, int32_t* gparent, int32_t* row_tree) {
+  const int b = blockIdx.x;
+  if (b == batch) {
+    for (int r = max(tree_off[batch], 0) + threadIdx.x; r < total; r += blockDim.x) {
+      gparent[r] = -1;
+      row_tree[r] = -1;
+    }
+    return;
+  }
+  const int off = tree_off[b];
+  const int N = tree_off[b + 1] - off;
+  for (int i = threadIdx.x; i < N; i += blockDim.x) {
+    const int r = off + i;
+    if (r < 0 || r >= total) continue;
+    const int p = parent[r];
+    gparent[r] = (i > 0 && p >= 0 && p < i) ? off + p : -1;
+    row_tree[r] = b;
+  }
+}
+
+__device__ __forceinline__ void lse_combine(float& M, float& S, float m2, float s2) {
+  const float Mn = fmaxf(M, m2);
+  if (Mn == -INFINITY) return;  // both empty
+  S = (M == -INFINITY ? 0.f : S * __expf(M - Mn)) + (m2 == -INFINITY ? 0.f : s2 * __expf(m2 - Mn));
+  M = Mn;
+}
+
+// Row m of the LM head's per-tile summaries -> rest_lse[m] = log sum exp over the row's
+// non-child tokens and rest_token[m] = the token of the largest noisy key.  One
+// workgroup per row; its n_part entries are contiguous and read in one round.
+__global__ __launch_bounds__(256) void sample_merge_kernel(const float4* part, int n_part, float* rest_lse,
+                                                           int32_t* rest_token) {
+  constexpr int R = 4;
+  __shared__ float s_m[4], s_s[4];
+  __shared__ unsigned long long s_k[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const float4* p = part + (int64_t)m * n_part;
+  float M = -INFINITY, S = 0.f;
+  unsigned long long K = 0ull;
+  for (int i0 = tid; i0 < n_part; i0 += R * 256) {
+    float4 q[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) q[u] = p[min(i0 + u * 256, n_part - 1)];  // in-range stand-in past the end
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      if (i0 + u * 256 >= n_part) continue;
+      lse_combine(M, S, q[u].x, q[u].y);
+      const unsigned long long k2 =
+          ((unsigned long long)__float_as_uint(q[u].w) << 32) | (unsigned long long)__float_as_uint(q[u].z);
+      K = k2 > K ? k2 : K;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(M, o, 64), s2 = __shfl_xor(S, o, 64);
+    const unsigned long long k2 = __shfl_xor(K, o, 64);
+    lse_combine(M, S, m2, s2);
+    K = k2 > K ? k2 : K;
+  }
+  const int w = tid >> 6;
+  if ((tid & 63) == 0) {
+    s_m[w] = M;
+    s_s[w] = S;
+    s_k[w] = K;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int j = 1; j < 4; ++j) {
+      lse_combine(M, S, s_m[j], s_s[j]);
+      K = s_k[j] > K ? s_k[j] : K;
+    }
+    rest_lse[m] = M == -INFINITY ? -INFINITY : M + __logf(S);
+    rest_token[m] = K ? (int32_t)(0xffffffffu - (uint32_t)(K & 0xffffffffull)) : -1;
+  }
+}
+
+// One workgroup (256 threads) per sequence.  The walk is sequential by nature (a child
+// is tried only once its elder siblings are rejected), so wave 0 runs it over LDS copies
+// of the tree: at each visited node two ballots over the parent array give its children
+// in index order, a wave reduction combines rest_lse with the children's logits into the
+// node's log-normaliser, and the children are then tried in turn.  The other waves only
+// help with the loads, the checks and the commit.
+__global__ __launch_bounds__(256) void accept_sample_kernel(AcceptArgs a) {
+  constexpr int NMAX = 128;
+  __shared__ int s_tok[NMAX], s_par[NMAX], s_rt[NMAX];
+  __shared__ float s_z[NMAX], s_rl[NMAX], s_u[NMAX];
+  __shared__ int s_path[NMAX + 1];
+  __shared__ int s_L, s_leaf, s_bonus, s_P, s_bad;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int off = a.tree_off[b];
+  const int N = a.tree_off[b + 1] - off;
+  if (N < 1 || N > NMAX) {
+    if (tid == 0) set_status(a.status, EAGLE_ERR_CAPACITY);
+    reject_sequence(a, b);
+    return;
+  }
+  for (int i = tid; i < N; i += blockDim.x) {
+    s_tok[i] = a.tokens[off + i];
+    s_par[i] = a.parent[off + i];
+    s_z[i] = a.child_logit[off + i];
+    s_rl[i] = a.rest_lse[off + i];
+    s_rt[i] = a.rest_token[off + i];
+    s_u[i] = a.u[off + i];
   }
   if (tid == 0) {
-    a.accept_len[b] = L;
-    a.next_token[b] = bonus;
+    s_P = a.prefix_len[b];
+    s_bad = 0;
   }
-  // commit K/V rows of path[0..L] into slots P..P+L (16-byte copies; rows are
-  // hd * elem bytes, a multiple of 16)
-  const int row_bytes = a.hd * a.elem;
-  const int chunks = row_bytes / 16;
-  const int per_node = a.hkv * chunks;
-  const int total = (L + 1) * per_node;
-  for (int i = tid; i < 2 * total; i += blockDim.x) {
-    const int which = i / total;  // 0: K, 1: V
-    const int r = i % total;
-    const int d = r / per_node;
-    const int h = (r % per_node) / chunks;
-    const int ch = r % chunks;
-    const char* src = (const char*)(which ? a.v_tree : a.k_tree) +
-                      ((int64_t)(off + s_path[d]) * a.hkv + h) * row_bytes + ch * 16;
-    char* dst = (char*)(which ? a.v_cache : a.k_cache) +
-                ((int64_t)b * a.cb + (int64_t)h * a.ch + (int64_t)(P + d) * a.ct) * a.elem + ch * 16;
-    *(uint4*)dst = *(const uint4*)src;
+  __syncthreads();
+  // a well-formed tree (parent[0] = -1, parent[i] in [0, i)) with distinct sibling tokens
+  for (int i = tid; i < N; i += blockDim.x) {
+    const int p = s_par[i];
+    bool bad = (i == 0) ? p != -1 : (p < 0 || p >= i);
+    if (!bad && i > 0)
+      for (int j = p + 1; j < i; ++j) bad |= s_par[j] == p && s_tok[j] == s_tok[i];
+    if (bad) atomicCAS(&s_bad, 0, 1);
   }
-  if (a.next_feature) {
-    for (int i = tid * 4; i < a.hidden; i += blockDim.x * 4)
-      *(float4*)(a.next_feature + (int64_t)b * a.hidden + i) =
-          *(const float4*)(a.h_nodes + (int64_t)(off + leaf) * a.hidden + i);
+  __syncthreads();
+  if (tid < 64 && !s_bad) {
+    const int lane = tid;
+    int node = 0, L = 0, bonus = -1;
+    while (true) {
+      if (lane == 0) s_path[L] = node;
+      const int c0 = lane, c1 = lane + 64;
+      const bool k0 = c0 > node && c0 < N && s_par[c0] == node;
+      const bool k1 = c1 > node && c1 < N && s_par[c1] == node;
+      const unsigned long long b0 = __ballot(k0), b1 = __ballot(k1);
+      const float z0 = k0 ? s_z[c0] : -INFINITY, z1 = k1 ? s_z[c1] : -INFINITY;
+      const float rl = s_rl[node];
+      const float mz = fmaxf(rl, wave_max(fmaxf(z0, z1)));
+      const float sz = wave_sum((k0 ? __expf(z0 - mz) : 0.f) + (k1 ? __expf(z1 - mz) : 0.f));
+      const float lse = mz + __logf((rl == -INFINITY ? 0.f : __expf(rl - mz)) + sz);
+      float r = 1.f;  // mass left after the rejected children
+      int next = -1;
+      for (int w = 0; w < 2 && next < 0; ++w) {
+        unsigned long long bits = w ? b1 : b0;
+        while (bits) {
+          const int c = w * 64 + __builtin_ctzll(bits);
+          bits &= bits - 1;
+          const float px = __expf(s_z[c] - lse);
+          if (s_u[c] * r < px) {
+            next = c;
+            break;
+          }
+          r -= px;
+        }
+      }
+      if (next < 0) {
+        bonus = s_rt[node];
+        break;
+      }
+      node = next;
+      ++L;
+    }
+    if (lane == 0) {
+      s_L = L;
+      s_leaf = node;
+      s_bonus = bonus;
+    }
   }
-  if (tid == 0) a.prefix_len[b] = P + L + 1;
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0) set_status(a.status, EAGLE_ERR_TREE);
+    reject_sequence(a, b);
+    return;
+  }
+  const int L = s_L, P = s_P;
+  if (L > a.max_accept || P < 0 || (int64_t)P + L + 1 > a.capacity) {
+    if (tid == 0) set_status(a.status, EAGLE_ERR_CAPACITY);
+    reject_sequence(a, b);
+    return;
+  }
+  commit_path(a, b, off, s_path, s_tok, L, s_leaf, s_bonus, P);
 }
 
 }  // namespace
@@ -193,6 +391,24 @@ int launch_tree_build(int batch, const int32_t* tree_off, const int32_t* parent,
 
 int launch_accept_commit(const AcceptArgs& a, int batch, hipStream_t s) {
   hipLaunchKernelGGL(accept_commit_kernel, dim3(batch), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
+}
+
+int launch_sample_prep(const int32_t* tree_off, const int32_t* parent, int batch, int total, int32_t* gparent,
+                       int32_t* row_tree, hipStream_t s) {
+  hipLaunchKernelGGL(sample_prep_kernel, dim3(batch + 1), dim3(128), 0, s, tree_off, parent, batch, total, gparent,
+                     row_tree);
+  return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
+}
+
+int launch_sample_merge(const float4* part, int n_part, int rows, float* rest_lse, int32_t* rest_token,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(sample_merge_kernel, dim3(rows), dim3(256), 0, s, part, n_part, rest_lse, rest_token);
+  return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
+}
+
+int launch_accept_sample(const AcceptArgs& a, int batch, hipStream_t s) {
+  hipLaunchKernelGGL(accept_sample_kernel, dim3(batch), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
 }
 

@@ -30,10 +30,11 @@ def with_packed_weights(weights, *, lm_head=True, layer=True):
 
 class TreeVerifier:
     """lm_layout: 0 if weights["w_lm"] is row-major [vocab][hidden], 1 if fragment-blocked;
-    weight_layout: the same for the layer matrices."""
+    weight_layout: the same for the layer matrices.  sample=True adds the buffers of
+    verification and acceptance at temperature T > 0 (verify_sample, accept_sample)."""
 
     def __init__(self, dims, weights, k_cache, v_cache, *, batch, max_total_nodes, max_nodes, max_prefix,
-                 max_accept=None, device="cuda", lm_layout=0, weight_layout=0):
+                 max_accept=None, device="cuda", lm_layout=0, weight_layout=0, sample=False):
         self.dims = dims
         self.dstruct = A.dims_struct(dims, lm_layout)
         self.lstruct = A.layer_struct(weights, weight_layout)
@@ -65,6 +66,12 @@ class TreeVerifier:
         self.next_feature = z(batch, H, dtype=torch.float32)
         self.status = z(1)
         ws = A.eagle_workspace_size(0, dims, batch, M, max_nodes, max_prefix)
+        if sample:
+            ws3 = A.eagle_workspace_size(3, dims, batch, M, max_nodes, max_prefix)
+            ws = max(ws, ws3) if ws and ws3 else 0
+            self.child_logit = z(M, dtype=torch.float32)
+            self.rest_lse = z(M, dtype=torch.float32)
+            self.rest_token = z(M)
         if ws == 0:
             raise A.EagleError(A.EAGLE_ERR_UNSUPPORTED, "eagle_workspace_size")
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
@@ -97,6 +104,33 @@ class TreeVerifier:
         self.encode(tree_off, parent, prefix_len, total_nodes)
         self.verify(tree_off, tokens, prefix_len, total_nodes, x=x, timer=timer)
         self.accept(tree_off, parent, tokens, prefix_len)
+
+    def verify_sample(self, tree_off, tokens, parent, prefix_len, total_nodes, temperature, gumbel, x=None,
+                      timer=None):
+        """gumbel: [batch][vocab] f32 noise, one row per tree."""
+        w = self.w
+        A.eagle_tree_verify_sample(self.dstruct, self.lstruct, w.get("final_ln"), w["w_lm"], tree_off, x,
+                                   w.get("embed") if x is None else None, tokens, parent, self.anc, self.mw,
+                                   self.pos, prefix_len, self.k_cache, self.v_cache, temperature, gumbel,
+                                   self.k_tree, self.v_tree, self.h, self.child_logit, self.rest_lse,
+                                   self.rest_token, self.workspace, total_nodes=total_nodes,
+                                   max_nodes=self.max_nodes, max_prefix=self.max_prefix, timer=timer)
+
+    def accept_sample(self, tree_off, parent, tokens, u, prefix_len):
+        """u: [total_nodes] f32 acceptance uniforms."""
+        d = self.dims
+        A.eagle_accept_commit_sample(tree_off, parent, tokens, self.child_logit, self.rest_lse, self.rest_token, u,
+                                     self.k_tree, self.v_tree, self.k_cache, self.v_cache, prefix_len, self.h,
+                                     self.next_feature, self.accept_len, self.path, self.out_tokens,
+                                     self.next_token, self.status, max_nodes=self.max_nodes,
+                                     max_accept=self.max_accept, n_kv_heads=d.n_kv_heads, head_dim=d.head_dim,
+                                     dtype=A.EAGLE_BF16 if d.dtype == "bf16" else A.EAGLE_F32, hidden=d.hidden)
+
+    def step_sample(self, tree_off, parent, tokens, prefix_len, total_nodes, temperature, gumbel, u, x=None,
+                    timer=None):
+        self.encode(tree_off, parent, prefix_len, total_nodes)
+        self.verify_sample(tree_off, tokens, parent, prefix_len, total_nodes, temperature, gumbel, x=x, timer=timer)
+        self.accept_sample(tree_off, parent, tokens, u, prefix_len)
 
 
 class TreeDrafter:
@@ -166,7 +200,7 @@ class EagleStep:
     step's roots are the accepted bonus tokens and their features."""
 
     def __init__(self, dims, params, weights, draft_weights, k_cache, v_cache, dk_cache, dv_cache, *, batch,
-                 max_prefix, device="cuda", lm_layout=0, weight_layout=0):
+                 max_prefix, device="cuda", lm_layout=0, weight_layout=0, sample=False):
         self.drafter = TreeDrafter(dims, params, weights, draft_weights, dk_cache, dv_cache, batch=batch,
                                    max_prefix=max_prefix, device=device, lm_layout=lm_layout,
                                    weight_layout=weight_layout)
@@ -174,7 +208,7 @@ class EagleStep:
         self.total = batch * M
         self.verifier = TreeVerifier(dims, weights, k_cache, v_cache, batch=batch, max_total_nodes=self.total,
                                      max_nodes=M, max_prefix=max_prefix, device=device, lm_layout=lm_layout,
-                                     weight_layout=weight_layout)
+                                     weight_layout=weight_layout, sample=sample)
 
     def step(self, root_feature, root_token, prefix_len, timer=None):
         d, v = self.drafter, self.verifier
@@ -182,4 +216,14 @@ class EagleStep:
         v.encode(d.tree_off, d.parent, prefix_len, self.total)
         v.verify(d.tree_off, d.tokens, prefix_len, self.total, timer=timer)
         v.accept(d.tree_off, d.parent, d.tokens, prefix_len)
+        return v.next_feature, v.next_token
+
+    def step_sample(self, root_feature, root_token, prefix_len, temperature, gumbel, u, timer=None):
+        """The same step with acceptance at temperature T > 0 (needs sample=True): gumbel
+        [batch][vocab] noise rows, u [batch * max_nodes] acceptance uniforms."""
+        d, v = self.drafter, self.verifier
+        d.expand(root_feature, root_token, prefix_len, timer=timer)
+        v.encode(d.tree_off, d.parent, prefix_len, self.total)
+        v.verify_sample(d.tree_off, d.tokens, d.parent, prefix_len, self.total, temperature, gumbel, timer=timer)
+        v.accept_sample(d.tree_off, d.parent, d.tokens, u, prefix_len)
         return v.next_feature, v.next_token
