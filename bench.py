@@ -303,10 +303,25 @@ def bench_sampling(args, wl, st, t, prefix0, feat, tok):
     acc = run(min(n, 10), count=True)
     acc_mean = float(np.mean(acc))
     nodes = st.total
+    # the sampling LM head at 960 rows is bound by MFMA (2 M H V flops), not by its bytes
+    # (weights once, bf16 feature rows, the noise rows, 12 bytes of results per row)
+    dims = wl.dims
+    lm_avg = lm_ms / max(lm_n, 1)
+    flops = 2.0 * nodes * dims.hidden * dims.vocab
+    byts = dims.vocab * dims.hidden * 2 + nodes * dims.hidden * 2 + gumbel.nbytes + nodes * 12
+    lm_roof = None
+    if lm_n:
+        ach = flops / (lm_avg * 1e-3) / 1e12
+        lm_roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                   "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops,
+                   "algorithmic_bytes": byts,
+                   "hbm_frac": round(byts / (lm_avg * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                   "kernel": "gemm_bf16_kernel<..., SAMPLE> (LM head + sampling epilogue)"}
     return {
         "temperature": T, "ms_verify": round(ms_verify, 4),
         "verify_nodes_s": round(nodes / (ms_verify * 1e-3), 1),
-        "lm_head_ms": round(lm_ms / max(lm_n, 1), 4),
+        "lm_head_ms": round(lm_avg, 4),
+        "lm_head_roofline": lm_roof,
         "verify_stage_ms": stages,
         "ms_per_step": round(ms_step, 4),
         "accepted_per_step": acc_mean, "accepted_tok_s": round(acc_mean / (ms_step * 1e-3), 1),
