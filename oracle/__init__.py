@@ -37,6 +37,8 @@ from .layer import (as_f64, rms_norm, rope_rotate_half, attend, layer_rows, veri
 from .accept import (accept_sequence, accept_batch, commit_sequence, sample_accept_sequence, sample_summaries,
                      sample_accept_from_summaries)
 from .draft import draft_expand, draft_select_level, draft_rerank, fuse_features
+from .decode import (verify_forward_layers, commit_layers, draft_kv_rows, draft_kv_commit, eagle_decode,
+                     greedy_decode)
 
 __all__ = [
     "tree_encode", "pack_ancestors", "encode_batch", "TreeEncoding",
@@ -45,4 +47,5 @@ __all__ = [
     "accept_sequence", "accept_batch", "commit_sequence", "sample_accept_sequence", "sample_summaries",
     "sample_accept_from_summaries",
     "draft_expand", "draft_select_level", "draft_rerank", "fuse_features",
+    "verify_forward_layers", "commit_layers", "draft_kv_rows", "draft_kv_commit", "eagle_decode", "greedy_decode",
 ]

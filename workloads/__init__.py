@@ -7,10 +7,12 @@ projection, no argmax, no acceptance), so both the fp64 CPU oracle and the HIP
 path can consume the same inputs without sharing any of the method's code.
 """
 from .bf16 import f32_to_bf16_bits, bf16_bits_to_f32, bf16_bits_to_f64
-from .configs import LayerDims, DraftParams, CONFIGS, Workload, make_workload, mini_dims
+from .configs import (LayerDims, DraftParams, CONFIGS, Workload, make_workload, mini_dims, StackWorkload,
+                      stack_workload)
 from . import trees
 
 __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64",
     "LayerDims", "DraftParams", "CONFIGS", "Workload", "make_workload", "mini_dims", "trees",
+    "StackWorkload", "stack_workload",
 ]

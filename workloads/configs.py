@@ -121,20 +121,22 @@ def gain_vector(seed, tid, n, std, dtype):
     return f32_to_bf16_bits(g) if dtype == "bf16" else g
 
 
-def layer_weights(seed, dims: LayerDims, prefix="", gamma_std=0.0):
-    """Random-init decoder-layer weights, [out][in] row-major."""
+def layer_weights(seed, dims: LayerDims, prefix="", gamma_std=0.0, tid_offset=0):
+    """Random-init decoder-layer weights, [out][in] row-major.  tid_offset shifts every
+    tensor id (layer l of a stack uses LAYER_TID_STRIDE * l)."""
     H, D, Hq, Hkv, F = dims.hidden, dims.head_dim, dims.n_q_heads, dims.n_kv_heads, dims.ffn
     t = dims.dtype
+    tid = lambda name: TID[prefix + name] + tid_offset  # noqa: E731
     w = {
-        "w_qkv": normal_tensor(seed, TID[prefix + "w_qkv"], (dims.qkv_rows, H), 0.02, t),
-        "w_o": normal_tensor(seed, TID[prefix + "w_o"], (H, Hq * D), 0.02, t),
+        "w_qkv": normal_tensor(seed, tid("w_qkv"), (dims.qkv_rows, H), 0.02, t),
+        "w_o": normal_tensor(seed, tid("w_o"), (H, Hq * D), 0.02, t),
     }
     if F > 0:
-        w["ln_attn"] = gain_vector(seed, TID[prefix + "ln_attn"], H, gamma_std, t)
-        w["ln_mlp"] = gain_vector(seed, TID[prefix + "ln_mlp"], H, gamma_std, t)
-        w["w_gate"] = normal_tensor(seed, TID[prefix + "w_gate"], (F, H), 0.02, t)
-        w["w_up"] = normal_tensor(seed, TID[prefix + "w_up"], (F, H), 0.02, t)
-        w["w_down"] = normal_tensor(seed, TID[prefix + "w_down"], (H, F), 0.02, t)
+        w["ln_attn"] = gain_vector(seed, tid("ln_attn"), H, gamma_std, t)
+        w["ln_mlp"] = gain_vector(seed, tid("ln_mlp"), H, gamma_std, t)
+        w["w_gate"] = normal_tensor(seed, tid("w_gate"), (F, H), 0.02, t)
+        w["w_up"] = normal_tensor(seed, tid("w_up"), (F, H), 0.02, t)
+        w["w_down"] = normal_tensor(seed, tid("w_down"), (H, F), 0.02, t)
     return w
 
 
@@ -285,3 +287,56 @@ def with_trees(wl: Workload, parents, tokens=None, x_seed_tid=None):
         wl2.x = normal_tensor(wl.seed, x_seed_tid or TID["x"], (int(wl2.tree_off[-1]), wl.dims.hidden), 1.0,
                               wl.dims.dtype)
     return wl2
+
+
+LAYER_TID_STRIDE = 1000  # tensor ids of layer l of a stack: TID[...] + LAYER_TID_STRIDE * l
+
+
+@dataclass
+class StackWorkload:
+    """A target of n_layers decoder layers under one LM head, with one KV cache per layer,
+    and a draft head (w_fc + one layer) with its own cache, for decode loops."""
+    seed: int
+    dims: LayerDims
+    n_layers: int
+    batch: int
+    prefix_len: np.ndarray   # [B] int32
+    cache_cap: int
+    layers: list             # n_layers weight dicts (w_qkv, w_o, ln_attn, ln_mlp, w_gate, w_up, w_down)
+    weights: dict            # final_ln, w_lm, embed
+    k_caches: np.ndarray     # [n_layers][B][Hkv][cap][D], prefix filled, rest zero
+    v_caches: np.ndarray
+    draft_weights: dict      # w_fc and the draft layer
+    dk_cache: np.ndarray     # [B][Hkv][cap][D]
+    dv_cache: np.ndarray
+    root_feature: np.ndarray  # [B][H] float32: the feature that precedes each root token
+    root_token: np.ndarray    # [B] int32
+
+
+def stack_workload(seed, dims: LayerDims, n_layers, *, batch=1, prefix=64, cache_cap=None, gamma_std=0.0,
+                   embed_std=0.02):
+    """Seeded stack of n_layers random-init layers (layer 0 draws the same tensors as the
+    single-layer workloads of this seed), prefix K/V N(0, 1) per layer, embedding
+    N(0, embed_std), a draft head, root features N(0, 1) and uniform root tokens."""
+    B = batch
+    prefix_len = np.array(prefix if np.ndim(prefix) else [prefix] * B, dtype=np.int32)
+    H, D, Hkv, V, t = dims.hidden, dims.head_dim, dims.n_kv_heads, dims.vocab, dims.dtype
+    cap = cache_cap or int(prefix_len.max()) + 64
+    layers = [layer_weights(seed, dims, gamma_std=gamma_std, tid_offset=LAYER_TID_STRIDE * l) for l in range(n_layers)]
+    weights = dict(w_lm=normal_tensor(seed, TID["w_lm"], (V, H), 0.02, t),
+                   embed=normal_tensor(seed, TID["embed"], (V, H), embed_std, t))
+    if dims.rms_eps > 0:
+        weights["final_ln"] = gain_vector(seed, TID["final_ln"], H, gamma_std, t)
+    kc = np.stack([_kv_cache(seed, TID["k_prefix"] + LAYER_TID_STRIDE * l, B, Hkv, cap, D, prefix_len, t)
+                   for l in range(n_layers)])
+    vc = np.stack([_kv_cache(seed, TID["v_prefix"] + LAYER_TID_STRIDE * l, B, Hkv, cap, D, prefix_len, t)
+                   for l in range(n_layers)])
+    dw = layer_weights(seed, dims, prefix="d_", gamma_std=gamma_std)
+    dw["w_fc"] = normal_tensor(seed, TID["w_fc"], (H, 2 * H), 0.02, t)
+    return StackWorkload(
+        seed=seed, dims=dims, n_layers=n_layers, batch=B, prefix_len=prefix_len, cache_cap=cap, layers=layers,
+        weights=weights, k_caches=kc, v_caches=vc, draft_weights=dw,
+        dk_cache=_kv_cache(seed, TID["d_k_prefix"], B, Hkv, cap, D, prefix_len, t),
+        dv_cache=_kv_cache(seed, TID["d_v_prefix"], B, Hkv, cap, D, prefix_len, t),
+        root_feature=normal_tensor(seed, TID["root_feature"], (B, H), 1.0, "f32"),
+        root_token=np.random.default_rng([seed, TID["root_token"]]).integers(0, V, size=B).astype(np.int32))
