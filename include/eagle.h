@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define EAGLE_ABI_VERSION 5
+#define EAGLE_ABI_VERSION 6
 
 typedef enum {
   EAGLE_OK = 0,
@@ -351,10 +351,83 @@ int eagle_draft_pool(const eagle_dims* dims, const eagle_draft_params* params, i
                      int32_t* token, int32_t* parent, int32_t* depth, float* cum_logp, float* logp,
                      int32_t* expanded, void* stream);
 
+/* ---- a target of several decoder layers, and the draft KV update --------------
+ * Method: "Speculative decoding with EAGLE", Deep dive (the target verifies every
+ * drafted token in one pass; the emitted text is what the target alone would produce)
+ * and Technical insight (the draft works on the target's hidden features and is fed the
+ * true embedding of the next token); "yuhuili" page (the draft reads the target's
+ * second-top-layer features).  The pages describe a full model; the readings here: the
+ * target is n_layers Llama-style layers (eagle_dims, ffn > 0 and rms_eps > 0) applied in
+ * order, each with its own KV cache, under one final norm and LM head; every layer sees
+ * the same tree mask and positions; a node's feature is the last layer's output.
+ *
+ * eagle_tree_verify_layers: eagle_tree_verify through layers[0 .. n_layers-1] (host
+ * array of n_layers eagle_layer_w; layer l's input is layer l-1's output h, f32).
+ * Caches: layer l's cache is at k_cache/v_cache + l * cache_layer_stride elements (each
+ * layer [B][Hkv][capacity][D] with the strides of `cache`).  Outputs: k_tree, v_tree
+ * [n_layers][total_nodes][Hkv][D] (layer l at l * total_nodes * Hkv * D elements),
+ * h_out = the last layer's output, argmax/maxlogit of the LM head on it; dbg_attn (NULL to
+ * skip) is the last layer's attention output.  n_layers == 1 is eagle_tree_verify.
+ * Errors: as eagle_tree_verify; n_layers outside 1..1024 or a negative stride ->
+ * EAGLE_ERR_ARG; n_layers > 1 without the MLP layer -> EAGLE_ERR_UNSUPPORTED.
+ * Workspace: eagle_workspace_size(0, ...), the same as one layer (buffers are reused). */
+int eagle_tree_verify_layers(const eagle_dims* dims, int32_t n_layers, const eagle_layer_w* layers,
+                             const void* final_ln, const void* w_lm, int32_t batch, const int32_t* tree_off,
+                             int32_t total_nodes, int32_t max_nodes, const void* x_in, const void* embed,
+                             const int32_t* tokens, const uint64_t* anc, int32_t mask_words, const int32_t* pos,
+                             const int32_t* prefix_len, int32_t max_prefix, const void* k_cache, const void* v_cache,
+                             const eagle_cache_layout* cache, int64_t cache_layer_stride, void* k_tree,
+                             void* v_tree, float* h_out, int32_t* argmax, float* maxlogit, float* dbg_attn,
+                             float* dbg_logits, void* workspace, size_t ws_bytes, eagle_timer* timer, void* stream);
+
+/* eagle_accept_commit_layers: eagle_accept_commit (same acceptance, outputs and errors)
+ * committing every layer: cache slot prefix_len[b] + d of layer l <- layer l's tree K/V
+ * of path[d], for l = 0 .. n_layers-1.  Layer l's cache is at l * cache_layer_stride
+ * elements and its tree K/V at l * tree_layer_stride elements (eagle_tree_verify_layers
+ * writes them at total_nodes * Hkv * D).  All layers share `cache`'s strides and
+ * capacity.  Strides must be positive multiples of 16 bytes when n_layers > 1, else
+ * EAGLE_ERR_ARG.  A rejected sequence (accept_len -1) is committed in no layer. */
+int eagle_accept_commit_layers(int32_t batch, const int32_t* tree_off, int32_t max_nodes, const int32_t* parent,
+                               const int32_t* tokens, const int32_t* argmax, const uint64_t* anc,
+                               int32_t mask_words, const int32_t* depth, const void* k_tree, const void* v_tree,
+                               void* k_cache, void* v_cache, const eagle_cache_layout* cache, int32_t n_kv_heads,
+                               int32_t head_dim, int32_t dtype, int32_t n_layers, int64_t cache_layer_stride,
+                               int64_t tree_layer_stride, int32_t* prefix_len, const float* h_nodes,
+                               int32_t hidden, float* next_feature, int32_t max_accept, int32_t* accept_len,
+                               int32_t* path, int32_t* out_tokens, int32_t* next_token, int32_t* dev_status,
+                               void* stream);
+
+/* eagle_draft_kv_commit: after an acceptance call, the draft head's cache slots of the
+ * committed positions recomputed from the target's true features.  The draft's cache is
+ * indexed by the same positions as the target's: slot t holds the draft layer's K/V of
+ * the row W_fc [f_(t-1) ; E[token_t]] at position t, f_(t-1) the target's feature at t - 1.
+ * Per sequence b with L = accept_len[b] >= 0 and P = prefix_len[b] - L - 1 (prefix_len
+ * already advanced by the commit), for d = 0..L:
+ *   f = root_feature[b] (d = 0: the feature that preceded this step's root, as given to
+ *       eagle_draft_expand) or h_nodes[tree_off[b] + path[b][d-1]] (d >= 1);
+ *   row = W_fc [f ; embed[tokens[tree_off[b] + path[b][d]]]];
+ *   slot P + d of dk_cache/dv_cache <- rotary(K rows of W_qkv RMSNorm(row)) at position
+ *       P + d, and the V rows of W_qkv RMSNorm(row) (RMSNorm with draft_layer->ln_attn).
+ * A sequence with accept_len -1 is left alone.  Inputs: w_fc [H][2H] and draft_layer
+ * (ln_attn, w_qkv; layout as eagle_draft_expand), embed [V][H], tokens and h_nodes
+ * [total_nodes][H] f32 of the verified trees, root_feature [B][H] f32 (must not be the
+ * buffer the acceptance call wrote next_feature into), accept_len [B] and path
+ * [B][max_accept + 1] from the acceptance call.  bf16 with head_dim 128 only
+ * (EAGLE_ERR_UNSUPPORTED otherwise).  Device error: a slot >= capacity sets
+ * *dev_status = EAGLE_ERR_CAPACITY and that row is not written.
+ * Workspace: eagle_workspace_size(4, dims, batch, 0, max_accept + 1, 0, NULL). */
+int eagle_draft_kv_commit(const eagle_dims* dims, const void* w_fc, const eagle_layer_w* draft_layer,
+                          const void* embed, int32_t batch, const int32_t* tree_off, const int32_t* tokens,
+                          const float* h_nodes, const float* root_feature, const int32_t* accept_len,
+                          const int32_t* path, int32_t max_accept, const int32_t* prefix_len, void* dk_cache,
+                          void* dv_cache, const eagle_cache_layout* cache, int32_t* dev_status, void* workspace,
+                          size_t ws_bytes, void* stream);
+
 /* ---- workspace -------------------------------------------------------------
- * Bytes of workspace a call needs.  which: 0 = eagle_tree_verify, 1 =
- * eagle_draft_expand, 2 = eagle_fuse_features, 3 = eagle_tree_verify_sample.  params is used only for
- * which == 1.  Returns 0 for unsupported arguments. */
+ * Bytes of workspace a call needs.  which: 0 = eagle_tree_verify and
+ * eagle_tree_verify_layers, 1 = eagle_draft_expand, 2 = eagle_fuse_features,
+ * 3 = eagle_tree_verify_sample, 4 = eagle_draft_kv_commit (max_nodes = max_accept + 1).
+ * params is used only for which == 1.  Returns 0 for unsupported arguments. */
 size_t eagle_workspace_size(int32_t which, const eagle_dims* dims, int32_t batch, int32_t total_nodes,
                             int32_t max_nodes, int32_t max_prefix, const eagle_draft_params* params);
 

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert E.lib().eagle_abi_version() == 5
+    assert E.lib().eagle_abi_version() == 6
     assert E.status_str(0) == "ok"
     assert "workspace" in E.status_str(A.EAGLE_ERR_WORKSPACE)
 
@@ -190,3 +190,70 @@ def test_accept_sample_host_errors():
     assert call(dtype=5) == A.EAGLE_ERR_UNSUPPORTED
     assert call(max_accept=500) == A.EAGLE_ERR_ARG
     assert call(hd=4) == A.EAGLE_ERR_UNSUPPORTED
+
+
+def test_verify_layers_host_errors():
+    from dataclasses import replace
+    L = E.lib()
+    cl = A.EagleCacheLayout(1 << 20, 1 << 16, 128, 4096)
+    ws_bytes = A.eagle_workspace_size(0, LLAMA8B, 1, 60, 60, 2048)
+    ws = ctypes.c_void_p(1 << 20)
+
+    def call(dims=LLAMA8B, n=2, arr_n=2, stride=1 << 24, gates=True, nbytes=ws_bytes):
+        d = A.dims_struct(dims)
+        lws = [A.EagleLayerW(4096, 4096, 4096, 4096, 4096 if gates else None, 4096, 4096, 0) for _ in range(arr_n)]
+        arr = (A.EagleLayerW * arr_n)(*lws)
+        return L.eagle_tree_verify_layers(ctypes.byref(d), n, arr, FAKE, FAKE, 1, FAKE, 60, 60, FAKE, None, None,
+                                          FAKE, 1, FAKE, FAKE, 2048, FAKE, FAKE, ctypes.byref(cl), stride, FAKE,
+                                          FAKE, FAKE, FAKE, FAKE, None, None, ws, nbytes, None, None)
+    assert call(n=0) == A.EAGLE_ERR_ARG
+    assert call(n=2000, arr_n=2) == A.EAGLE_ERR_ARG
+    assert call(stride=-1) == A.EAGLE_ERR_ARG
+    assert call(gates=False) == A.EAGLE_ERR_ARG  # a layer without its MLP matrices
+    assert call(dims=TINY) == A.EAGLE_ERR_UNSUPPORTED  # a stack needs the MLP layer
+    assert call(dims=replace(LLAMA8B, head_dim=96)) == A.EAGLE_ERR_UNSUPPORTED
+    assert call(nbytes=ws_bytes - 1) == A.EAGLE_ERR_WORKSPACE
+
+
+def test_accept_commit_layers_host_errors():
+    cl = A.EagleCacheLayout(1 << 20, 1 << 16, 128, 4096)
+    f = E.lib().eagle_accept_commit_layers
+
+    def call(**kw):
+        a = dict(B=1, maxn=60, mw=1, n=4, cs=1 << 24, ts=1 << 20, dtype=0, tree_off=FAKE)
+        a.update(kw)
+        return f(a["B"], a["tree_off"], a["maxn"], FAKE, FAKE, FAKE, FAKE, a["mw"], FAKE, FAKE, FAKE, FAKE, FAKE,
+                 ctypes.byref(cl), 8, 128, a["dtype"], a["n"], a["cs"], a["ts"], FAKE, None, 4096, None, 16, FAKE,
+                 FAKE, FAKE, FAKE, None, None)
+    assert call(n=0) == A.EAGLE_ERR_ARG
+    assert call(cs=0) == A.EAGLE_ERR_ARG
+    assert call(ts=-64) == A.EAGLE_ERR_ARG
+    assert call(ts=3) == A.EAGLE_ERR_ARG  # not a multiple of 16 bytes
+    assert call(tree_off=None) == A.EAGLE_ERR_ARG
+    assert call(maxn=130, mw=2) == A.EAGLE_ERR_CAPACITY
+    assert call(dtype=5) == A.EAGLE_ERR_UNSUPPORTED
+
+
+def test_draft_kv_commit_host_errors():
+    from dataclasses import replace
+    L = E.lib()
+    cl = A.EagleCacheLayout(1 << 20, 1 << 16, 128, 4096)
+    ws_bytes = A.eagle_workspace_size(4, LLAMA8B, 16, 0, 7, 0)
+    assert ws_bytes > 0
+    assert A.eagle_workspace_size(4, TINY, 16, 0, 7, 0) == 0
+    ws = ctypes.c_void_p(1 << 20)
+    lw = A.EagleLayerW(4096, 4096, 4096, 4096, 4096, 4096, 4096, 0)
+
+    def call(dims=LLAMA8B, w_fc=FAKE, h=FAKE, root=FAKE, max_accept=6, w_s=ws, nbytes=ws_bytes):
+        d = A.dims_struct(dims)
+        return L.eagle_draft_kv_commit(ctypes.byref(d), w_fc, ctypes.byref(lw), FAKE, 16, FAKE, FAKE, h, root, FAKE,
+                                       FAKE, max_accept, FAKE, FAKE, FAKE, ctypes.byref(cl), None, w_s, nbytes, None)
+    assert call(w_fc=None) == A.EAGLE_ERR_ARG
+    assert call(h=None) == A.EAGLE_ERR_ARG
+    assert call(root=None) == A.EAGLE_ERR_ARG
+    assert call(max_accept=-1) == A.EAGLE_ERR_ARG
+    assert call(max_accept=128) == A.EAGLE_ERR_ARG
+    assert call(w_s=ctypes.c_void_p((1 << 20) + 16)) == A.EAGLE_ERR_ARG
+    assert call(nbytes=ws_bytes - 1) == A.EAGLE_ERR_WORKSPACE
+    assert call(dims=TINY) == A.EAGLE_ERR_UNSUPPORTED
+    assert call(dims=replace(LLAMA8B, head_dim=64)) == A.EAGLE_ERR_UNSUPPORTED

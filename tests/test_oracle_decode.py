@@ -109,24 +109,7 @@ def _textbook_greedy(wl, n):
 
 
 def _planted_tree(rng, n, continuation, depth):
-    """A random tree whose first node at ``depth`` carries ``continuation`` along its root
-    path (siblings of a planted node get other tokens); depth 0 plants nothing."""
-    par = T.random_tree(rng, n)
-    dep = T.depths(par)
-    toks = T.tree_tokens(rng, par, DIMS.vocab)
-    cands = [i for i in range(n) if dep[i] == depth]
-    if depth > 0 and cands:
-        path = []
-        j = cands[0]
-        while j != -1:
-            path.append(j)
-            j = par[j]
-        for d, node in enumerate(path[::-1][1:], start=1):
-            toks[node] = continuation[d - 1]
-            for s in range(n):
-                if s != node and par[s] == par[node] and toks[s] == toks[node]:
-                    toks[s] = (toks[s] + 1) % DIMS.vocab
-    return par, toks
+    return T.planted_tree(rng, n, DIMS.vocab, continuation, depth)
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])

@@ -75,6 +75,15 @@ PROTOTYPES = {
     "eagle_accept_commit_sample": (_I, [_I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                         ctypes.POINTER(EagleCacheLayout), _I, _I, _I, _P, _P, _I, _P, _I, _P, _P,
                                         _P, _P, _P, _P]),
+    "eagle_tree_verify_layers": (_I, [ctypes.POINTER(EagleDims), _I, ctypes.POINTER(EagleLayerW), _P, _P, _I, _P,
+                                      _I, _I, _P, _P, _P, _P, _I, _P, _P, _I, _P, _P,
+                                      ctypes.POINTER(EagleCacheLayout), ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P,
+                                      _P, _S, _P, _P]),
+    "eagle_accept_commit_layers": (_I, [_I, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
+                                        ctypes.POINTER(EagleCacheLayout), _I, _I, _I, _I, ctypes.c_int64,
+                                        ctypes.c_int64, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P, _P]),
+    "eagle_draft_kv_commit": (_I, [ctypes.POINTER(EagleDims), _P, ctypes.POINTER(EagleLayerW), _P, _I, _P, _P, _P,
+                                   _P, _P, _P, _I, _P, _P, _P, ctypes.POINTER(EagleCacheLayout), _P, _P, _S, _P]),
     "eagle_draft_expand": (_I, [ctypes.POINTER(EagleDims), ctypes.POINTER(EagleDraftParams), _P,
                                 ctypes.POINTER(EagleLayerW), _P, _P, _P, _I, _P, _P, _P, _P,
                                 ctypes.POINTER(EagleCacheLayout), _P, _I, _P, _P, _P, _P, _P, _S, _P, _P]),
@@ -183,6 +192,67 @@ def eagle_tree_verify(dims, layer, final_ln, w_lm, tree_off, x_in, embed, tokens
                                  _p(dbg_logits), _p(workspace), workspace.numel() * workspace.element_size(),
                                  _t(timer), _stream(stream))
     _check(st, "eagle_tree_verify")
+
+
+def layers_array(layers, layout=0):
+    """A ctypes array of EagleLayerW, one per layer dict (or EagleLayerW) of ``layers``."""
+    structs = [lw if isinstance(lw, EagleLayerW) else layer_struct(lw, layout) for lw in layers]
+    return (EagleLayerW * len(structs))(*structs)
+
+
+def eagle_tree_verify_layers(dims, layers, final_ln, w_lm, tree_off, x_in, embed, tokens, anc, mask_words, pos,
+                             prefix_len, k_caches, v_caches, k_tree, v_tree, h_out, argmax, maxlogit, workspace, *,
+                             total_nodes, max_nodes, max_prefix, dbg_attn=None, dbg_logits=None, timer=None,
+                             stream=None):
+    """layers: a ctypes array from layers_array (or a list of layer dicts); k_caches/v_caches
+    [n_layers][B][Hkv][cap][D]; k_tree/v_tree [n_layers][total_nodes][Hkv][D]."""
+    d = dims_struct(dims) if not isinstance(dims, EagleDims) else dims
+    arr = layers if isinstance(layers, ctypes.Array) else layers_array(layers)
+    cl = cache_struct(k_caches[0])
+    if k_caches.stride(0) != v_caches.stride(0):
+        raise EagleError(EAGLE_ERR_ARG, "eagle_tree_verify_layers: K and V caches differ in layout")
+    B = tree_off.numel() - 1
+    st = lib().eagle_tree_verify_layers(ctypes.byref(d), len(arr), arr, _p(final_ln), _p(w_lm), B, _p(tree_off),
+                                        total_nodes, max_nodes, _p(x_in), _p(embed), _p(tokens), _p(anc),
+                                        mask_words, _p(pos), _p(prefix_len), max_prefix, _p(k_caches),
+                                        _p(v_caches), ctypes.byref(cl), k_caches.stride(0), _p(k_tree), _p(v_tree),
+                                        _p(h_out), _p(argmax), _p(maxlogit), _p(dbg_attn), _p(dbg_logits),
+                                        _p(workspace), workspace.numel() * workspace.element_size(), _t(timer),
+                                        _stream(stream))
+    _check(st, "eagle_tree_verify_layers")
+
+
+def eagle_accept_commit_layers(tree_off, parent, tokens, argmax, anc, mask_words, depth, k_tree, v_tree, k_caches,
+                               v_caches, prefix_len, h_nodes, next_feature, accept_len, path, out_tokens, next_token,
+                               dev_status=None, *, max_nodes, max_accept, n_kv_heads, head_dim, dtype, hidden,
+                               stream=None):
+    """k_caches/v_caches [n_layers][B][Hkv][cap][D]; k_tree/v_tree [n_layers][total_nodes][Hkv][D]."""
+    cl = cache_struct(k_caches[0])
+    B = tree_off.numel() - 1
+    nl = k_caches.shape[0]
+    if k_caches.stride(0) != v_caches.stride(0) or k_tree.stride(0) != v_tree.stride(0) or k_tree.shape[0] != nl:
+        raise EagleError(EAGLE_ERR_ARG, "eagle_accept_commit_layers: layer layouts differ")
+    st = lib().eagle_accept_commit_layers(B, _p(tree_off), max_nodes, _p(parent), _p(tokens), _p(argmax), _p(anc),
+                                          mask_words, _p(depth), _p(k_tree), _p(v_tree), _p(k_caches),
+                                          _p(v_caches), ctypes.byref(cl), n_kv_heads, head_dim, dtype, nl,
+                                          k_caches.stride(0), k_tree.stride(0), _p(prefix_len), _p(h_nodes), hidden,
+                                          _p(next_feature), max_accept, _p(accept_len), _p(path), _p(out_tokens),
+                                          _p(next_token), _p(dev_status), _stream(stream))
+    _check(st, "eagle_accept_commit_layers")
+
+
+def eagle_draft_kv_commit(dims, w_fc, draft_layer, embed, tree_off, tokens, h_nodes, root_feature, accept_len, path,
+                          prefix_len, dk_cache, dv_cache, workspace, dev_status=None, *, max_accept, stream=None):
+    d = dims_struct(dims) if not isinstance(dims, EagleDims) else dims
+    lw = layer_struct(draft_layer) if not isinstance(draft_layer, EagleLayerW) else draft_layer
+    cl = cache_struct(dk_cache)
+    B = tree_off.numel() - 1
+    st = lib().eagle_draft_kv_commit(ctypes.byref(d), _p(w_fc), ctypes.byref(lw), _p(embed), B, _p(tree_off),
+                                     _p(tokens), _p(h_nodes), _p(root_feature), _p(accept_len), _p(path),
+                                     max_accept, _p(prefix_len), _p(dk_cache), _p(dv_cache), ctypes.byref(cl),
+                                     _p(dev_status), _p(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream))
+    _check(st, "eagle_draft_kv_commit")
 
 
 def eagle_accept_commit(tree_off, parent, tokens, argmax, anc, mask_words, depth, k_tree, v_tree, k_cache, v_cache,

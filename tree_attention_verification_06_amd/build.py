@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libeagle_hip.so")
-SOURCES = ["abi.cpp", "tree.hip", "gemm.hip", "attn.hip", "draft.hip", "util.hip"]
+SOURCES = ["abi.cpp", "tree.hip", "gemm.hip", "attn.hip", "draft.hip", "decode.hip", "util.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -171,9 +171,12 @@ struct SampleOut {
   int32_t* rest_token;
 };
 
-// Verification of every node of every tree: one decoder layer + LM head with a fused
-// argmax, or (so != nullptr) with the sampling epilogue and its per-row merge.
-int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_ln, const void* w_lm, int B,
+// Verification of every node of every tree: n_layers decoder layers (layers[0..n_layers-1],
+// applied in order; layer l reads the caches at l * cache_ls elements and writes its tree
+// K/V at l * total_nodes * Hkv * D) + LM head with a fused argmax, or (so != nullptr) with
+// the sampling epilogue and its per-row merge.
+int verify_impl(const eagle_dims* d, const eagle_layer_w* layers, int n_layers, int64_t cache_ls,
+                const void* final_ln, const void* w_lm, int B,
                 const int32_t* tree_off, int total_nodes, int max_nodes, const void* x_in, const void* embed,
                 const int32_t* tokens, const uint64_t* anc, int mw, const int32_t* pos, const int32_t* prefix_len,
                 int max_prefix, const void* k_cache, const void* v_cache, const eagle_cache_layout* cache,
@@ -182,9 +185,14 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
                 const SampleOut* so = nullptr) {
   int rc = check_dims(d);
   if (rc) return rc;
-  if (!lw || !w_lm || !tree_off || !anc || !pos || !prefix_len || !k_cache || !v_cache || !cache || !k_tree ||
+  if (!layers || !w_lm || !tree_off || !anc || !pos || !prefix_len || !k_cache || !v_cache || !cache || !k_tree ||
       !v_tree || !h_out || !ws)
     return EAGLE_ERR_ARG;
+  if (n_layers < 1 || n_layers > 1024) return EAGLE_ERR_ARG;
+  // a stack needs the pre-norm layer with an MLP: the residual stream of layer l > 0 is the
+  // previous layer's f32 output, and the down epilogue prepares the next layer's norm
+  if (n_layers > 1 && (d->ffn <= 0 || !(d->rms_eps > 0.f))) return EAGLE_ERR_UNSUPPORTED;
+  if (n_layers > 1 && cache_ls < 0) return EAGLE_ERR_ARG;
   if (!so && !argmax) return EAGLE_ERR_ARG;
   if (so) {
     if (!so->parent || !tokens || !so->gumbel || !so->child_logit || !so->rest_lse || !so->rest_token)
@@ -195,11 +203,14 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     return EAGLE_ERR_ARG;
   if (!x_in && (!embed || !tokens)) return EAGLE_ERR_ARG;
   const bool norm = d->rms_eps > 0.f;
-  if (!lw->w_qkv || !lw->w_o) return EAGLE_ERR_ARG;
-  if (lw->layout != 0 && lw->layout != 1) return EAGLE_ERR_ARG;
-  if (lw->layout == 1 && d->dtype != EAGLE_BF16) return EAGLE_ERR_UNSUPPORTED;
-  if (norm && (!lw->ln_attn || !lw->ln_mlp || !lw->w_gate || !lw->w_up || !lw->w_down || !final_ln))
-    return EAGLE_ERR_ARG;
+  if (norm && !final_ln) return EAGLE_ERR_ARG;
+  for (int l = 0; l < n_layers; ++l) {
+    const eagle_layer_w* lw = layers + l;
+    if (!lw->w_qkv || !lw->w_o) return EAGLE_ERR_ARG;
+    if (lw->layout != 0 && lw->layout != 1) return EAGLE_ERR_ARG;
+    if (lw->layout == 1 && d->dtype != EAGLE_BF16) return EAGLE_ERR_UNSUPPORTED;
+    if (norm && (!lw->ln_attn || !lw->ln_mlp || !lw->w_gate || !lw->w_up || !lw->w_down)) return EAGLE_ERR_ARG;
+  }
   if (((uintptr_t)ws) & 255) return EAGLE_ERR_ARG;
   if (cache->token_stride % 8 || cache->head_stride % 8 || cache->batch_stride % 8 || cache->capacity < 0)
     return EAGLE_ERR_ARG;
@@ -242,7 +253,16 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     timer_end(timer, s);
     if (rc) return rc;
   }
-  // 1. RMSNorm -> QKV projection -> rotary at pos -> q (workspace), k_tree, v_tree
+  const int64_t tree_ls = (int64_t)M * Hkv * D;  // elements between two layers' tree K/V
+  for (int l = 0; l < n_layers; ++l) {
+  const eagle_layer_w* lw = layers + l;
+  const bool first = l == 0;
+  const eagle_layer_w* next = l + 1 < n_layers ? layers + l + 1 : nullptr;
+  void* k_tree_l = (char*)k_tree + (size_t)l * tree_ls * elem_size(dt);
+  void* v_tree_l = (char*)v_tree + (size_t)l * tree_ls * elem_size(dt);
+  // 1. RMSNorm -> QKV projection -> rotary at pos -> q (workspace), k_tree, v_tree.  Layer
+  //    l > 0 reads the previous layer's output: on the bf16 path as bf16(ln_attn * h) and
+  //    row sums of squares written by that layer's down epilogue
   {
     GemmDesc g = base_desc(d);
     g.w0 = lw->w_qkv;
@@ -251,17 +271,28 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     g.k = H;
     g.ldw = H;
     g.m = M;
-    g.x.a = xseg;
-    g.x.b = xseg;
+    if (first) {
+      g.x.a = xseg;
+      g.x.norm = norm ? 1 : 0;
+      g.x.gain = norm ? lw->ln_attn : nullptr;
+    } else if (bf) {
+      g.x.a = seg(h16, dt, H);
+      g.x.norm = 2;
+      g.x.ssq_in = ssq_h;
+      g.x.np = L.p_down.n_tiles;
+    } else {
+      g.x.a = seg(h_out, EAGLE_F32, H);
+      g.x.norm = 1;
+      g.x.gain = lw->ln_attn;
+    }
+    g.x.b = g.x.a;
     g.x.ka = H;
-    g.x.norm = norm ? 1 : 0;
-    g.x.gain = norm ? lw->ln_attn : nullptr;
     g.x.gain_dtype = dt;
     g.x.eps = d->rms_eps;
     g.epi.kind = EPI_QKV;
     g.epi.q_out = q;
-    g.epi.k_out = k_tree;
-    g.epi.v_out = v_tree;
+    g.epi.k_out = k_tree_l;
+    g.epi.v_out = v_tree_l;
     g.epi.out_dtype = dt;
     g.epi.pos = pos;
     g.epi.hq = Hq;
@@ -283,14 +314,14 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     a.hkv = Hkv;
     a.hd = D;
     a.q = q;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
+    a.k_cache = (const char*)k_cache + (size_t)l * cache_ls * elem_size(dt);
+    a.v_cache = (const char*)v_cache + (size_t)l * cache_ls * elem_size(dt);
     a.cb = cache->batch_stride;
     a.ch = cache->head_stride;
     a.ct = cache->token_stride;
     a.cap = cache->capacity;
-    a.k_tree = k_tree;
-    a.v_tree = v_tree;
+    a.k_tree = k_tree_l;
+    a.v_tree = v_tree_l;
     a.anc = anc;
     a.mw = mw;
     a.tree_off = tree_off;
@@ -298,7 +329,7 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     a.max_nodes = max_nodes;
     a.max_prefix = max_prefix;
     a.out = attn;
-    a.dbg = dbg_attn;
+    a.dbg = l + 1 == n_layers ? dbg_attn : nullptr;
     a.part_o = (float*)(w + L.attn_part);
     a.part_ml = a.part_o + (size_t)B * Hkv * L.pa.n_chunks * L.pa.rmax * D;
     rc = dt == EAGLE_F32 ? launch_attn_f32(a, M, timer, s) : launch_attn(a, L.pa, timer, s);
@@ -306,7 +337,8 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
   }
   // 3. O projection + residual -> y (or h_out for the attention-only layer); on the bf16
   //    path the epilogue also writes bf16(gain * y) and row sums of squares for the
-  //    next RMSNorm, so the next GEMM streams bf16 activations
+  //    next RMSNorm, so the next GEMM streams bf16 activations.  The residual is the
+  //    layer input: x (or the token embeddings) for layer 0, h_out (f32) after that
   float* yout = F > 0 ? y : h_out;
   {
     GemmDesc g = base_desc(d);
@@ -322,9 +354,14 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     g.epi.kind = EPI_RESID;
     g.epi.out = yout;
     g.epi.ld_out = H;
-    g.epi.resid = x_in ? x_in : embed;
-    g.epi.resid_idx = x_in ? nullptr : tokens;
-    g.epi.resid_dtype = dt;
+    if (first) {
+      g.epi.resid = x_in ? x_in : embed;
+      g.epi.resid_idx = x_in ? nullptr : tokens;
+      g.epi.resid_dtype = dt;
+    } else {
+      g.epi.resid = h_out;
+      g.epi.resid_dtype = EAGLE_F32;
+    }
     g.epi.ld_resid = H;
     if (bf) {
       g.epi.xn_out = F > 0 ? y16 : h16;
@@ -371,7 +408,8 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     rc = launch_gemm(g, L.p_gu, s);
     timer_end(timer, s);
     if (rc) return rc;
-    // 5. down projection + residual -> h_out (and bf16(final gain * h) + row sums of squares)
+    // 5. down projection + residual -> h_out (and bf16(gain * h) + row sums of squares,
+    //    with the next layer's attention gain, or the final gain after the last layer)
     GemmDesc g2 = base_desc(d);
     g2.w0 = lw->w_down;
     g2.w_layout = lw->layout;
@@ -390,7 +428,7 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     g2.epi.ld_resid = H;
     if (bf) {
       g2.epi.xn_out = h16;
-      g2.epi.xn_gain = final_ln;
+      g2.epi.xn_gain = next ? next->ln_attn : final_ln;
       g2.epi.ssq_out = ssq_h;
     }
     common(g2);
@@ -399,6 +437,7 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* lw, const void* final_
     timer_end(timer, s);
     if (rc) return rc;
   }
+  }  // layers
   // 6. final RMSNorm -> LM head with fused row argmax
   {
     GemmDesc g = base_desc(d);
@@ -547,9 +586,23 @@ int eagle_tree_verify(const eagle_dims* dims, const eagle_layer_w* layer, const 
                       const void* k_cache, const void* v_cache, const eagle_cache_layout* cache, void* k_tree,
                       void* v_tree, float* h_out, int32_t* argmax, float* maxlogit, float* dbg_attn,
                       float* dbg_logits, void* workspace, size_t ws_bytes, eagle_timer* timer, void* stream) {
-  return verify_impl(dims, layer, final_ln, w_lm, batch, tree_off, total_nodes, max_nodes, x_in, embed, tokens, anc,
-                     mask_words, pos, prefix_len, max_prefix, k_cache, v_cache, cache, k_tree, v_tree, h_out,
-                     argmax, maxlogit, dbg_attn, dbg_logits, workspace, ws_bytes, timer, (hipStream_t)stream);
+  return verify_impl(dims, layer, 1, 0, final_ln, w_lm, batch, tree_off, total_nodes, max_nodes, x_in, embed,
+                     tokens, anc, mask_words, pos, prefix_len, max_prefix, k_cache, v_cache, cache, k_tree, v_tree,
+                     h_out, argmax, maxlogit, dbg_attn, dbg_logits, workspace, ws_bytes, timer, (hipStream_t)stream);
+}
+
+int eagle_tree_verify_layers(const eagle_dims* dims, int32_t n_layers, const eagle_layer_w* layers,
+                             const void* final_ln, const void* w_lm, int32_t batch, const int32_t* tree_off,
+                             int32_t total_nodes, int32_t max_nodes, const void* x_in, const void* embed,
+                             const int32_t* tokens, const uint64_t* anc, int32_t mask_words, const int32_t* pos,
+                             const int32_t* prefix_len, int32_t max_prefix, const void* k_cache, const void* v_cache,
+                             const eagle_cache_layout* cache, int64_t cache_layer_stride, void* k_tree,
+                             void* v_tree, float* h_out, int32_t* argmax, float* maxlogit, float* dbg_attn,
+                             float* dbg_logits, void* workspace, size_t ws_bytes, eagle_timer* timer, void* stream) {
+  return verify_impl(dims, layers, n_layers, cache_layer_stride, final_ln, w_lm, batch, tree_off, total_nodes,
+                     max_nodes, x_in, embed, tokens, anc, mask_words, pos, prefix_len, max_prefix, k_cache, v_cache,
+                     cache, k_tree, v_tree, h_out, argmax, maxlogit, dbg_attn, dbg_logits, workspace, ws_bytes, timer,
+                     (hipStream_t)stream);
 }
 
 int eagle_accept_commit(int32_t batch, const int32_t* tree_off, int32_t max_nodes, const int32_t* parent,
@@ -571,6 +624,38 @@ int eagle_accept_commit(int32_t batch, const int32_t* tree_off, int32_t max_node
   a.mw = mask_words;
   a.depth = depth;
   return launch_accept_commit(a, batch, (hipStream_t)stream);
+}
+
+int eagle_accept_commit_layers(int32_t batch, const int32_t* tree_off, int32_t max_nodes, const int32_t* parent,
+                               const int32_t* tokens, const int32_t* argmax, const uint64_t* anc,
+                               int32_t mask_words, const int32_t* depth, const void* k_tree, const void* v_tree,
+                               void* k_cache, void* v_cache, const eagle_cache_layout* cache, int32_t n_kv_heads,
+                               int32_t head_dim, int32_t dtype, int32_t n_layers, int64_t cache_layer_stride,
+                               int64_t tree_layer_stride, int32_t* prefix_len, const float* h_nodes,
+                               int32_t hidden, float* next_feature, int32_t max_accept, int32_t* accept_len,
+                               int32_t* path, int32_t* out_tokens, int32_t* next_token, int32_t* dev_status,
+                               void* stream) {
+  if (!argmax || !anc || !depth) return EAGLE_ERR_ARG;
+  if (mask_words < 1 || mask_words > 2 || max_nodes > 64 * mask_words) return EAGLE_ERR_CAPACITY;
+  if (n_layers < 1 || n_layers > 1024) return EAGLE_ERR_ARG;
+  if (n_layers > 1 && (cache_layer_stride <= 0 || tree_layer_stride <= 0)) return EAGLE_ERR_ARG;
+  AcceptArgs a{};
+  int rc = commit_args(a, batch, tree_off, max_nodes, parent, tokens, k_tree, v_tree, k_cache, v_cache, cache,
+                       n_kv_heads, head_dim, dtype, prefix_len, h_nodes, hidden, next_feature, max_accept,
+                       accept_len, path, out_tokens, next_token, dev_status);
+  if (rc) return rc;
+  const int es = elem_size(dtype);
+  if ((cache_layer_stride * es) % 16 || (tree_layer_stride * es) % 16) return EAGLE_ERR_ARG;
+  a.argmax = argmax;
+  a.anc = anc;
+  a.mw = mask_words;
+  a.depth = depth;
+  a.n_layers = n_layers;
+  a.cache_ls = cache_layer_stride;
+  a.tree_ls = tree_layer_stride;
+  rc = launch_accept_commit(a, batch, (hipStream_t)stream);
+  if (rc) return rc;
+  return launch_commit_layers(a, batch, (hipStream_t)stream);
 }
 
 int eagle_accept_commit_sample(int32_t batch, const int32_t* tree_off, int32_t max_nodes, const int32_t* parent,
@@ -605,9 +690,9 @@ int eagle_tree_verify_sample(const eagle_dims* dims, const eagle_layer_w* layer,
                              float* rest_lse, int32_t* rest_token, void* workspace, size_t ws_bytes,
                              eagle_timer* timer, void* stream) {
   SampleOut so{parent, temperature, gumbel, child_logit, rest_lse, rest_token};
-  return verify_impl(dims, layer, final_ln, w_lm, batch, tree_off, total_nodes, max_nodes, x_in, embed, tokens, anc,
-                     mask_words, pos, prefix_len, max_prefix, k_cache, v_cache, cache, k_tree, v_tree, h_out,
-                     nullptr, nullptr, nullptr, nullptr, workspace, ws_bytes, timer, (hipStream_t)stream, &so);
+  return verify_impl(dims, layer, 1, 0, final_ln, w_lm, batch, tree_off, total_nodes, max_nodes, x_in, embed,
+                     tokens, anc, mask_words, pos, prefix_len, max_prefix, k_cache, v_cache, cache, k_tree, v_tree,
+                     h_out, nullptr, nullptr, nullptr, nullptr, workspace, ws_bytes, timer, (hipStream_t)stream, &so);
 }
 
 size_t eagle_workspace_size(int32_t which, const eagle_dims* dims, int32_t batch, int32_t total_nodes,
@@ -616,6 +701,7 @@ size_t eagle_workspace_size(int32_t which, const eagle_dims* dims, int32_t batch
   if (which == 1) return draft_workspace(dims, params, batch, max_prefix);
   if (which == 2) return fuse_layout(dims, batch).total;
   if (which == 3) return verify_workspace(dims, batch, total_nodes, max_nodes, max_prefix, true);
+  if (which == 4) return draft_kv_workspace(dims, batch, max_nodes - 1);
   return 0;
 }
 

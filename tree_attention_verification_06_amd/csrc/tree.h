@@ -37,6 +37,10 @@ struct AcceptArgs {
   const float* rest_lse;
   const int32_t* rest_token;
   const float* u;
+  // commit of a layer stack (commit_layers_kernel): layer l's tree K/V start at
+  // l * tree_ls elements of k_tree/v_tree and its caches at l * cache_ls elements
+  int n_layers;
+  int64_t cache_ls, tree_ls;
 };
 
 int launch_tree_build(int batch, const int32_t* tree_off, const int32_t* parent, const int32_t* prefix_len, int mw,
@@ -47,5 +51,7 @@ int launch_sample_prep(const int32_t* tree_off, const int32_t* parent, int batch
 int launch_sample_merge(const float4* part, int n_part, int rows, float* rest_lse, int32_t* rest_token,
                         hipStream_t s);
 int launch_accept_sample(const AcceptArgs& a, int batch, hipStream_t s);
+// Layers 1 .. n_layers-1 of a stack, after launch_accept_commit committed layer 0.
+int launch_commit_layers(const AcceptArgs& a, int batch, hipStream_t s);
 
 }  // namespace eagle

@@ -389,6 +389,59 @@ int launch_tree_build(int batch, const int32_t* tree_off, const int32_t* parent,
   return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
 }
 
+// Commit of the layers above the first in a stack of decoder layers.  accept_commit_kernel
+// has already chosen the path, committed layer 0 and advanced prefix_len, so workgroup
+// (b, l - 1) reads accept_len[b] and path[b] and copies layer l's tree K/V of the path into
+// that layer's cache slots P .. P + L with P = prefix_len[b] - L - 1.  A rejected sequence
+// (accept_len -1) is skipped.  Each thread issues up to four independent 16-byte loads
+// before its stores, so the copy is not one load latency per chunk.
+__global__ __launch_bounds__(256) void commit_layers_kernel(AcceptArgs a) {
+  const int b = blockIdx.x, l = blockIdx.y + 1;
+  const int L = a.accept_len[b];
+  if (L < 0) return;
+  const int P = a.prefix_len[b] - L - 1;
+  const int off = a.tree_off[b];
+  const int stride = a.max_accept + 1;
+  const int row_bytes = a.hd * a.elem;
+  const int chunks = row_bytes / 16;
+  const int per_node = a.hkv * chunks;
+  const int total = 2 * (L + 1) * per_node;
+  const char* kt = (const char*)a.k_tree + (size_t)l * a.tree_ls * a.elem;
+  const char* vt = (const char*)a.v_tree + (size_t)l * a.tree_ls * a.elem;
+  char* kc = (char*)a.k_cache + (size_t)l * a.cache_ls * a.elem;
+  char* vc = (char*)a.v_cache + (size_t)l * a.cache_ls * a.elem;
+  constexpr int U = 4;
+  for (int i0 = threadIdx.x; i0 < total; i0 += U * blockDim.x) {
+    uint4 v[U];
+    char* dst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * blockDim.x;
+      dst[u] = nullptr;
+      if (i < total) {
+        const int which = i / (total / 2);  // 0: K, 1: V
+        const int r = i % (total / 2);
+        const int d = r / per_node;
+        const int h = (r % per_node) / chunks;
+        const int ch = r % chunks;
+        const int node = a.path[(int64_t)b * stride + d];
+        v[u] = *(const uint4*)((which ? vt : kt) + ((int64_t)(off + node) * a.hkv + h) * row_bytes + ch * 16);
+        dst[u] = (which ? vc : kc) + ((int64_t)b * a.cb + (int64_t)h * a.ch + (int64_t)(P + d) * a.ct) * a.elem +
+                 ch * 16;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (dst[u]) *(uint4*)dst[u] = v[u];
+  }
+}
+
+int launch_commit_layers(const AcceptArgs& a, int batch, hipStream_t s) {
+  if (a.n_layers < 2) return EAGLE_OK;
+  hipLaunchKernelGGL(commit_layers_kernel, dim3(batch, a.n_layers - 1), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
+}
+
 int launch_accept_commit(const AcceptArgs& a, int batch, hipStream_t s) {
   hipLaunchKernelGGL(accept_commit_kernel, dim3(batch), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;

@@ -227,3 +227,134 @@ class EagleStep:
         v.verify_sample(d.tree_off, d.tokens, d.parent, prefix_len, self.total, temperature, gumbel, timer=timer)
         v.accept_sample(d.tree_off, d.parent, d.tokens, u, prefix_len)
         return v.next_feature, v.next_token
+
+
+class StackVerifier(TreeVerifier):
+    """TreeVerifier through a stack of decoder layers (eagle_tree_verify_layers and
+    eagle_accept_commit_layers).  weights: final_ln, w_lm (and embed); layers: one weight
+    dict per layer (layout weight_layout); k_caches/v_caches [n_layers][B][Hkv][cap][D].
+    k_tree/v_tree are [n_layers][max_total_nodes][Hkv][D]."""
+
+    def __init__(self, dims, weights, layers, k_caches, v_caches, *, batch, max_total_nodes, max_nodes, max_prefix,
+                 max_accept=None, device="cuda", lm_layout=0, weight_layout=0):
+        super().__init__(dims, weights, k_caches[0], v_caches[0], batch=batch, max_total_nodes=max_total_nodes,
+                         max_nodes=max_nodes, max_prefix=max_prefix, max_accept=max_accept, device=device,
+                         lm_layout=lm_layout, weight_layout=weight_layout)
+        self.layers = layers
+        self.larr = A.layers_array(layers, weight_layout)
+        self.n_layers = len(layers)
+        self.k_caches = k_caches
+        self.v_caches = v_caches
+        n = self.n_layers
+        self.k_tree = torch.zeros(n, *self.k_tree.shape, dtype=self.k_tree.dtype, device=device)
+        self.v_tree = torch.zeros(n, *self.v_tree.shape, dtype=self.v_tree.dtype, device=device)
+
+    def verify(self, tree_off, tokens, prefix_len, total_nodes, x=None, embed=None, dbg_attn=None, dbg_logits=None,
+               timer=None):
+        w = self.w
+        A.eagle_tree_verify_layers(self.dstruct, self.larr, w.get("final_ln"), w["w_lm"], tree_off, x,
+                                   embed if embed is not None else w.get("embed") if x is None else None, tokens,
+                                   self.anc, self.mw, self.pos, prefix_len, self.k_caches, self.v_caches, self.k_tree,
+                                   self.v_tree, self.h, self.argmax, self.maxlogit, self.workspace,
+                                   total_nodes=total_nodes, max_nodes=self.max_nodes, max_prefix=self.max_prefix,
+                                   dbg_attn=dbg_attn, dbg_logits=dbg_logits, timer=timer)
+
+    def accept(self, tree_off, parent, tokens, prefix_len):
+        d = self.dims
+        A.eagle_accept_commit_layers(tree_off, parent, tokens, self.argmax, self.anc, self.mw, self.depth, self.k_tree,
+                                     self.v_tree, self.k_caches, self.v_caches, prefix_len, self.h, self.next_feature,
+                                     self.accept_len, self.path, self.out_tokens, self.next_token, self.status,
+                                     max_nodes=self.max_nodes, max_accept=self.max_accept, n_kv_heads=d.n_kv_heads,
+                                     head_dim=d.head_dim, dtype=A.EAGLE_BF16 if d.dtype == "bf16" else A.EAGLE_F32,
+                                     hidden=d.hidden)
+
+
+class DraftKV:
+    """The draft-KV update after acceptance (eagle_draft_kv_commit) with its workspace."""
+
+    def __init__(self, dims, weights, draft_weights, dk_cache, dv_cache, *, batch, max_accept, device="cuda",
+                 weight_layout=0):
+        self.dstruct = A.dims_struct(dims)
+        self.lstruct = A.layer_struct(draft_weights, weight_layout)
+        self.w = weights
+        self.dw = draft_weights
+        self.dk_cache = dk_cache
+        self.dv_cache = dv_cache
+        self.max_accept = max_accept
+        ws = A.eagle_workspace_size(4, dims, batch, 0, max_accept + 1, 0)
+        if ws == 0:
+            raise A.EagleError(A.EAGLE_ERR_UNSUPPORTED, "eagle_workspace_size")
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        A.eagle_workspace_init(self.workspace)
+
+    def commit(self, verifier, tree_off, tokens, root_feature, prefix_len, timer=None):
+        """Slots of the path verifier.accept just committed, from verifier.h and root_feature
+        (the feature given to this step's draft; not verifier.next_feature)."""
+        v = verifier
+        A.eagle_draft_kv_commit(self.dstruct, self.dw["w_fc"], self.lstruct, self.w["embed"], tree_off, tokens, v.h,
+                                root_feature, v.accept_len, v.path, prefix_len, self.dk_cache, self.dv_cache,
+                                self.workspace, v.status, max_accept=v.max_accept)
+
+
+class EagleStackStep:
+    """The full speculative step with a target of several layers: draft a tree per sequence,
+    encode it, verify it through every layer, accept, commit every layer's K/V, then rewrite
+    the draft cache slots of the committed path from the target's true features.  No host
+    synchronisation.  step() returns (next_feature, next_token); the feature buffers
+    alternate between two tensors, so the returned feature can be passed straight back as the
+    next step's root feature."""
+
+    def __init__(self, dims, params, weights, layers, draft_weights, k_caches, v_caches, dk_cache, dv_cache, *, batch,
+                 max_prefix, device="cuda", lm_layout=0, weight_layout=0):
+        self.drafter = TreeDrafter(dims, params, weights, draft_weights, dk_cache, dv_cache, batch=batch,
+                                   max_prefix=max_prefix, device=device, lm_layout=lm_layout,
+                                   weight_layout=weight_layout)
+        M = self.drafter.max_nodes
+        self.total = batch * M
+        # an accepted path is at most the draft depth long
+        self.verifier = StackVerifier(dims, weights, layers, k_caches, v_caches, batch=batch,
+                                      max_total_nodes=self.total, max_nodes=M, max_prefix=max_prefix,
+                                      max_accept=params.depth, device=device, lm_layout=lm_layout,
+                                      weight_layout=weight_layout)
+        self.dkv = DraftKV(dims, weights, draft_weights, dk_cache, dv_cache, batch=batch, max_accept=params.depth,
+                           device=device, weight_layout=weight_layout)
+        self.feats = [self.verifier.next_feature, torch.zeros_like(self.verifier.next_feature)]
+        self.n = 0
+
+    def step(self, root_feature, root_token, prefix_len, timer=None):
+        d, v = self.drafter, self.verifier
+        v.next_feature = self.feats[self.n % 2]
+        if v.next_feature.data_ptr() == root_feature.data_ptr():
+            v.next_feature = self.feats[(self.n + 1) % 2]
+        self.n += 1
+        d.expand(root_feature, root_token, prefix_len, timer=timer)
+        v.encode(d.tree_off, d.parent, prefix_len, self.total)
+        v.verify(d.tree_off, d.tokens, prefix_len, self.total, timer=timer)
+        v.accept(d.tree_off, d.parent, d.tokens, prefix_len)
+        self.dkv.commit(v, d.tree_off, d.tokens, root_feature, prefix_len, timer=timer)
+        return v.next_feature, v.next_token
+
+
+class GreedyStackDecoder:
+    """Plain greedy decoding of a batch through the same layer stack and kernels: each step
+    verifies the one-node tree of every sequence's last token, commits its K/V in every layer
+    and emits its argmax.  step() returns the emitted tokens (device, [batch]), which are also
+    the next step's inputs."""
+
+    def __init__(self, dims, weights, layers, k_caches, v_caches, *, batch, max_prefix, device="cuda", lm_layout=0,
+                 weight_layout=0):
+        self.v = StackVerifier(dims, weights, layers, k_caches, v_caches, batch=batch, max_total_nodes=batch,
+                               max_nodes=1, max_prefix=max_prefix, max_accept=0, device=device, lm_layout=lm_layout,
+                               weight_layout=weight_layout)
+        self.B = batch
+        self.tree_off = torch.arange(batch + 1, dtype=torch.int32, device=device)
+        self.parent = torch.full((batch,), -1, dtype=torch.int32, device=device)
+        self.tokens = torch.zeros(batch, dtype=torch.int32, device=device)
+
+    def step(self, tokens, prefix_len, timer=None):
+        v = self.v
+        self.tokens.copy_(tokens)
+        v.encode(self.tree_off, self.parent, prefix_len, self.B)
+        v.verify(self.tree_off, self.tokens, prefix_len, self.B, timer=timer)
+        v.accept(self.tree_off, self.parent, self.tokens, prefix_len)
+        return v.next_token

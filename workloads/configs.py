@@ -314,16 +314,17 @@ class StackWorkload:
 
 
 def stack_workload(seed, dims: LayerDims, n_layers, *, batch=1, prefix=64, cache_cap=None, gamma_std=0.0,
-                   embed_std=0.02):
+                   embed_std=0.02, lm_std=0.02):
     """Seeded stack of n_layers random-init layers (layer 0 draws the same tensors as the
     single-layer workloads of this seed), prefix K/V N(0, 1) per layer, embedding
-    N(0, embed_std), a draft head, root features N(0, 1) and uniform root tokens."""
+    N(0, embed_std), LM head N(0, lm_std), a draft head, root features N(0, 1) and uniform
+    root tokens."""
     B = batch
     prefix_len = np.array(prefix if np.ndim(prefix) else [prefix] * B, dtype=np.int32)
     H, D, Hkv, V, t = dims.hidden, dims.head_dim, dims.n_kv_heads, dims.vocab, dims.dtype
     cap = cache_cap or int(prefix_len.max()) + 64
     layers = [layer_weights(seed, dims, gamma_std=gamma_std, tid_offset=LAYER_TID_STRIDE * l) for l in range(n_layers)]
-    weights = dict(w_lm=normal_tensor(seed, TID["w_lm"], (V, H), 0.02, t),
+    weights = dict(w_lm=normal_tensor(seed, TID["w_lm"], (V, H), lm_std, t),
                    embed=normal_tensor(seed, TID["embed"], (V, H), embed_std, t))
     if dims.rms_eps > 0:
         weights["final_ln"] = gain_vector(seed, TID["final_ln"], H, gamma_std, t)

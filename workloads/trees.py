@@ -169,3 +169,26 @@ def tree_tokens(rng, parent, vocab, root_token=None):
         for i, t in zip(ch, draw):
             tok[i] = int(t)
     return tok
+
+
+def planted_tree(rng, n, vocab, continuation, depth):
+    """A random recursive tree of n nodes with random tokens whose first node at ``depth``
+    carries ``continuation[0 .. depth-1]`` along its root path (siblings of a planted node
+    get other tokens); depth 0 plants nothing.  Returns (parent, tokens); the root's token
+    is left for the caller to set."""
+    par = random_tree(rng, n)
+    dep = depths(par)
+    toks = tree_tokens(rng, par, vocab)
+    cands = [i for i in range(n) if dep[i] == depth]
+    if depth > 0 and cands:
+        path = []
+        j = cands[0]
+        while j != -1:
+            path.append(j)
+            j = par[j]
+        for d, node in enumerate(path[::-1][1:], start=1):
+            toks[node] = int(continuation[d - 1])
+            for s in range(n):
+                if s != node and par[s] == par[node] and toks[s] == toks[node]:
+                    toks[s] = (toks[s] + 1) % vocab
+    return par, toks
