@@ -48,6 +48,13 @@ def parse():
                     help="temperature of the sampling-acceptance measurements (T > 0)")
     ap.add_argument("--eagle-only", action="store_true",
                     help="run only the full EAGLE step (for profiling its kernels apart from the verify step)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-loop comparison over a stack of layers (EAGLE vs plain greedy)")
+    ap.add_argument("--decode-only", action="store_true", help="run only the decode-loop comparison")
+    ap.add_argument("--decode-layers", type=int, default=32,
+                    help="target depth of the decode-loop comparison (32: the Llama-3-8B depth)")
+    ap.add_argument("--decode-steps", type=int, default=10)
+    ap.add_argument("--decode-batches", default="1,16")
     return ap.parse_args()
 
 
@@ -226,6 +233,147 @@ def bench_eagle_step(args):
         "data": "synthetic: random-init draft head and target layer N(0,0.02), root features N(0,1), "
                 "draft KV prefix N(0,1); the roots of each step are the previous step's bonus tokens",
     }
+
+
+def layer_bytes(dims):
+    """Weight bytes of one bf16 decoder layer (QKV, O, gate, up, down; gains ignored)."""
+    H, D, Hq, Hkv, F = dims.hidden, dims.head_dim, dims.n_q_heads, dims.n_kv_heads, dims.ffn
+    return 2 * (dims.qkv_rows * H + H * Hq * D + 3 * F * H)
+
+
+def bench_decode(args):
+    """A target of --decode-layers Llama-3-8B-shaped layers under the shared LM head, with a
+    2048-token prefix, decoded two ways through the same kernels at each batch of
+    --decode-batches:
+      plain greedy decoding: the one-node tree of each sequence's last token per step
+        (tree build -> verify through every layer -> accept + commit = the argmax);
+      EAGLE: draft (depth 6, top-10, frontier 10, 60 nodes) -> tree build -> verify of the
+        drafted nodes through every layer -> accept + commit every layer -> draft KV update
+        of the committed positions from the target's true features.
+    Both loops run on device without host synchronisation; the cache grows by the committed
+    tokens.  With random weights the drafts are not accepted (L = 0), so the measured
+    speedup is that of one token per step; the break-even accepted length and the speedup
+    projected at 3.5 and 4.5 tokens per step (the pages' typical accepted lengths) follow
+    from the two step times.  Weights and caches are drawn on the device with torch's
+    generator (N(0, 0.02) weights, N(0, 1) caches and features): the stack is 14 GB."""
+    import torch
+    import tree_attention_verification_06_amd as E
+    from tree_attention_verification_06_amd.runner import EagleStackStep, GreedyStackDecoder, with_packed_weights
+    from workloads import DraftParams
+    from workloads.configs import LLAMA8B
+
+    dims, nl, n = LLAMA8B, args.decode_layers, args.decode_steps
+    H, D, Hq, Hkv, F, V = dims.hidden, dims.head_dim, dims.n_q_heads, dims.n_kv_heads, dims.ffn, dims.vocab
+    p = DraftParams()
+    packed = args.weight_layout == "packed"
+    layout = 1 if packed else 0
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5000 if args.seed is None else args.seed)
+
+    def randn(*shape, std=0.02):
+        x = torch.empty(*shape, dtype=torch.bfloat16, device="cuda")
+        x.normal_(0.0, std, generator=gen)
+        return x
+
+    def ones():
+        return torch.ones(H, dtype=torch.bfloat16, device="cuda")
+
+    def layer():
+        w = dict(ln_attn=ones(), ln_mlp=ones(), w_qkv=randn(dims.qkv_rows, H), w_o=randn(H, Hq * D),
+                 w_gate=randn(F, H), w_up=randn(F, H), w_down=randn(H, F))
+        return with_packed_weights(w, lm_head=False) if packed else w
+
+    t0 = time.perf_counter()
+    layers = [layer() for _ in range(nl)]
+    head = dict(final_ln=ones(), w_lm=randn(V, H), embed=randn(V, H))
+    if packed:
+        head = with_packed_weights(head, layer=False)
+    dw = layer()
+    dw["w_fc"] = E.eagle_pack_fragments(randn(H, 2 * H)) if packed else randn(H, 2 * H)
+    torch.cuda.synchronize()
+    log(f"decode: {nl} layers drawn and laid out in {time.perf_counter() - t0:.1f}s")
+    P0 = 2048
+    warm = 3
+    cap = P0 + (warm + 2 * n + 4) * (p.depth + 1) + 16
+    stack_bytes = nl * layer_bytes(dims) + lm_head_bytes(dims, 1)
+    out = {"target": f"{nl} Llama-3-8B-shaped decoder layers + LM head (vocab {V})", "n_layers": nl,
+           "prefix": P0, "weight_layout": layout_name(args), "steps": n,
+           "draft": {"depth": p.depth, "top_k": p.top_k, "frontier": p.frontier, "max_nodes": p.max_nodes,
+                     "conf_threshold": p.conf_threshold},
+           "batches": {}}
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for B in [int(b) for b in args.decode_batches.split(",") if b]:
+        kc = randn(nl, B, Hkv, cap, D, std=1.0)
+        vc = randn(nl, B, Hkv, cap, D, std=1.0)
+        dkc = randn(B, Hkv, cap, D, std=1.0)
+        dvc = randn(B, Hkv, cap, D, std=1.0)
+        prefix = torch.full((B,), P0, dtype=torch.int32, device="cuda")
+        root_tok = torch.randint(0, V, (B,), dtype=torch.int32, device="cuda", generator=gen)
+        root_feat = torch.empty(B, H, dtype=torch.float32, device="cuda").normal_(0.0, 1.0, generator=gen)
+
+        # plain greedy decoding
+        dec = GreedyStackDecoder(dims, head, layers, kc, vc, batch=B, max_prefix=cap, lm_layout=layout,
+                                 weight_layout=layout)
+        tok = root_tok.clone()
+        for _ in range(warm):
+            tok = dec.step(tok, prefix).clone()
+        prefix.fill_(P0)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            tok = dec.step(tok, prefix)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_plain = e0.elapsed_time(e1) / n
+        if int(dec.v.status.item()) != 0:
+            raise RuntimeError(f"plain decode: device status {int(dec.v.status.item())}")
+        del dec
+
+        # EAGLE over the same stack
+        st = EagleStackStep(dims, p, head, layers, dw, kc, vc, dkc, dvc, batch=B, max_prefix=cap, lm_layout=layout,
+                            weight_layout=layout)
+        prefix.fill_(P0)
+        feat, tok = root_feat.clone(), root_tok.clone()
+        for _ in range(warm):
+            feat, tok = st.step(feat, tok, prefix)
+        prefix.fill_(P0)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            feat, tok = st.step(feat, tok, prefix)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_eagle = e0.elapsed_time(e1) / n
+        # accepted tokens per step (a separate pass that reads accept_len after each step)
+        acc = []
+        for _ in range(n):
+            feat, tok = st.step(feat, tok, prefix)
+            acc.append(int((st.verifier.accept_len + 1).sum().item()))
+        if int(st.verifier.status.item()) != 0:
+            raise RuntimeError(f"EAGLE decode: device status {int(st.verifier.status.item())}")
+        del st
+        acc_seq = float(np.mean(acc)) / B  # emitted tokens per sequence per step
+        kv_bytes = nl * B * Hkv * P0 * D * 2 * 2
+        roof_plain_ms = (stack_bytes + kv_bytes) / (HBM_PEAK_GBS * 1e9) * 1e3
+        out["batches"][str(B)] = {
+            "plain_ms_per_step": round(ms_plain, 4), "plain_tok_s": round(B / (ms_plain * 1e-3), 1),
+            "plain_roofline": {"bound": "hbm", "algorithmic_bytes": stack_bytes + kv_bytes,
+                               "t_roof_ms": round(roof_plain_ms, 4), "frac": round(roof_plain_ms / ms_plain, 4)},
+            "eagle_ms_per_step": round(ms_eagle, 4), "eagle_tokens_per_seq_step": round(acc_seq, 3),
+            "eagle_tok_s": round(acc_seq * B / (ms_eagle * 1e-3), 1),
+            "speedup_measured": round(acc_seq * ms_plain / ms_eagle, 3),
+            "break_even_tokens_per_step": round(ms_eagle / ms_plain, 3),
+            "projected_speedup": {str(tau): round(tau * ms_plain / ms_eagle, 3) for tau in (3.5, 4.5)},
+        }
+        log(f"decode B={B}: plain {ms_plain:.3f} ms/step, EAGLE {ms_eagle:.3f} ms/step, "
+            f"{acc_seq:.2f} tokens/seq/step")
+        del kc, vc, dkc, dvc
+        torch.cuda.empty_cache()
+    out["data"] = ("synthetic: random-init target stack, LM head, embedding and draft head N(0,0.02) drawn on the "
+                   "device; KV prefixes and root features N(0,1); each step's roots are the previous step's bonus "
+                   "tokens")
+    return out
 
 
 def bench_sampling(args, wl, st, t, prefix0, feat, tok):
@@ -437,6 +585,9 @@ def main():
     if args.eagle_only:
         print(json.dumps({"eagle_step": bench_eagle_step(args)}), flush=True)
         return
+    if args.decode_only:
+        print(json.dumps({"decode": bench_decode(args)}), flush=True)
+        return
     cfg = args.config
     extra = args.warmup + args.steps + 8
     t0 = time.perf_counter()
@@ -565,6 +716,9 @@ def main():
         del v, t
         torch.cuda.empty_cache()
         out["eagle_step"] = bench_eagle_step(args)
+    if not args.no_decode and dims.dtype == "bf16":
+        torch.cuda.empty_cache()
+        out["decode"] = bench_decode(args)
     if args.pmc_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
