@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define EAGLE_ABI_VERSION 6
+#define EAGLE_ABI_VERSION 7
 
 typedef enum {
   EAGLE_OK = 0,
@@ -107,11 +107,25 @@ typedef struct {
   int32_t layout;      /* 0 row-major, 1 fragment-blocked */
 } eagle_layer_w;
 
-/* KV cache geometry, in elements: element (b, h, t, d) is at
- * b*batch_stride + h*head_stride + t*token_stride + d. */
+/* KV cache geometry, in elements.
+ * Contiguous (block_table == NULL): element (b, h, t, d) is at
+ *   b*batch_stride + h*head_stride + t*token_stride + d.
+ * Paged (block_table != NULL), for continuous batching: the cache is a pool of n_pages
+ * pages of page_size token slots each, and sequence b owns the pages listed in
+ * block_table[b * max_blocks .. + max_blocks - 1] (device int32): element (b, h, t, d) is at
+ *   block_table[b*max_blocks + t/page_size]*batch_stride + h*head_stride
+ *     + (t % page_size)*token_stride + d,
+ * i.e. batch_stride is the page stride.  page_size must be a positive multiple of 64
+ * and capacity <= max_blocks * page_size (else EAGLE_ERR_ARG).  Pages may be shared by
+ * no two sequences that are written.  A page id outside [0, n_pages) is read as page
+ * n_pages - 1 or 0 (no fault; the values are meaningless) and is never written: a
+ * commit that would write through it sets *dev_status = EAGLE_ERR_ARG and skips that
+ * row.  The same table serves every layer of a stack (the layer stride moves the pool). */
 typedef struct {
   int64_t batch_stride, head_stride, token_stride;
   int32_t capacity; /* slots per (b, h) */
+  const int32_t* block_table;
+  int32_t page_size, max_blocks, n_pages;
 } eagle_cache_layout;
 
 /* Draft expansion parameters (readings of the pages' EAGLE-2 description). */

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert E.lib().eagle_abi_version() == 6
+    assert E.lib().eagle_abi_version() == 7
     assert E.status_str(0) == "ok"
     assert "workspace" in E.status_str(A.EAGLE_ERR_WORKSPACE)
 
@@ -257,3 +257,28 @@ def test_draft_kv_commit_host_errors():
     assert call(nbytes=ws_bytes - 1) == A.EAGLE_ERR_WORKSPACE
     assert call(dims=TINY) == A.EAGLE_ERR_UNSUPPORTED
     assert call(dims=replace(LLAMA8B, head_dim=64)) == A.EAGLE_ERR_UNSUPPORTED
+
+
+def test_paged_cache_layout_host_errors():
+    """A block table needs a page size that is a positive multiple of 64, positive
+    max_blocks and n_pages, and capacity <= max_blocks * page_size."""
+    cases = [(dict(), A.EAGLE_OK), (dict(page_size=48), A.EAGLE_ERR_ARG), (dict(page_size=0), A.EAGLE_ERR_ARG),
+             (dict(max_blocks=0), A.EAGLE_ERR_ARG), (dict(n_pages=0), A.EAGLE_ERR_ARG),
+             (dict(capacity=64 * 33), A.EAGLE_ERR_ARG)]
+    L = E.lib()
+    d = A.dims_struct(LLAMA8B)
+    lw = A.EagleLayerW(4096, 4096, 4096, 4096, 4096, 4096, 4096, 0)
+    for kw, want in cases:
+        f = dict(capacity=64 * 32, page_size=64, max_blocks=32, n_pages=100)
+        f.update(kw)
+        cl = A.EagleCacheLayout(1 << 20, 1 << 13, 128, f["capacity"], 4096, f["page_size"], f["max_blocks"],
+                                f["n_pages"])
+        # a workspace that is too small: a valid layout gets as far as the workspace check
+        st = L.eagle_tree_verify(ctypes.byref(d), ctypes.byref(lw), FAKE, FAKE, 1, FAKE, 60, 60, FAKE, None, None, FAKE,
+                                 1, FAKE, FAKE, 2048, FAKE, FAKE, ctypes.byref(cl), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                 None, ctypes.c_void_p(1 << 20), 16, None, None)
+        assert st == (A.EAGLE_ERR_WORKSPACE if want == A.EAGLE_OK else want), (kw, st)
+        st = L.eagle_accept_commit(1, FAKE, 60, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(cl),
+                                   8, 128, 0, FAKE, None, 4096, None, 16, FAKE, FAKE, FAKE, FAKE, None, None)
+        if want != A.EAGLE_OK:
+            assert st == want, (kw, st)

@@ -1,0 +1,314 @@
+"""Paged KV caches (continuous batching) on the GPU, through the C ABI: every call that
+reads or writes a cache gives bit-identical results whether the cache is contiguous or a
+pool of pages addressed through a block table (the same arithmetic in the same order; only
+the addresses differ), commits land in the right pages and nowhere else, a sequence that
+joins a running batch can reuse the pages of one that left, and a bad page id is refused
+on the device instead of being written through."""
+import numpy as np
+import pytest
+
+from workloads import DraftParams, make_workload, mini_dims, stack_workload, trees as T
+from workloads.configs import TID, normal_tensor
+from workloads.device import to_tensor, upload
+
+pytestmark = pytest.mark.gpu
+
+PS = 64
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def _to_pages(cache, pages, table, cap):
+    """Copy a contiguous cache [B][Hkv][cap][D] into the pages its table rows name."""
+    tb = table.cpu().numpy()
+    for b in range(tb.shape[0]):
+        for blk, pg in enumerate(tb[b]):
+            t0 = blk * PS
+            if pg < 0 or t0 >= cap:
+                continue
+            t1 = min(t0 + PS, cap)
+            pages[pg, :, :t1 - t0] = cache[b, :, t0:t1]
+
+
+def _from_pages(pages, table, cap):
+    tb = table.cpu().numpy()
+    B = tb.shape[0]
+    out = pages.new_zeros((B, pages.shape[1], cap, pages.shape[3]))
+    for b in range(B):
+        for blk, pg in enumerate(tb[b]):
+            t0 = blk * PS
+            if pg < 0 or t0 >= cap:
+                continue
+            t1 = min(t0 + PS, cap)
+            out[b, :, t0:t1] = pages[pg, :, :t1 - t0]
+    return out
+
+
+def _pool(shape_cache, n_pages, seed, dtype=None):
+    """A page pool [n_pages][Hkv][PS][D] of random values (unowned pages must stay so)."""
+    import torch
+    B, Hkv, cap, D = shape_cache
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    p = torch.empty(n_pages, Hkv, PS, D, dtype=dtype or torch.bfloat16, device="cuda")
+    p.normal_(0, 1, generator=g)
+    return p
+
+
+def _tables(B, cap, n_pages, seed):
+    """Block tables of B sequences over a shuffled pool with spare pages."""
+    import torch
+    maxb = -(-cap // PS)
+    perm = np.random.default_rng(seed).permutation(n_pages)[:B * maxb].reshape(B, maxb)
+    return torch.tensor(perm, dtype=torch.int32, device="cuda"), maxb
+
+
+def test_paged_verify_and_commit_bit_identical():
+    import torch
+    from tree_attention_verification_06_amd._abi import PagedCache
+    from tree_attention_verification_06_amd.runner import TreeVerifier
+    dims = mini_dims()
+    parents = [T.static_tree_60(), T.random_tree(np.random.default_rng(3), 25), T.chain(10)]
+    wl = make_workload(2, seed=31, dims=dims, batch=3, prefix=[200, 77, 130], parents=parents)
+    t = upload(wl)
+    M, cap = wl.n_nodes, wl.cache_cap
+    table, maxb = _tables(3, cap, 3 * (-(-cap // PS)) + 5, 31)
+    n_pages = 3 * maxb + 5
+    kp, vp = _pool(t["k_cache"].shape, n_pages, 1), _pool(t["k_cache"].shape, n_pages, 2)
+    _to_pages(t["k_cache"], kp, table, cap)
+    _to_pages(t["v_cache"], vp, table, cap)
+    owned = set(table.flatten().tolist())
+    spare = [p for p in range(n_pages) if p not in owned]
+    kp0 = kp.clone()
+    plen_c, plen_p = t["prefix_len"].clone(), t["prefix_len"].clone()
+    vc = TreeVerifier(dims, t["weights"], t["k_cache"], t["v_cache"], batch=3, max_total_nodes=M, max_nodes=60,
+                      max_prefix=cap)
+    vpg = TreeVerifier(dims, t["weights"], PagedCache(kp, table, PS), PagedCache(vp, table, PS), batch=3,
+                       max_total_nodes=M, max_nodes=60, max_prefix=cap)
+    for v, pl in ((vc, plen_c), (vpg, plen_p)):
+        v.encode(t["tree_off"], t["parent"], pl, M)
+        v.verify(t["tree_off"], t["tokens"], pl, M, x=t["x"])
+    torch.cuda.synchronize()
+    for k in ("h", "argmax", "maxlogit", "k_tree", "v_tree"):
+        assert torch.equal(getattr(vc, k), getattr(vpg, k)), k
+    # plant a depth-3 path in tree 0 from the GPU's argmax (node inputs are given, so tokens
+    # do not change the target's choices), then accept and commit in both layouts
+    g = vc.argmax.cpu().numpy()
+    tok = wl.tokens.copy()
+    dep = T.depths(parents[0])
+    j = [i for i in range(60) if dep[i] == 3][0]
+    while j > 0:
+        tok[j] = g[parents[0][j]]
+        j = parents[0][j]
+    tt = to_tensor(tok)
+    for v, pl in ((vc, plen_c), (vpg, plen_p)):
+        v.accept(t["tree_off"], t["parent"], tt, pl)
+    torch.cuda.synchronize()
+    assert int(vc.status.item()) == 0 and int(vpg.status.item()) == 0
+    assert int(vc.accept_len[0]) >= 3
+    for k in ("accept_len", "path", "out_tokens", "next_token", "next_feature"):
+        assert torch.equal(getattr(vc, k), getattr(vpg, k)), k
+    assert torch.equal(plen_c, plen_p)
+    assert torch.equal(_from_pages(kp, table, cap), t["k_cache"])
+    assert torch.equal(_from_pages(vp, table, cap), t["v_cache"])
+    assert torch.equal(kp[spare], kp0[spare])
+
+
+def test_paged_stack_and_draft_kv_bit_identical():
+    import torch
+    from tree_attention_verification_06_amd._abi import PagedCache
+    from tree_attention_verification_06_amd.runner import DraftKV, StackVerifier
+    dims = mini_dims()
+    wl = stack_workload(12, dims, 2, batch=2, prefix=[200, 77], cache_cap=256, embed_std=1.0, lm_std=0.2)
+    tt = lambda a: to_tensor(a)  # noqa: E731
+    w = {k: tt(v) for k, v in wl.weights.items()}
+    layers = [{k: tt(v) for k, v in lw.items()} for lw in wl.layers]
+    dw = {k: tt(v) for k, v in wl.draft_weights.items()}
+    kc, vc_, dkc, dvc = tt(wl.k_caches), tt(wl.v_caches), tt(wl.dk_cache), tt(wl.dv_cache)
+    table, maxb = _tables(2, 256, 2 * 4 + 3, 12)
+    n_pages = 2 * maxb + 3
+    kpool = torch.stack([_pool(kc[l].shape, n_pages, 10 + l) for l in range(2)])
+    vpool = torch.stack([_pool(kc[l].shape, n_pages, 20 + l) for l in range(2)])
+    for l in range(2):
+        _to_pages(kc[l], kpool[l], table, 256)
+        _to_pages(vc_[l], vpool[l], table, 256)
+    dkp, dvp = _pool(dkc.shape, n_pages, 30), _pool(dkc.shape, n_pages, 31)
+    _to_pages(dkc, dkp, table, 256)
+    _to_pages(dvc, dvp, table, 256)
+    rng = np.random.default_rng(12)
+    parents = [T.static_tree_60(), T.random_tree(rng, 25)]
+    sizes = [len(p) for p in parents]
+    off = tt(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32))
+    par = tt(np.concatenate([np.asarray(p, dtype=np.int32) for p in parents]))
+    tok = tt(np.concatenate([T.tree_tokens(rng, p, dims.vocab) for p in parents]).astype(np.int32))
+    M = sum(sizes)
+    plen_c, plen_p = tt(wl.prefix_len), tt(wl.prefix_len)
+    root = tt(wl.root_feature)
+    runs = []
+    for paged in (False, True):
+        K = PagedCache(kpool, table, PS) if paged else kc
+        V = PagedCache(vpool, table, PS) if paged else vc_
+        DK = PagedCache(dkp, table, PS) if paged else dkc
+        DV = PagedCache(dvp, table, PS) if paged else dvc
+        pl = plen_p if paged else plen_c
+        v = StackVerifier(dims, w, layers, K, V, batch=2, max_total_nodes=M, max_nodes=60, max_prefix=256)
+        dkv = DraftKV(dims, w, dw, DK, DV, batch=2, max_accept=v.max_accept)
+        v.encode(off, par, pl, M)
+        v.verify(off, tok, pl, M)
+        v.accept(off, par, tok, pl)
+        dkv.commit(v, off, tok, root, pl)
+        torch.cuda.synchronize()
+        assert int(v.status.item()) == 0
+        runs.append(v)
+    a, b = runs
+    for k in ("h", "argmax", "k_tree", "v_tree", "accept_len", "path", "next_feature"):
+        assert torch.equal(getattr(a, k), getattr(b, k)), k
+    for l in range(2):
+        assert torch.equal(_from_pages(kpool[l], table, 256), kc[l])
+        assert torch.equal(_from_pages(vpool[l], table, 256), vc_[l])
+    assert torch.equal(_from_pages(dkp, table, 256), dkc)
+    assert torch.equal(_from_pages(dvp, table, 256), dvc)
+
+
+def test_paged_draft_expand_bit_identical():
+    import torch
+    from tree_attention_verification_06_amd._abi import PagedCache
+    from tree_attention_verification_06_amd.runner import TreeDrafter
+    dims = mini_dims()
+    p = DraftParams(depth=3, top_k=4, frontier=4, max_nodes=16)
+    wl = make_workload(5, seed=41, dims=dims, batch=2, prefix=[200, 77], draft=p)
+    t = upload(wl)
+    cap = wl.cache_cap
+    table, maxb = _tables(2, cap, 2 * (-(-cap // PS)) + 2, 41)
+    n_pages = 2 * maxb + 2
+    dkp, dvp = _pool(t["dk_cache"].shape, n_pages, 5), _pool(t["dk_cache"].shape, n_pages, 6)
+    _to_pages(t["dk_cache"], dkp, table, cap)
+    _to_pages(t["dv_cache"], dvp, table, cap)
+    outs = []
+    for DK, DV in ((t["dk_cache"], t["dv_cache"]), (PagedCache(dkp, table, PS), PagedCache(dvp, table, PS))):
+        d = TreeDrafter(dims, p, t["weights"], t["draft_weights"], DK, DV, batch=2, max_prefix=cap)
+        d.expand(t["root_feature"], t["root_token"], t["prefix_len"])
+        torch.cuda.synchronize()
+        outs.append((d.tree_off.clone(), d.parent.clone(), d.tokens.clone(), d.cum.clone()))
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+
+
+def test_continuous_batching_reuses_pages():
+    """Step 1 verifies {A, B}; A leaves and C joins on A's freed pages; step 2 verifies
+    {B, C} on the paged pool and must equal a contiguous run of the same batch, whose caches
+    hold B after step 1 and C's prefix."""
+    import torch
+    from tree_attention_verification_06_amd.runner import PagePool, TreeVerifier
+    dims = mini_dims()
+    cap = 320
+    seqs = {}
+    for name, seed, P in (("A", 51, 200), ("B", 52, 77), ("C", 53, 130)):
+        wl = make_workload(2, seed=seed, dims=dims, batch=1, prefix=[P],
+                           parents=[T.random_tree(np.random.default_rng(seed), 20)])
+        seqs[name] = wl
+    w = upload(seqs["A"])["weights"]  # one model for every sequence
+    pool = PagePool(n_pages=10, page_size=PS, max_blocks=cap // PS)
+    Hkv, D = dims.n_kv_heads, dims.head_dim
+    kpool = torch.zeros(10, Hkv, PS, D, dtype=torch.bfloat16, device="cuda")
+    vpool = torch.zeros_like(kpool)
+
+    def admit(name):
+        wl = seqs[name]
+        pool.reserve(name, int(wl.prefix_len[0]) + 32)
+        tb = pool.table([name])
+        src_k, src_v = to_tensor(wl.k_cache), to_tensor(wl.v_cache)
+        n = min(src_k.shape[2], len(pool.owned[name]) * PS)
+        _to_pages(src_k[:, :, :n], kpool, tb, n)
+        _to_pages(src_v[:, :, :n], vpool, tb, n)
+
+    def step(names, caches, plen):
+        wls = [seqs[n] for n in names]
+        parents = [wl.parents[0] for wl in wls]
+        sizes = [len(p) for p in parents]
+        M = sum(sizes)
+        off = to_tensor(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32))
+        par = to_tensor(np.concatenate([np.asarray(p, dtype=np.int32) for p in parents]))
+        tok = to_tensor(np.concatenate([wl.tokens for wl in wls]).astype(np.int32))
+        x = to_tensor(np.concatenate([wl.x for wl in wls]))
+        v = TreeVerifier(dims, w, caches[0], caches[1], batch=len(names), max_total_nodes=M, max_nodes=20,
+                         max_prefix=cap)
+        v.encode(off, par, plen, M)
+        v.verify(off, tok, plen, M, x=x)
+        v.accept(off, par, tok, plen)
+        torch.cuda.synchronize()
+        assert int(v.status.item()) == 0
+        return v
+
+    admit("A")
+    admit("B")
+    tb1 = pool.table(["A", "B"])
+    plen1 = to_tensor(np.array([200, 77], dtype=np.int32))
+    step(["A", "B"], (pool.paged(kpool, tb1), pool.paged(vpool, tb1)), plen1)
+    a_pages = list(pool.owned["A"])
+    pool.release("A")
+    admit("C")
+    assert set(pool.owned["C"]) & set(a_pages), "C should reuse pages A released"
+    tb2 = pool.table(["B", "C"])
+    plen2 = to_tensor(np.array([int(plen1[1]), 130], dtype=np.int32))
+    # contiguous reference of the same batch: B's cache after step 1 and C's prefix
+    kc = _from_pages(kpool, tb2, cap)
+    vc = _from_pages(vpool, tb2, cap)
+    plen2c = plen2.clone()
+    vp = step(["B", "C"], (pool.paged(kpool, tb2), pool.paged(vpool, tb2)), plen2)
+    vcnt = step(["B", "C"], (kc, vc), plen2c)
+    for k in ("h", "argmax", "k_tree", "accept_len", "path", "next_token"):
+        assert torch.equal(getattr(vp, k), getattr(vcnt, k)), k
+    assert torch.equal(plen2, plen2c)
+    assert torch.equal(_from_pages(kpool, tb2, cap), kc)
+    _log("continuous batching: C reused pages", sorted(set(pool.owned["C"]) & set(a_pages)))
+
+
+def test_bad_page_id_is_refused_not_written():
+    import torch
+    from tree_attention_verification_06_amd._abi import EAGLE_ERR_ARG, PagedCache
+    from tree_attention_verification_06_amd.runner import TreeVerifier
+    dims = mini_dims()
+    wl = make_workload(2, seed=61, dims=dims, batch=1, prefix=[100], parents=[T.chain(5)])
+    t = upload(wl)
+    cap = 128
+    n_pages = 6
+    kp = torch.zeros(n_pages, dims.n_kv_heads, PS, dims.head_dim, dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    # tokens 0..63 in page 3; the committed slots 100.. fall in block 1, whose id is invalid
+    table = torch.tensor([[3, n_pages + 7]], dtype=torch.int32, device="cuda")
+    v = TreeVerifier(dims, t["weights"], PagedCache(kp, table, PS), PagedCache(vp, table, PS), batch=1,
+                     max_total_nodes=5, max_nodes=5, max_prefix=cap)
+    v.encode(t["tree_off"], t["parent"], t["prefix_len"], 5)
+    v.verify(t["tree_off"], t["tokens"], t["prefix_len"], 5, x=t["x"])
+    v.accept(t["tree_off"], t["parent"], t["tokens"], t["prefix_len"])
+    torch.cuda.synchronize()
+    assert int(v.status.item()) == EAGLE_ERR_ARG
+    others = [p for p in range(n_pages) if p != 3]
+    assert not kp[others].any() and not vp[others].any()
+
+
+def test_paged_fp32_layer_bit_identical():
+    """The fp32 attention-only layer (VALU attention) on a paged cache."""
+    import torch
+    from tree_attention_verification_06_amd._abi import PagedCache
+    from tree_attention_verification_06_amd.runner import TreeVerifier
+    wl = make_workload(1, seed=71)
+    t = upload(wl)
+    M, cap = wl.n_nodes, wl.cache_cap
+    table, maxb = _tables(1, cap, -(-cap // PS) + 3, 71)
+    n_pages = maxb + 3
+    kp = _pool(t["k_cache"].shape, n_pages, 7, torch.float32)
+    vp = _pool(t["k_cache"].shape, n_pages, 8, torch.float32)
+    _to_pages(t["k_cache"], kp, table, cap)
+    _to_pages(t["v_cache"], vp, table, cap)
+    outs = []
+    for K, V in ((t["k_cache"], t["v_cache"]), (PagedCache(kp, table, PS), PagedCache(vp, table, PS))):
+        v = TreeVerifier(wl.dims, t["weights"], K, V, batch=1, max_total_nodes=M, max_nodes=M, max_prefix=cap)
+        v.step(t["tree_off"], t["parent"], t["tokens"], t["prefix_len"].clone(), M, x=t["x"])
+        torch.cuda.synchronize()
+        outs.append(v)
+    for k in ("h", "argmax", "maxlogit", "k_tree"):
+        assert torch.equal(getattr(outs[0], k), getattr(outs[1], k)), k

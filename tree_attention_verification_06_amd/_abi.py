@@ -46,7 +46,36 @@ class EagleLayerW(ctypes.Structure):
 
 class EagleCacheLayout(ctypes.Structure):
     _fields_ = [("batch_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
-                ("token_stride", ctypes.c_int64), ("capacity", ctypes.c_int32)]
+                ("token_stride", ctypes.c_int64), ("capacity", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("page_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("n_pages", ctypes.c_int32)]
+
+
+class PagedCache:
+    """A paged KV cache, accepted wherever a cache tensor is: pages [n_pages][Hkv][page_size][D]
+    (or [n_layers][n_pages][Hkv][page_size][D] for a stack of layers) addressed through
+    block_table [B][max_blocks] (device int32 page ids).  Sequence b's token t lives in page
+    block_table[b][t // page_size] at slot t % page_size; capacity = max_blocks * page_size."""
+
+    def __init__(self, pages, block_table, page_size):
+        self.pages = pages
+        self.block_table = block_table
+        self.page_size = int(page_size)
+        if pages.shape[-2] != self.page_size:
+            raise EagleError(EAGLE_ERR_ARG, "PagedCache: pages must be [..][n_pages][Hkv][page_size][D]")
+
+    @property
+    def shape(self):
+        return self.pages.shape
+
+    def stride(self, i):
+        return self.pages.stride(i)
+
+    def data_ptr(self):
+        return self.pages.data_ptr()
+
+    def __getitem__(self, layer):
+        return PagedCache(self.pages[layer], self.block_table, self.page_size)
 
 
 class EagleDraftParams(ctypes.Structure):
@@ -157,10 +186,15 @@ def layer_struct(w, layout=0):
 
 
 def cache_struct(cache):
-    """EagleCacheLayout of a contiguous [B][Hkv][cap][D] tensor."""
+    """EagleCacheLayout of a contiguous [B][Hkv][cap][D] tensor or of a PagedCache."""
+    if isinstance(cache, PagedCache):
+        n_pages, Hkv, ps, D = cache.pages.shape
+        s = cache.pages.stride()
+        maxb = cache.block_table.shape[1]
+        return EagleCacheLayout(s[0], s[1], s[2], maxb * ps, cache.block_table.data_ptr(), ps, maxb, n_pages)
     B, Hkv, cap, D = cache.shape
     s = cache.stride()
-    return EagleCacheLayout(s[0], s[1], s[2], cap)
+    return EagleCacheLayout(s[0], s[1], s[2], cap, None, 0, 0, 0)
 
 
 def draft_params_struct(p):

@@ -212,8 +212,7 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* layers, int n_layers, 
     if (norm && (!lw->ln_attn || !lw->ln_mlp || !lw->w_gate || !lw->w_up || !lw->w_down)) return EAGLE_ERR_ARG;
   }
   if (((uintptr_t)ws) & 255) return EAGLE_ERR_ARG;
-  if (cache->token_stride % 8 || cache->head_stride % 8 || cache->batch_stride % 8 || cache->capacity < 0)
-    return EAGLE_ERR_ARG;
+  if (check_cache_layout(cache)) return EAGLE_ERR_ARG;
   const VerifyLayout L = plan_verify(d, B, total_nodes, max_nodes, max_prefix, so != nullptr);
   if (ws_bytes < L.total) return EAGLE_ERR_WORKSPACE;
   char* w = (char*)ws;
@@ -320,6 +319,10 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* layers, int n_layers, 
     a.ch = cache->head_stride;
     a.ct = cache->token_stride;
     a.cap = cache->capacity;
+    a.table = cache->block_table;
+    a.ps = cache->page_size;
+    a.maxb = cache->max_blocks;
+    a.npages = cache->n_pages;
     a.k_tree = k_tree_l;
     a.v_tree = v_tree_l;
     a.anc = anc;
@@ -519,6 +522,7 @@ int commit_args(AcceptArgs& a, int batch, const int32_t* tree_off, int max_nodes
   if (n_kv_heads < 1 || head_dim < 1 || (head_dim * es) % 16) return EAGLE_ERR_UNSUPPORTED;
   if ((cache->token_stride * es) % 16 || (cache->head_stride * es) % 16 || (cache->batch_stride * es) % 16)
     return EAGLE_ERR_ARG;
+  if (check_cache_layout(cache) && cache->block_table) return EAGLE_ERR_ARG;
   if (next_feature && (!h_nodes || hidden < 1 || hidden % 4)) return EAGLE_ERR_ARG;
   a.tree_off = tree_off;
   a.parent = parent;
@@ -527,10 +531,8 @@ int commit_args(AcceptArgs& a, int batch, const int32_t* tree_off, int max_nodes
   a.v_tree = v_tree;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
-  a.cb = cache->batch_stride;
-  a.ch = cache->head_stride;
-  a.ct = cache->token_stride;
   a.capacity = cache->capacity;
+  a.cv = cache_view(cache);
   a.hkv = n_kv_heads;
   a.hd = head_dim;
   a.elem = es;

@@ -11,8 +11,10 @@ struct AttnArgs {
   const void* q;         // [sum N][hq][hd]
   const void* k_cache;   // cache layout below
   const void* v_cache;
-  int64_t cb, ch, ct;    // cache strides (elements)
+  int64_t cb, ch, ct;    // cache strides (elements); cb is the page stride when paged
   int cap;               // cache slots per (b, h); prefix lengths are clamped to it
+  const int32_t* table;  // paged cache: block table [B][maxb] (nullptr: contiguous)
+  int ps, maxb, npages;  // page size, table entries per sequence, pages in the pool
   const void* k_tree;    // [sum N][hkv][hd]
   const void* v_tree;
   const uint64_t* anc;   // [sum N][mw]

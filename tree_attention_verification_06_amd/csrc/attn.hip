@@ -50,6 +50,9 @@ __device__ __forceinline__ int remap_xcd(int b, int total) {
   return (b % kXcds) * per + b / kXcds;
 }
 
+// PAGED: the cache is a page pool addressed through a.table (see CacheView); the
+// contiguous instantiation is unchanged code.
+template <bool PAGED>
 __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, int grid_real) {
   __shared__ __align__(16) bf16 ks[2][KT * KS];
   __shared__ __align__(16) bf16 vs[2][KT * VS];
@@ -126,8 +129,10 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
   // scores in log2 units: q.k / sqrt(128) * log2(e)
   const float sl2 = 0.08838834764831845f * 1.4426950408889634f;
 
-  const bf16* kc = (const bf16*)a.k_cache + (int64_t)b * a.cb + (int64_t)kvh * a.ch;
-  const bf16* vc = (const bf16*)a.v_cache + (int64_t)b * a.cb + (int64_t)kvh * a.ch;
+  // contiguous: the (b, kv head) row base; paged: the kv head's offset within a page
+  const int64_t cbase = (PAGED ? 0 : (int64_t)b * a.cb) + (int64_t)kvh * a.ch;
+  const bf16* kc = (const bf16*)a.k_cache + cbase;
+  const bf16* vc = (const bf16*)a.v_cache + cbase;
   const bf16* kt_base = (const bf16*)a.k_tree + ((int64_t)off * a.hkv + kvh) * HD;
   const bf16* vt_base = (const bf16*)a.v_tree + ((int64_t)off * a.hkv + kvh) * HD;
   const int64_t tree_stride = (int64_t)a.hkv * HD;
@@ -144,8 +149,15 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
       const int i = tid + u * NWA * 64;
       const int key = min(kt0 + (i >> 4), k1 - 1);
       const int gd = i & 15;
-      const bf16* kp = tree_chunk ? kt_base + key * tree_stride : kc + key * a.ct;
-      const bf16* vp = tree_chunk ? vt_base + key * tree_stride : vc + key * a.ct;
+      int64_t coff = (int64_t)key * a.ct;
+      if constexpr (PAGED) {
+        // tree chunks never consult the table (their keys are node indices)
+        const CacheView cv{a.cb, a.ch, a.ct, a.table, a.ps, a.maxb, a.npages};
+        bool ok;
+        coff = cache_offset(cv, b, kvh, tree_chunk ? 0 : key, ok) - (int64_t)kvh * a.ch;
+      }
+      const bf16* kp = tree_chunk ? kt_base + key * tree_stride : kc + coff;
+      const bf16* vp = tree_chunk ? vt_base + key * tree_stride : vc + coff;
       kreg[slot][u] = *(const uint4*)(kp + gd * 8);
       vreg[slot][u] = *(const uint4*)(vp + gd * 8);
     }
@@ -362,8 +374,13 @@ __global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnArgs a) {
   const float* q = (const float*)a.q + ((int64_t)node_g * hq + h) * hd;
   for (int d = lane; d < hd; d += 64) qs[d] = q[d];
   __syncthreads();
-  const float* kc = (const float*)a.k_cache + (int64_t)b * a.cb + (int64_t)kvh * a.ch;
-  const float* vc = (const float*)a.v_cache + (int64_t)b * a.cb + (int64_t)kvh * a.ch;
+  const CacheView cv{a.cb, a.ch, a.ct, a.table, a.ps, a.maxb, a.npages};
+  auto coff = [&](int t) {
+    bool ok;
+    return cache_offset(cv, b, kvh, t, ok);
+  };
+  const float* kc = (const float*)a.k_cache;
+  const float* vc = (const float*)a.v_cache;
   const float* ktr = (const float*)a.k_tree;
   const float* vtr = (const float*)a.v_tree;
   const float scale = rsqrtf((float)hd);
@@ -372,7 +389,7 @@ __global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnArgs a) {
     float s = -INFINITY;
     const float* kp = nullptr;
     if (j < P) {
-      kp = kc + (int64_t)j * a.ct;
+      kp = kc + coff(j);
     } else {
       const int jn = j - P;
       const uint64_t word = a.anc[(int64_t)(off + i) * a.mw + (jn >> 6)];
@@ -400,7 +417,7 @@ __global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnArgs a) {
     for (int j = 0; j < P + N; ++j) {
       const float p = sc[j];
       if (p == 0.f) continue;
-      const float* vp = j < P ? vc + (int64_t)j * a.ct : vtr + ((int64_t)(off + j - P) * a.hkv + kvh) * hd;
+      const float* vp = j < P ? vc + coff(j) : vtr + ((int64_t)(off + j - P) * a.hkv + kvh) * hd;
       acc += p * vp[d];
     }
     const float out = acc / sum;
@@ -453,7 +470,10 @@ int launch_attn(AttnArgs& a, const AttnPlan& p, eagle_timer* timer, hipStream_t 
   const int grid = a.batch * a.hkv * p.n_chunks * p.row_groups;
   const int padded = (grid + kXcds - 1) / kXcds * kXcds;
   timer_begin(timer, ST_ATTN, s);
-  hipLaunchKernelGGL(tree_attn_bf16_kernel, dim3(padded), dim3(NWA * 64), 0, s, a, grid);
+  if (a.table)
+    hipLaunchKernelGGL(tree_attn_bf16_kernel<true>, dim3(padded), dim3(NWA * 64), 0, s, a, grid);
+  else
+    hipLaunchKernelGGL(tree_attn_bf16_kernel<false>, dim3(padded), dim3(NWA * 64), 0, s, a, grid);
   timer_end(timer, s);
   const int g = a.hq / a.hkv;
   const int mgrid = a.batch * a.hkv * ((a.max_nodes * g + 1) / 2);

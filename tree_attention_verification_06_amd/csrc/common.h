@@ -84,6 +84,44 @@ __device__ __forceinline__ void group_sum_n(float (&v)[N]) {
   }
 }
 
+// Cache addressing shared by every kernel that reads or writes a KV cache: contiguous
+// (table == nullptr: b*cb + h*ch + t*ct) or paged (the page table[b*maxb + t/ps], then
+// page*cb + h*ch + (t%ps)*ct; cb is the page stride).  Elements, not bytes.
+struct CacheView {
+  int64_t cb, ch, ct;
+  const int32_t* table;
+  int ps, maxb, npages;
+};
+// Offset of (b, h, t); a page id outside [0, npages) gives ok = false and the offset of
+// a valid page (so a read stays in bounds; writers must skip the row).
+__device__ __forceinline__ int64_t cache_offset(const CacheView& c, int b, int h, int t, bool& ok) {
+  ok = true;
+  if (!c.table) return (int64_t)b * c.cb + (int64_t)h * c.ch + (int64_t)t * c.ct;
+  int pg = c.table[(int64_t)b * c.maxb + t / c.ps];
+  if (pg < 0 || pg >= c.npages) {
+    ok = false;
+    pg = pg < 0 ? 0 : c.npages - 1;
+  }
+  return (int64_t)pg * c.cb + (int64_t)h * c.ch + (int64_t)(t % c.ps) * c.ct;
+}
+
+// Host: argument check of a cache layout whose element size divides 16 bytes into 8
+// elements or fewer (strides in multiples of 8 elements keep every 16-byte access
+// aligned for bf16 and f32 alike), and the paging fields when a block table is given.
+inline int check_cache_layout(const eagle_cache_layout* c) {
+  if (!c) return EAGLE_ERR_ARG;
+  if (c->token_stride % 8 || c->head_stride % 8 || c->batch_stride % 8 || c->capacity < 0) return EAGLE_ERR_ARG;
+  if (c->block_table) {
+    if (c->page_size <= 0 || c->page_size % 64 || c->max_blocks <= 0 || c->n_pages <= 0) return EAGLE_ERR_ARG;
+    if ((int64_t)c->capacity > (int64_t)c->max_blocks * c->page_size) return EAGLE_ERR_ARG;
+  }
+  return EAGLE_OK;
+}
+inline CacheView cache_view(const eagle_cache_layout* c) {
+  return CacheView{c->batch_stride, c->head_stride, c->token_stride, c->block_table,
+                   c->block_table ? c->page_size : 1, c->max_blocks, c->n_pages};
+}
+
 // Per-launch HIP event timing (optional).
 struct Timer;
 void timer_begin(eagle_timer* t, int stage, hipStream_t s);

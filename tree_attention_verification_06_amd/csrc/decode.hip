@@ -77,7 +77,7 @@ struct DkvArgs {
   const bf16* v;
   bf16* dk_cache;
   bf16* dv_cache;
-  int64_t cb, ch, ct;
+  CacheView cv;
   int cap;
   int32_t* status;
 };
@@ -120,13 +120,18 @@ __global__ __launch_bounds__(256) void draft_kv_scatter_kernel(DkvArgs a) {
     if (threadIdx.x == 0) set_status(a.status, EAGLE_ERR_CAPACITY);
     return;
   }
+  bool ok;
+  const int64_t row0 = cache_offset(a.cv, b, 0, slot, ok);  // the slot's offset at head 0
+  if (!ok) {
+    if (threadIdx.x == 0) set_status(a.status, EAGLE_ERR_ARG);
+    return;
+  }
   const int chunks = a.hd / 8;
   const int per = a.hkv * chunks;
   for (int i = threadIdx.x; i < 2 * per; i += blockDim.x) {
     const int which = i / per, j = i % per, h = j / chunks, c = j % chunks;
     const uint4 v = *(const uint4*)((which ? a.v : a.k) + ((int64_t)r * a.hkv + h) * a.hd + c * 8);
-    *(uint4*)((which ? a.dv_cache : a.dk_cache) + (int64_t)b * a.cb + (int64_t)h * a.ch + (int64_t)slot * a.ct +
-              c * 8) = v;
+    *(uint4*)((which ? a.dv_cache : a.dk_cache) + row0 + (int64_t)h * a.cv.ch + c * 8) = v;
   }
 }
 
@@ -157,8 +162,7 @@ int draft_kv_commit_impl(const eagle_dims* d, const void* w_fc, const eagle_laye
     return EAGLE_ERR_ARG;
   if (lw->layout != 0 && lw->layout != 1) return EAGLE_ERR_ARG;
   if (((uintptr_t)ws) & 255) return EAGLE_ERR_ARG;
-  if (cache->token_stride % 8 || cache->head_stride % 8 || cache->batch_stride % 8 || cache->capacity < 0)
-    return EAGLE_ERR_ARG;
+  if (check_cache_layout(cache)) return EAGLE_ERR_ARG;
   const int S = max_accept + 1, R = B * S;
   const DkvLayout L = plan_dkv(d, B, S);
   if (ws_bytes < L.total) return EAGLE_ERR_WORKSPACE;
@@ -186,9 +190,7 @@ int draft_kv_commit_impl(const eagle_dims* d, const void* w_fc, const eagle_laye
   a.v = (const bf16*)(w + L.v);
   a.dk_cache = (bf16*)dk_cache;
   a.dv_cache = (bf16*)dv_cache;
-  a.cb = cache->batch_stride;
-  a.ch = cache->head_stride;
-  a.ct = cache->token_stride;
+  a.cv = cache_view(cache);
   a.cap = cache->capacity;
   a.status = dev_status;
   float* ssq = (float*)(w + L.ssq);

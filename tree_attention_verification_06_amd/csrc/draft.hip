@@ -567,8 +567,7 @@ int draft_expand_impl(const eagle_dims* d, const eagle_draft_params* pr, const v
     return EAGLE_ERR_ARG;
   if (lw->layout != 0 && lw->layout != 1) return EAGLE_ERR_ARG;
   if (((uintptr_t)ws) & 255) return EAGLE_ERR_ARG;
-  if (cache->token_stride % 8 || cache->head_stride % 8 || cache->batch_stride % 8 || cache->capacity < 0)
-    return EAGLE_ERR_ARG;
+  if (check_cache_layout(cache)) return EAGLE_ERR_ARG;
   const DraftLayout L = plan_draft(d, pr, B, max_prefix);
   if (ws_bytes < L.total) return EAGLE_ERR_WORKSPACE;
   char* w = (char*)ws;
@@ -689,6 +688,10 @@ int draft_expand_impl(const eagle_dims* d, const eagle_draft_params* pr, const v
       a.ch = cache->head_stride;
       a.ct = cache->token_stride;
       a.cap = cache->capacity;
+      a.table = cache->block_table;
+      a.ps = cache->page_size;
+      a.maxb = cache->max_blocks;
+      a.npages = cache->n_pages;
       a.k_tree = kd;
       a.v_tree = vd;
       a.anc = st.anc;

@@ -17,7 +17,7 @@ struct AcceptArgs {
   const void* v_tree;
   void* k_cache;
   void* v_cache;
-  int64_t cb, ch, ct;
+  CacheView cv;  // cache addressing (contiguous or paged)
   int capacity;
   int hkv, hd, elem;
   int32_t* prefix_len;

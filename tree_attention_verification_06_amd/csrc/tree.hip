@@ -86,8 +86,13 @@ __device__ void commit_path(const AcceptArgs& a, int b, int off, const int* s_pa
     const int ch = r % chunks;
     const char* src = (const char*)(which ? a.v_tree : a.k_tree) +
                       ((int64_t)(off + s_path[d]) * a.hkv + h) * row_bytes + ch * 16;
-    char* dst = (char*)(which ? a.v_cache : a.k_cache) +
-                ((int64_t)b * a.cb + (int64_t)h * a.ch + (int64_t)(P + d) * a.ct) * a.elem + ch * 16;
+    bool ok;
+    const int64_t co = cache_offset(a.cv, b, h, P + d, ok);
+    if (!ok) {  // a bad page id: never written through
+      set_status(a.status, EAGLE_ERR_ARG);
+      continue;
+    }
+    char* dst = (char*)(which ? a.v_cache : a.k_cache) + co * a.elem + ch * 16;
     *(uint4*)dst = *(const uint4*)src;
   }
   if (a.next_feature) {
@@ -426,8 +431,12 @@ __global__ __launch_bounds__(256) void commit_layers_kernel(AcceptArgs a) {
         const int ch = r % chunks;
         const int node = a.path[(int64_t)b * stride + d];
         v[u] = *(const uint4*)((which ? vt : kt) + ((int64_t)(off + node) * a.hkv + h) * row_bytes + ch * 16);
-        dst[u] = (which ? vc : kc) + ((int64_t)b * a.cb + (int64_t)h * a.ch + (int64_t)(P + d) * a.ct) * a.elem +
-                 ch * 16;
+        bool ok;
+        const int64_t co = cache_offset(a.cv, b, h, P + d, ok);
+        if (ok)
+          dst[u] = (which ? vc : kc) + co * a.elem + ch * 16;
+        else
+          set_status(a.status, EAGLE_ERR_ARG);  // a bad page id: never written through
       }
     }
 #pragma unroll

@@ -358,3 +358,46 @@ class GreedyStackDecoder:
         v.verify(self.tree_off, self.tokens, prefix_len, self.B, timer=timer)
         v.accept(self.tree_off, self.parent, self.tokens, prefix_len)
         return v.next_token
+
+
+class PagePool:
+    """Host-side page allocator of a paged KV cache, for continuous batching: sequences join
+    and grow (pages taken from a free list), leave (pages returned for reuse), and each step
+    runs on the block table of whichever sequences are active.  Page ids only: the pages
+    themselves are caller-owned tensors [n_pages][Hkv][page_size][D] (or with a leading layer
+    dimension), wrapped with paged()."""
+
+    def __init__(self, n_pages, page_size, max_blocks, device="cuda"):
+        self.n_pages = n_pages
+        self.page_size = page_size
+        self.max_blocks = max_blocks
+        self.device = device
+        self.free = list(range(n_pages))
+        self.owned = {}
+
+    def reserve(self, seq, n_tokens):
+        """Pages for sequence ``seq`` so that it can hold n_tokens slots; returns its page list."""
+        pages = self.owned.setdefault(seq, [])
+        need = -(-n_tokens // self.page_size)
+        if need > self.max_blocks:
+            raise A.EagleError(A.EAGLE_ERR_CAPACITY, f"PagePool: {n_tokens} tokens exceed max_blocks")
+        while len(pages) < need:
+            if not self.free:
+                raise A.EagleError(A.EAGLE_ERR_CAPACITY, "PagePool: out of pages")
+            pages.append(self.free.pop(0))
+        return pages
+
+    def release(self, seq):
+        """Return a sequence's pages; they are the next ones handed out."""
+        self.free[:0] = self.owned.pop(seq, [])
+
+    def table(self, seqs):
+        """Device block table [len(seqs)][max_blocks] of the given sequences (-1: unowned)."""
+        t = torch.full((len(seqs), self.max_blocks), -1, dtype=torch.int32)
+        for i, q in enumerate(seqs):
+            pg = self.owned.get(q, [])
+            t[i, :len(pg)] = torch.tensor(pg, dtype=torch.int32)
+        return t.to(self.device)
+
+    def paged(self, pages, table):
+        return A.PagedCache(pages, table, self.page_size)
