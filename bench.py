@@ -303,16 +303,10 @@ def bench_decode(args):
            "batches": {}}
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for B in [int(b) for b in args.decode_batches.split(",") if b]:
-        kc = randn(nl, B, Hkv, cap, D, std=1.0)
-        vc = randn(nl, B, Hkv, cap, D, std=1.0)
-        dkc = randn(B, Hkv, cap, D, std=1.0)
-        dvc = randn(B, Hkv, cap, D, std=1.0)
+    def run_loops(B, kc, vc, dkc, dvc, root_tok, root_feat, count):
+        """ms per step of plain greedy decoding and of the EAGLE step on the given caches (and
+        the emitted tokens per step of the EAGLE loop when ``count``)."""
         prefix = torch.full((B,), P0, dtype=torch.int32, device="cuda")
-        root_tok = torch.randint(0, V, (B,), dtype=torch.int32, device="cuda", generator=gen)
-        root_feat = torch.empty(B, H, dtype=torch.float32, device="cuda").normal_(0.0, 1.0, generator=gen)
-
-        # plain greedy decoding
         dec = GreedyStackDecoder(dims, head, layers, kc, vc, batch=B, max_prefix=cap, lm_layout=layout,
                                  weight_layout=layout)
         tok = root_tok.clone()
@@ -329,8 +323,6 @@ def bench_decode(args):
         if int(dec.v.status.item()) != 0:
             raise RuntimeError(f"plain decode: device status {int(dec.v.status.item())}")
         del dec
-
-        # EAGLE over the same stack
         st = EagleStackStep(dims, p, head, layers, dw, kc, vc, dkc, dvc, batch=B, max_prefix=cap, lm_layout=layout,
                             weight_layout=layout)
         prefix.fill_(P0)
@@ -345,14 +337,39 @@ def bench_decode(args):
         e1.record(stream)
         torch.cuda.synchronize()
         ms_eagle = e0.elapsed_time(e1) / n
-        # accepted tokens per step (a separate pass that reads accept_len after each step)
-        acc = []
-        for _ in range(n):
+        acc = []  # emitted tokens per step (a separate pass that reads accept_len after each step)
+        for _ in range(n if count else 0):
             feat, tok = st.step(feat, tok, prefix)
             acc.append(int((st.verifier.accept_len + 1).sum().item()))
         if int(st.verifier.status.item()) != 0:
             raise RuntimeError(f"EAGLE decode: device status {int(st.verifier.status.item())}")
         del st
+        return ms_plain, ms_eagle, acc
+
+    PSZ = 64
+    for B in [int(b) for b in args.decode_batches.split(",") if b]:
+        root_tok = torch.randint(0, V, (B,), dtype=torch.int32, device="cuda", generator=gen)
+        root_feat = torch.empty(B, H, dtype=torch.float32, device="cuda").normal_(0.0, 1.0, generator=gen)
+        kc = randn(nl, B, Hkv, cap, D, std=1.0)
+        vc = randn(nl, B, Hkv, cap, D, std=1.0)
+        dkc = randn(B, Hkv, cap, D, std=1.0)
+        dvc = randn(B, Hkv, cap, D, std=1.0)
+        ms_plain, ms_eagle, acc = run_loops(B, kc, vc, dkc, dvc, root_tok, root_feat, True)
+        del kc, vc, dkc, dvc
+        torch.cuda.empty_cache()
+        # the same loops on paged caches: 64-token pages, every sequence's pages scattered
+        # over the pool by a random permutation (the continuous-batching layout)
+        maxb = -(-cap // PSZ)
+        n_pages = B * maxb
+        perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(B)).to(torch.int32)
+        table = perm.reshape(B, maxb).to("cuda")
+        kp = E.PagedCache(randn(nl, n_pages, Hkv, PSZ, D, std=1.0), table, PSZ)
+        vp = E.PagedCache(randn(nl, n_pages, Hkv, PSZ, D, std=1.0), table, PSZ)
+        dkp = E.PagedCache(randn(n_pages, Hkv, PSZ, D, std=1.0), table, PSZ)
+        dvp = E.PagedCache(randn(n_pages, Hkv, PSZ, D, std=1.0), table, PSZ)
+        pms_plain, pms_eagle, _ = run_loops(B, kp, vp, dkp, dvp, root_tok, root_feat, False)
+        del kp, vp, dkp, dvp
+        torch.cuda.empty_cache()
         acc_seq = float(np.mean(acc)) / B  # emitted tokens per sequence per step
         kv_bytes = nl * B * Hkv * P0 * D * 2 * 2
         roof_plain_ms = (stack_bytes + kv_bytes) / (HBM_PEAK_GBS * 1e9) * 1e3
@@ -365,11 +382,13 @@ def bench_decode(args):
             "speedup_measured": round(acc_seq * ms_plain / ms_eagle, 3),
             "break_even_tokens_per_step": round(ms_eagle / ms_plain, 3),
             "projected_speedup": {str(tau): round(tau * ms_plain / ms_eagle, 3) for tau in (3.5, 4.5)},
+            "paged": {"page_size": PSZ, "plain_ms_per_step": round(pms_plain, 4),
+                      "eagle_ms_per_step": round(pms_eagle, 4),
+                      "plain_overhead_pct": round(100 * (pms_plain / ms_plain - 1), 2),
+                      "eagle_overhead_pct": round(100 * (pms_eagle / ms_eagle - 1), 2)},
         }
-        log(f"decode B={B}: plain {ms_plain:.3f} ms/step, EAGLE {ms_eagle:.3f} ms/step, "
-            f"{acc_seq:.2f} tokens/seq/step")
-        del kc, vc, dkc, dvc
-        torch.cuda.empty_cache()
+        log(f"decode B={B}: plain {ms_plain:.3f} ms/step (paged {pms_plain:.3f}), EAGLE {ms_eagle:.3f} ms/step "
+            f"(paged {pms_eagle:.3f}), {acc_seq:.2f} tokens/seq/step")
     out["data"] = ("synthetic: random-init target stack, LM head, embedding and draft head N(0,0.02) drawn on the "
                    "device; KV prefixes and root features N(0,1); each step's roots are the previous step's bonus "
                    "tokens")

@@ -144,18 +144,23 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
   constexpr int GPT = KT * 16 / (NWA * 64);  // 16-byte groups per thread per tensor
   uint4 kreg[2][GPT], vreg[2][GPT];
   auto load_kv = [&](int slot, int kt0) {
+    // paged: kt0 is a multiple of 64 or the chunk's last key, and page sizes are multiples
+    // of 64, so every key this call loads lies in kt0's page: one (uniform) table lookup.
+    // Tree chunks never consult the table (their keys are node indices).
+    int64_t page_off = 0;
+    if constexpr (PAGED) {
+      const CacheView cv{a.cb, a.ch, a.ct, a.table, a.ps, a.maxb, a.npages};
+      const int t0 = tree_chunk ? 0 : kt0;
+      bool ok;
+      page_off = cache_offset(cv, b, 0, t0, ok) - (int64_t)(t0 % a.ps) * a.ct;
+    }
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
       const int i = tid + u * NWA * 64;
       const int key = min(kt0 + (i >> 4), k1 - 1);
       const int gd = i & 15;
       int64_t coff = (int64_t)key * a.ct;
-      if constexpr (PAGED) {
-        // tree chunks never consult the table (their keys are node indices)
-        const CacheView cv{a.cb, a.ch, a.ct, a.table, a.ps, a.maxb, a.npages};
-        bool ok;
-        coff = cache_offset(cv, b, kvh, tree_chunk ? 0 : key, ok) - (int64_t)kvh * a.ch;
-      }
+      if constexpr (PAGED) coff = page_off + (int64_t)(key % a.ps) * a.ct;
       const bf16* kp = tree_chunk ? kt_base + key * tree_stride : kc + coff;
       const bf16* vp = tree_chunk ? vt_base + key * tree_stride : vc + coff;
       kreg[slot][u] = *(const uint4*)(kp + gd * 8);
