@@ -44,6 +44,14 @@ constexpr int KS = HD + 8;              // LDS row stride of the K tile (bf16)
 constexpr int VS = HD + 16;             // LDS row stride of the V tile (bf16): the four keys
                                         // of one transpose read land in distinct banks
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest even) in one gfx950 v_cvt_pk_bf16_f32; a in the
+// low half.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
 
 __device__ __forceinline__ int remap_xcd(int b, int total) {
   const int per = (total + kXcds - 1) / kXcds;
@@ -194,6 +202,20 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
     const bf16* ksb = ks[SL];
     const bf16* vsb = vs[SL];
 
+    // visibility bits of this lane's 16 keys of the tile, per row block: the ancestor word
+    // covering the tile (prefix chunks: all ones) cut at the chunk end, shifted to the lane's
+    // 4-key group; key (st, i) is then bit (st & 1) * 16 + i of the low (st < 2) or high word
+    uint32_t vlo[RBW], vhi[RBW];
+#pragma unroll
+    for (int j = 0; j < RBW; ++j) {
+      // bits 0 .. n-1 set, n = the tile's keys before the chunk end, in [0, 64]; shift
+      // arithmetic only (no select that could become a branch after the score MFMAs)
+      const int n = min(max(k1 - kt0, 0), 64);
+      const uint64_t bound = (~0ull >> ((64 - n) & 63)) & (0ull - (uint64_t)(n != 0));
+      const uint64_t ws = (((kt0 & 64) ? vis1[j] : vis0[j]) & bound) >> (lq * 4);
+      vlo[j] = (uint32_t)ws;
+      vhi[j] = (uint32_t)(ws >> 32);
+    }
     float s[RBW][4][4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -207,9 +229,7 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
         for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[j][kk], acc, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = kt0 + st * 16 + lq * 4 + i;
-          const uint64_t word = (key & 64) ? vis1[j] : vis0[j];
-          const bool vis = (key < k1) & (bool)((word >> (key & 63)) & 1ull);
+          const bool vis = ((st < 2 ? vlo[j] : vhi[j]) >> ((st & 1) * 16 + i)) & 1u;
           s[j][st][i] = vis ? acc[i] * sl2 : -INFINITY;
         }
       }
@@ -226,14 +246,14 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mnew = fmaxf(mrow[j], mx);
       const float mbase = (mnew == -INFINITY) ? 0.f : mnew;
-      const float fac = exp2f(mrow[j] - mbase);
+      const float fac = __builtin_amdgcn_exp2f(mrow[j] - mbase);
       mrow[j] = mnew;
       float ps = 0.f;
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(s[j][st][i] - mbase);
+          const float p = __builtin_amdgcn_exp2f(s[j][st][i] - mbase);
           s[j][st][i] = p;
           ps += p;
         }
@@ -251,10 +271,10 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
           uint32_t u[4];
           bf16x8_t v;
         } pk;
-        pk.u[0] = pack2bf(s[j][2 * G][0], s[j][2 * G][1]);
-        pk.u[1] = pack2bf(s[j][2 * G][2], s[j][2 * G][3]);
-        pk.u[2] = pack2bf(s[j][2 * G + 1][0], s[j][2 * G + 1][1]);
-        pk.u[3] = pack2bf(s[j][2 * G + 1][2], s[j][2 * G + 1][3]);
+        pk.u[0] = cvt_pk_bf16(s[j][2 * G][0], s[j][2 * G][1]);
+        pk.u[1] = cvt_pk_bf16(s[j][2 * G][2], s[j][2 * G][3]);
+        pk.u[2] = cvt_pk_bf16(s[j][2 * G + 1][0], s[j][2 * G + 1][1]);
+        pk.u[3] = cvt_pk_bf16(s[j][2 * G + 1][2], s[j][2 * G + 1][3]);
         pb[j] = pk.v;
       }
       // V^T fragments by transpose reads: lane (q = lq, s = lr) addresses key
