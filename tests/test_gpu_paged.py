@@ -312,3 +312,41 @@ def test_paged_fp32_layer_bit_identical():
         outs.append(v)
     for k in ("h", "argmax", "maxlogit", "k_tree"):
         assert torch.equal(getattr(outs[0], k), getattr(outs[1], k)), k
+
+
+def test_paged_sampling_acceptance_bit_identical():
+    """Verification and acceptance at T > 0 (the sampling LM head and walk) commit through the
+    same paged addressing: bit-identical to the contiguous cache."""
+    import torch
+    from tree_attention_verification_06_amd._abi import PagedCache
+    from tree_attention_verification_06_amd.runner import TreeVerifier
+    from workloads.configs import sample_inputs
+    dims = mini_dims()
+    rng = np.random.default_rng(81)
+    parents = [T.static_tree_60(), T.random_tree(rng, 25), T.chain(10)]
+    wl = make_workload(2, seed=81, dims=dims, batch=3, prefix=[200, 77, 130], parents=parents)
+    t = upload(wl)
+    gumbel, u = sample_inputs(wl)
+    gt, ut = to_tensor(gumbel), to_tensor(u)
+    M, cap = wl.n_nodes, wl.cache_cap
+    table, maxb = _tables(3, cap, 3 * (-(-cap // PS)) + 4, 81)
+    n_pages = 3 * maxb + 4
+    kp, vp = _pool(t["k_cache"].shape, n_pages, 11), _pool(t["k_cache"].shape, n_pages, 12)
+    _to_pages(t["k_cache"], kp, table, cap)
+    _to_pages(t["v_cache"], vp, table, cap)
+    runs = []
+    for K, V in ((t["k_cache"], t["v_cache"]), (PagedCache(kp, table, PS), PagedCache(vp, table, PS))):
+        pl = t["prefix_len"].clone()
+        v = TreeVerifier(dims, t["weights"], K, V, batch=3, max_total_nodes=M, max_nodes=60, max_prefix=cap,
+                         sample=True)
+        v.step_sample(t["tree_off"], t["parent"], t["tokens"], pl, M, 0.7, gt, ut, x=t["x"])
+        torch.cuda.synchronize()
+        assert int(v.status.item()) == 0
+        runs.append((v, pl))
+    (a, pa), (b, pb) = runs
+    for k in ("child_logit", "rest_lse", "rest_token", "accept_len", "path", "out_tokens", "next_token",
+              "next_feature"):
+        assert torch.equal(getattr(a, k), getattr(b, k)), k
+    assert torch.equal(pa, pb)
+    assert torch.equal(_from_pages(kp, table, cap), t["k_cache"])
+    assert torch.equal(_from_pages(vp, table, cap), t["v_cache"])
