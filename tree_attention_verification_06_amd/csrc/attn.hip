@@ -151,28 +151,31 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
   // (keys past the chunk are clamped to its last key and zeroed when stored).
   constexpr int GPT = KT * 16 / (NWA * 64);  // 16-byte groups per thread per tensor
   uint4 kreg[2][GPT], vreg[2][GPT];
+  // Addressing: thread row rowk = i >> 4 (a key within the tile) and 16-byte group gd = i & 15
+  // are fixed per thread; a call's keys are kt0 + min(rowk, k1 - 1 - kt0) (clamped to the
+  // chunk's last key), so the offset is a uniform base plus row * stride.  Paged: kt0 is a
+  // multiple of 64 or the chunk's last key, and page sizes are multiples of 64, so every key
+  // of a call lies in kt0's page: one (uniform) table lookup.  Tree chunks never consult the
+  // table (their keys are node indices).
+  const int64_t kst = tree_chunk ? tree_stride : a.ct;  // elements between consecutive keys
+  const bf16* kb = (tree_chunk ? kt_base : kc) + (tid & 15) * 8;
+  const bf16* vb = (tree_chunk ? vt_base : vc) + (tid & 15) * 8;
   auto load_kv = [&](int slot, int kt0) {
-    // paged: kt0 is a multiple of 64 or the chunk's last key, and page sizes are multiples
-    // of 64, so every key this call loads lies in kt0's page: one (uniform) table lookup.
-    // Tree chunks never consult the table (their keys are node indices).
-    int64_t page_off = 0;
+    int64_t base = (int64_t)kt0 * kst;
     if constexpr (PAGED) {
-      const CacheView cv{a.cb, a.ch, a.ct, a.table, a.ps, a.maxb, a.npages};
-      const int t0 = tree_chunk ? 0 : kt0;
-      bool ok;
-      page_off = cache_offset(cv, b, 0, t0, ok) - (int64_t)(t0 % a.ps) * a.ct;
+      if (!tree_chunk) {
+        const CacheView cv{a.cb, a.ch, a.ct, a.table, a.ps, a.maxb, a.npages};
+        bool ok;
+        base = cache_offset(cv, b, 0, kt0, ok);  // kt0's slot in its page, head 0
+      }
     }
+    const int last = k1 - 1 - kt0;
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
-      const int i = tid + u * NWA * 64;
-      const int key = min(kt0 + (i >> 4), k1 - 1);
-      const int gd = i & 15;
-      int64_t coff = (int64_t)key * a.ct;
-      if constexpr (PAGED) coff = page_off + (int64_t)(key % a.ps) * a.ct;
-      const bf16* kp = tree_chunk ? kt_base + key * tree_stride : kc + coff;
-      const bf16* vp = tree_chunk ? vt_base + key * tree_stride : vc + coff;
-      kreg[slot][u] = *(const uint4*)(kp + gd * 8);
-      vreg[slot][u] = *(const uint4*)(vp + gd * 8);
+      const int r = min((tid + u * NWA * 64) >> 4, last);
+      const int64_t off = base + (int64_t)r * kst;
+      kreg[slot][u] = *(const uint4*)(kb + off);
+      vreg[slot][u] = *(const uint4*)(vb + off);
     }
   };
   auto store_kv = [&](int slot, int buf, int kt0) {
