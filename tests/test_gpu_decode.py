@@ -285,3 +285,78 @@ def test_greedy_stack_decoder_matches_oracle():
         assert min(gaps) > GAP_BF16
         assert out[b].tolist() == ref
     assert t["prefix_len"].tolist() == [int(p) + 12 for p in wl.prefix_len]
+
+
+def test_eagle_stack_step_updates_the_draft_cache_from_the_given_root():
+    """Three full steps over a two-layer stack (draft -> encode -> verify -> accept + per-layer
+    commit -> draft KV update), each step fed the previous step's returned feature: the draft
+    cache slot of each step's root holds the draft K/V of [the feature given to that step ;
+    E[its root token]] at its position (the feature buffers alternate, so the acceptance call's
+    next feature never overwrites the root feature before the update reads it), and the prefix
+    grows by the accepted length + 1."""
+    import torch
+    from tree_attention_verification_06_amd.runner import EagleStackStep
+    from workloads import DraftParams
+    wl = stack_workload(21, mini_dims(), 2, batch=2, prefix=[200, 77], cache_cap=300, embed_std=1.0, lm_std=0.2)
+    d = wl.dims
+    t = _upload(wl)
+    st = EagleStackStep(d, DraftParams(depth=3, top_k=4, frontier=4, max_nodes=16), t["weights"], t["layers"],
+                        t["draft_weights"], t["k_caches"], t["v_caches"], t["dk_cache"], t["dv_cache"], batch=2,
+                        max_prefix=300)
+    feat, tok = t["root_feature"].clone(), t["root_token"].clone()
+    prefix = t["prefix_len"]
+    for step in range(3):
+        P0 = prefix.cpu().numpy().copy()
+        f0 = feat.cpu().numpy().astype(np.float64)
+        r0 = tok.cpu().numpy().copy()
+        feat, tok = st.step(feat, tok, prefix)
+        torch.cuda.synchronize()
+        assert int(st.verifier.status.item()) == 0
+        L = st.verifier.accept_len.cpu().numpy()
+        assert (prefix.cpu().numpy() == P0 + L + 1).all()
+        dk, dv = np_of(t["dk_cache"]), np_of(t["dv_cache"])
+        for b in range(2):
+            rk, rv = draft_kv_rows(d, wl.draft_weights, wl.weights["embed"], f0[b:b + 1], [int(r0[b])],
+                                   np.array([P0[b]]))
+            ek = rel_err(dk[b][:, P0[b]], rk[0])
+            ev = rel_err(dv[b][:, P0[b]], rv[0])
+            _log(f"  step {step} seq {b}: accept {L[b]}, root slot draft K/V rel err {ek:.2e} {ev:.2e}")
+            assert ek <= TOL_BF16 and ev <= TOL_BF16
+
+
+def test_stack_commit_refuses_a_full_cache_in_every_layer():
+    """A sequence with no room left is rejected (accept_len -1, EAGLE_ERR_CAPACITY): no layer's
+    cache, no draft slot and not its prefix change; the other sequence commits normally."""
+    import torch
+    from tree_attention_verification_06_amd._abi import EAGLE_ERR_CAPACITY
+    from tree_attention_verification_06_amd.runner import DraftKV
+    wl = _stack(13, prefix=(299, 50))  # capacity 300: sequence 0 has one free slot
+    d = wl.dims
+    t = _upload(wl)
+    rng = np.random.default_rng(13)
+    parents = [T.chain(4), T.random_tree(rng, 9)]
+    tokens = [T.tree_tokens(rng, p, d.vocab) for p in parents]
+    off, par, tok = _trees(parents, tokens)
+    M = len(tok)
+    x = to_tensor(normal_tensor(wl.seed, TID["x"], (M, d.hidden), 1.0, "bf16"))
+    ot, pt = to_tensor(off), to_tensor(par)
+    v = _verifier(wl, t, 9, M, max_prefix=300)
+    v.encode(ot, pt, t["prefix_len"], M)
+    v.verify(ot, to_tensor(tok), t["prefix_len"], M, x=x)
+    torch.cuda.synchronize()
+    g = v.argmax.cpu().numpy()
+    for j in range(1, 4):  # sequence 0's chain fully matches: L = 3 needs 4 slots, only 1 is free
+        tok[j] = g[j - 1]
+    tt = to_tensor(tok)
+    kc0, dk0 = t["k_caches"].clone(), t["dk_cache"].clone()
+    v.accept(ot, pt, tt, t["prefix_len"])
+    dkv = DraftKV(d, t["weights"], t["draft_weights"], t["dk_cache"], t["dv_cache"], batch=2, max_accept=v.max_accept)
+    dkv.commit(v, ot, tt, t["root_feature"], t["prefix_len"])
+    torch.cuda.synchronize()
+    assert int(v.status.item()) == EAGLE_ERR_CAPACITY
+    assert int(v.accept_len[0]) == -1 and int(t["prefix_len"][0]) == 299
+    assert torch.equal(t["k_caches"][:, 0], kc0[:, 0]) and torch.equal(t["dk_cache"][0], dk0[0])
+    L1 = int(v.accept_len[1])
+    assert L1 >= 0 and int(t["prefix_len"][1]) == 50 + L1 + 1
+    for l in range(N_LAYERS):
+        assert torch.equal(t["k_caches"][l, 1, :, 50], v.k_tree[l, off[1]])
