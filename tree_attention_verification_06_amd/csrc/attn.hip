@@ -326,22 +326,25 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
 }
 
 // Combine the chunks of every query row in fixed order: o = sum_c 2^(m_c - M) o_c / L.
+// A workgroup takes MROWS rows; 32 threads per row, each with 4 consecutive d (16-byte
+// partial loads, one 8-byte bf16 store).
+constexpr int MROWS = 8;
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int grid_real) {
   const int bid = blockIdx.x;
   if (bid >= grid_real) return;
   const int g = a.hq / a.hkv;
   const int rmax = a.max_nodes * g;
-  const int rpairs = (rmax + 1) / 2;
+  const int rgroups = (rmax + MROWS - 1) / MROWS;
   int t = bid;
-  const int rp = t % rpairs;
-  t /= rpairs;
+  const int rg = t % rgroups;
+  t /= rgroups;
   const int kvh = t % a.hkv;
   const int b = t / a.hkv;
   const int off = a.tree_off[b];
   const int N = a.n_nodes ? a.n_nodes[b] : a.tree_off[b + 1] - off;
   const int qlo = a.q_lo ? a.q_lo[b] : 0;
-  const int row = rp * 2 + threadIdx.x / HD;
-  const int d = threadIdx.x % HD;
+  const int row = rg * MROWS + threadIdx.x / 32;
+  const int d4 = (threadIdx.x % 32) * 4;
   if (row >= (N - qlo) * g || N - qlo > a.max_nodes || N > 64 * a.mw) return;
   const int P = min(max(a.prefix_len[b], 0), a.cap);
   const int n_pref = min((P + a.kch - 1) / a.kch, a.n_chunks - 1);
@@ -358,29 +361,34 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int grid_re
 #pragma unroll
     for (int u = 0; u < 4; ++u) M = fmaxf(M, m4[u]);
   }
-  float L = 0.f, O = 0.f;
+  float L = 0.f;
+  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j0 = 0; j0 < cnt; j0 += 4) {
-    float m4[4], l4[4], o4[4];
+    float m4[4], l4[4];
+    float4 o4[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t pi = (base + chunk_of(min(j0 + u, cnt - 1))) * rmax + row;
       m4[u] = a.part_ml[pi * 2];
       l4[u] = a.part_ml[pi * 2 + 1];
-      o4[u] = a.part_o[pi * HD + d];
+      o4[u] = *(const float4*)(a.part_o + pi * HD + d4);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float f = (j0 + u < cnt) ? exp2f(m4[u] - M) : 0.f;
       L += f * l4[u];
-      O += f * o4[u];
+      O.x += f * o4[u].x;
+      O.y += f * o4[u].y;
+      O.z += f * o4[u].z;
+      O.w += f * o4[u].w;
     }
   }
-  const float out = O / L;
+  const float4 out = make_float4(O.x / L, O.y / L, O.z / L, O.w / L);
   const int node = qlo + row / g, hh = row % g;
   const int64_t orow = a.q_stride ? (int64_t)b * a.q_stride + (node - qlo) : (int64_t)(off + node);
-  const int64_t oi = orow * a.hq * HD + (int64_t)(kvh * g + hh) * HD + d;
-  ((bf16*)a.out)[oi] = f2bf(out);
-  if (a.dbg) a.dbg[oi] = out;
+  const int64_t oi = orow * a.hq * HD + (int64_t)(kvh * g + hh) * HD + d4;
+  *(uint2*)((bf16*)a.out + oi) = make_uint2(cvt_pk_bf16(out.x, out.y), cvt_pk_bf16(out.z, out.w));
+  if (a.dbg) *(float4*)(a.dbg + oi) = out;
 }
 
 // fp32 path: one wave per (node, query head); scores staged in LDS.
@@ -504,7 +512,7 @@ int launch_attn(AttnArgs& a, const AttnPlan& p, eagle_timer* timer, hipStream_t 
     hipLaunchKernelGGL(tree_attn_bf16_kernel<false>, dim3(padded), dim3(NWA * 64), 0, s, a, grid);
   timer_end(timer, s);
   const int g = a.hq / a.hkv;
-  const int mgrid = a.batch * a.hkv * ((a.max_nodes * g + 1) / 2);
+  const int mgrid = a.batch * a.hkv * ((a.max_nodes * g + MROWS - 1) / MROWS);
   timer_begin(timer, ST_ATTN_MERGE, s);
   hipLaunchKernelGGL(attn_merge_kernel, dim3(mgrid), dim3(256), 0, s, a, mgrid);
   timer_end(timer, s);
