@@ -360,3 +360,33 @@ def test_stack_commit_refuses_a_full_cache_in_every_layer():
     assert L1 >= 0 and int(t["prefix_len"][1]) == 50 + L1 + 1
     for l in range(N_LAYERS):
         assert torch.equal(t["k_caches"][l, 1, :, 50], v.k_tree[l, off[1]])
+
+
+def test_stack_verify_fp32_layers():
+    """The fp32 path of a stack (VALU GEMMs and attention): layers above the first read the
+    previous layer's f32 output with the RMSNorm computed in the GEMM; against the oracle at
+    the fp32 tolerance."""
+    import torch
+    from tests._gpu import GAP_F32, TOL_F32
+    from workloads import LayerDims
+    dims = LayerDims(256, 4, 2, 64, 384, 1000, 1.0e4, 1e-5, "f32")
+    wl = stack_workload(17, dims, 2, batch=2, prefix=[90, 33], cache_cap=160, embed_std=1.0, lm_std=0.2)
+    t = _upload(wl)
+    rng = np.random.default_rng(17)
+    parents = [T.random_tree(rng, 12), T.chain(6)]
+    off, par, tok = _trees(parents, [T.tree_tokens(rng, p, dims.vocab) for p in parents])
+    M = len(tok)
+    v = _verifier(wl, t, 12, M, max_prefix=160)
+    ot, pt, tt = to_tensor(off), to_tensor(par), to_tensor(tok)
+    v.encode(ot, pt, t["prefix_len"], M)
+    v.verify(ot, tt, t["prefix_len"], M)
+    torch.cuda.synchronize()
+    ref = verify_forward_layers(dims, wl.weights, wl.layers, None, parents, wl.prefix_len, wl.k_caches, wl.v_caches,
+                                embed_tokens=tok)
+    errs = {f"k_tree[{l}]": rel_err(np_of(v.k_tree[l]), ref["k_tree"][l]) for l in range(2)}
+    errs["h"] = rel_err(np_of(v.h), ref["h"])
+    errs["maxlogit"] = rel_err(np_of(v.maxlogit), ref["maxlogit"])
+    _log("  fp32 stack max rel err", {k: f"{e:.2e}" for k, e in errs.items()})
+    assert all(e <= TOL_F32 for e in errs.values()), errs
+    decisive = ref["gap"] > GAP_F32
+    assert (np_of(v.argmax)[decisive] == ref["argmax"][decisive]).all()
