@@ -522,7 +522,7 @@ int commit_args(AcceptArgs& a, int batch, const int32_t* tree_off, int max_nodes
   if (n_kv_heads < 1 || head_dim < 1 || (head_dim * es) % 16) return EAGLE_ERR_UNSUPPORTED;
   if ((cache->token_stride * es) % 16 || (cache->head_stride * es) % 16 || (cache->batch_stride * es) % 16)
     return EAGLE_ERR_ARG;
-  if (check_cache_layout(cache) && cache->block_table) return EAGLE_ERR_ARG;
+  if (cache->block_table && check_cache_layout(cache)) return EAGLE_ERR_ARG;  // the paging fields
   if (next_feature && (!h_nodes || hidden < 1 || hidden % 4)) return EAGLE_ERR_ARG;
   a.tree_off = tree_off;
   a.parent = parent;
