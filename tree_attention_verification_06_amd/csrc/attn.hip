@@ -105,24 +105,26 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
   bf16x8_t qf[RBW][4];
   uint64_t vis0[RBW], vis1[RBW];
 #pragma unroll
+  // Loads are unconditional (rows past R read row R - 1, which exists since row_base < R,
+  // and are then given a zero query and an all-visible mask): a load under a branch would
+  // be waited for at the join, before the first K/V loads could be issued.
   for (int j = 0; j < RBW; ++j) {
     const int row = row_base + (w * RBW + j) * 16 + lr;
-    vis0[j] = ~0ull;
-    vis1[j] = ~0ull;
-    if (row < R) {
-      const int node = qlo + row / g, hh = row % g;
-      const int64_t qrow = a.q_stride ? (int64_t)b * a.q_stride + (node - qlo) : (int64_t)(off + node);
-      const bf16* qp = q + (qrow * a.hq + kvh * g + hh) * HD;
+    const bool live = row < R;
+    const int rc = live ? row : R - 1;
+    const int node = qlo + rc / g, hh = rc % g;
+    const int64_t qrow = a.q_stride ? (int64_t)b * a.q_stride + (node - qlo) : (int64_t)(off + node);
+    const bf16* qp = q + (qrow * a.hq + kvh * g + hh) * HD;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qf[j][kk] = *(const bf16x8_t*)(qp + kk * 32 + lq * 8);
-      if (tree_chunk) {
-        vis0[j] = a.anc[(int64_t)(off + node) * a.mw];
-        vis1[j] = a.mw > 1 ? a.anc[(int64_t)(off + node) * a.mw + 1] : 0ull;
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qf[j][kk] = bf16x8_t{};
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8_t v = *(const bf16x8_t*)(qp + kk * 32 + lq * 8);
+      qf[j][kk] = live ? v : bf16x8_t{};
     }
+    const uint64_t* ap = a.anc + (int64_t)(off + node) * a.mw;
+    const uint64_t a0 = ap[0];
+    const uint64_t a1 = ap[a.mw > 1 ? 1 : 0];
+    vis0[j] = (tree_chunk && live) ? a0 : ~0ull;
+    vis1[j] = (tree_chunk && live) ? (a.mw > 1 ? a1 : 0ull) : ~0ull;
   }
 
   f32x4 o[RBW][8];
