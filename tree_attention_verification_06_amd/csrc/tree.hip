@@ -19,14 +19,18 @@ __device__ __forceinline__ void set_status(int32_t* st, int code) {
 __global__ __launch_bounds__(128) void tree_build_kernel(const int32_t* tree_off, const int32_t* parent,
                                                          const int32_t* prefix_len, int mw, uint64_t* anc,
                                                          int32_t* depth, int32_t* pos, int32_t* status) {
+  // the tree's parent array is staged in LDS (one round of loads) and every ancestor walk
+  // runs there, instead of one dependent global load per level of depth
   __shared__ int s_bad;
+  __shared__ int s_par[128];
   const int b = blockIdx.x;
   const int off = tree_off[b];
   const int N = tree_off[b + 1] - off;
-  if (threadIdx.x == 0) s_bad = (N < 1 || N > 64 * mw) ? EAGLE_ERR_CAPACITY : 0;
+  if (threadIdx.x == 0) s_bad = (N < 1 || N > 64 * mw || N > 128) ? EAGLE_ERR_CAPACITY : 0;
   __syncthreads();
   for (int i = threadIdx.x; i < N && !s_bad; i += blockDim.x) {
     const int p = parent[off + i];
+    s_par[i] = p;
     if ((i == 0 && p != -1) || (i > 0 && (p < 0 || p >= i))) atomicCAS(&s_bad, 0, EAGLE_ERR_TREE);
   }
   __syncthreads();
@@ -45,7 +49,7 @@ __global__ __launch_bounds__(128) void tree_build_kernel(const int32_t* tree_off
     while (true) {
       words[j >> 6] |= 1ull << (j & 63);
       if (j == 0) break;
-      j = parent[off + j];
+      j = s_par[j];
       ++d;
     }
     for (int w = 0; w < mw; ++w) anc[(int64_t)(off + i) * mw + w] = words[w];
