@@ -287,7 +287,7 @@ class DraftKV:
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
         A.eagle_workspace_init(self.workspace)
 
-    def commit(self, verifier, tree_off, tokens, root_feature, prefix_len, timer=None):
+    def commit(self, verifier, tree_off, tokens, root_feature, prefix_len):
         """Slots of the path verifier.accept just committed, from verifier.h and root_feature
         (the feature given to this step's draft; not verifier.next_feature)."""
         v = verifier
@@ -331,7 +331,7 @@ class EagleStackStep:
         v.encode(d.tree_off, d.parent, prefix_len, self.total)
         v.verify(d.tree_off, d.tokens, prefix_len, self.total, timer=timer)
         v.accept(d.tree_off, d.parent, d.tokens, prefix_len)
-        self.dkv.commit(v, d.tree_off, d.tokens, root_feature, prefix_len, timer=timer)
+        self.dkv.commit(v, d.tree_off, d.tokens, root_feature, prefix_len)
         return v.next_feature, v.next_token
 
 
