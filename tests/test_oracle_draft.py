@@ -173,3 +173,60 @@ def test_forcing_own_decisions_reproduces_free_run(tau):
     for a, b in zip(free, forced):
         assert a["parent"] == b["parent"] and a["tokens"] == b["tokens"] and a["cum"] == b["cum"]
         assert [c["token"] for c in a["pool"]] == [c["token"] for c in b["pool"]]
+
+
+@pytest.mark.parametrize("seed,tau", [(0, 0.0), (3, 0.0), (6, 0.2)])
+def test_branching_tree_equals_sequential_run_along_each_root_path(seed, tau):
+    """Every expanded node of a branching draft (top-3, frontier 3, depth 4) must carry
+    exactly what the one-layer draft head computes when it is run left to right over that
+    node's root path alone ("LLM parallel decoding EAGLE" page, how EAGLE works: the head
+    predicts the next feature from the feature and token before it, and its candidates are
+    expanded into a tree; "Speculative decoding with EAGLE" page, technical insight: the
+    row for a token is formed from the feature before it and that token's true embedding).
+    A draft row that also saw nodes off its own root path, or took a sibling's feature,
+    gives a different f_hat and different child log-probabilities."""
+    wl = _wl(seed, B=2)
+    params = DraftParams(depth=4, top_k=3, frontier=3, max_nodes=40, conf_threshold=tau)
+    res = _run(wl, params, trace=True)
+    W_fc, E = wf(wl.draft_weights["w_fc"]), wl.weights["embed"]
+    checked = 0
+    for b, r in enumerate(res):
+        pool = r["pool"]
+        P = int(wl.prefix_len[b])
+        expanded = [(lvl, row, n) for lvl, lv in enumerate(r["levels"]) for row, n in enumerate(lv["frontier"])]
+        assert len(expanded) > 4 and any(pool[n]["depth"] >= 2 for _, _, n in expanded)
+        for lvl, row, n in expanded:
+            path = []
+            j = n
+            while j >= 0:
+                path.append(j)
+                j = pool[j]["parent"]
+            path.reverse()
+            dec = SequentialDecoder(wl.dims, wl.draft_weights, wl.dk_cache[b, :, :P], wl.dv_cache[b, :, :P])
+            f = wf(wl.root_feature[b])
+            cum = 0.0
+            for j in path:
+                f = dec.step(W_fc @ np.concatenate([f, wf(E[pool[j]["token"]])]))["h"]
+                if j != n:
+                    z = logits_of(wl.dims, wl.weights, f)
+                    lse = z.max() + np.log(np.sum(np.exp(z - z.max())))
+                    nxt = path[path.index(j) + 1]
+                    cum += min(0.0, z[pool[nxt]["token"]] - lse)
+            assert dec.pos == P + pool[n]["depth"] + 1
+            assert np.abs(r["levels"][lvl]["fhat"][row] - f).max() < 1e-10 * max(1.0, np.abs(f).max())
+            assert abs(pool[n]["cum"] - cum) < 1e-10
+            z = logits_of(wl.dims, wl.weights, f)
+            lse = z.max() + np.log(np.sum(np.exp(z - z.max())))
+            kids = [c for c in r["levels"][lvl]["children"] if pool[c]["parent"] == n]
+            left = list(range(len(z)))
+            for c in kids:                      # children = the top_k tokens by an explicit scan
+                best = left[0]
+                for t in left:
+                    if z[t] > z[best]:
+                        best = t
+                left.remove(best)
+                assert pool[c]["token"] == best
+                assert abs(pool[c]["logp"] - (z[best] - lse)) < 1e-10
+                assert abs(pool[c]["cum"] - (cum + min(0.0, z[best] - lse))) < 1e-10
+            checked += 1
+    assert checked >= 10
