@@ -180,7 +180,9 @@ int eagle_pack_fragments(const void* w, int32_t rows, int32_t cols, void* out, v
  * not touched), max_nodes >= every tree size, both host ints.
  * Errors: mask_words*64 < max_nodes -> EAGLE_ERR_CAPACITY (host).  A tree with
  * parent[0] != -1 or parent[i] outside [0, i) sets *dev_status = EAGLE_ERR_TREE
- * and its anc words are all zero (depth/pos then undefined). */
+ * and its anc words are all zero (depth/pos then undefined).  A tree of more than
+ * max_nodes nodes, or reaching past total_nodes, sets *dev_status =
+ * EAGLE_ERR_CAPACITY and nothing of it is written. */
 int eagle_tree_build(int32_t batch, const int32_t* tree_off, int32_t total_nodes, int32_t max_nodes,
                      const int32_t* parent, const int32_t* prefix_len, int32_t mask_words,
                      uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* dev_status, void* stream);
@@ -199,7 +201,9 @@ int eagle_tree_build(int32_t batch, const int32_t* tree_off, int32_t total_nodes
  * Inputs: x_in [total_nodes][H] (dtype) or NULL; embed [V][H] or NULL; tokens
  * [total_nodes]; anc [total_nodes][mask_words]; pos [total_nodes]; prefix_len
  * [B]; k_cache/v_cache (read only).  Host ints: total_nodes, max_nodes,
- * max_prefix >= every prefix_len[b] (bounds the work grid).  total_nodes may
+ * max_prefix (sizes the split of the prefix over workgroups; a prefix_len[b] above
+ * it is still attended in full, by the last split, only more slowly; prefix_len is
+ * clamped to the cache capacity).  total_nodes may
  * exceed tree_off[B]: rows past it are padding, computed row by row and never
  * attended to (their tokens must still be valid ids when x_in is NULL).
  * Outputs: k_tree, v_tree [total_nodes][Hkv][D] (dtype; post-rotary keys),
@@ -238,8 +242,10 @@ int eagle_tree_verify(const eagle_dims* dims, const eagle_layer_w* layer, const 
  * Outputs: accept_len [B], path and out_tokens [B][max_accept + 1] (entries
  * past L are -1), next_token [B], next_feature [B][hidden] f32 (NULL to skip).
  * Device errors: L > max_accept or prefix_len + L + 1 > capacity set
- * *dev_status = EAGLE_ERR_CAPACITY; that sequence gets accept_len -1 and no
- * commit. */
+ * *dev_status = EAGLE_ERR_CAPACITY; a malformed parent array, or depth / anc
+ * that are not its encoding (e.g. left zeroed or stale by a failed
+ * eagle_tree_build), sets *dev_status = EAGLE_ERR_TREE; such a sequence gets
+ * accept_len -1, next_token -1, path and out_tokens all -1 and no commit. */
 int eagle_accept_commit(int32_t batch, const int32_t* tree_off, int32_t max_nodes, const int32_t* parent,
                         const int32_t* tokens, const int32_t* argmax, const uint64_t* anc, int32_t mask_words,
                         const int32_t* depth, const void* k_tree, const void* v_tree, void* k_cache,

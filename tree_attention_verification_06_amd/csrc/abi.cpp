@@ -578,7 +578,8 @@ int eagle_tree_build(int32_t batch, const int32_t* tree_off, int32_t total_nodes
   if (mask_words < 1 || mask_words > 2) return EAGLE_ERR_UNSUPPORTED;
   if (max_nodes > 64 * mask_words) return EAGLE_ERR_CAPACITY;
   hipStream_t s = (hipStream_t)stream;
-  return launch_tree_build(batch, tree_off, parent, prefix_len, mask_words, anc, depth, pos, dev_status, s);
+  return launch_tree_build(batch, tree_off, parent, prefix_len, mask_words, max_nodes, total_nodes, anc, depth, pos,
+                           dev_status, s);
 }
 
 int eagle_tree_verify(const eagle_dims* dims, const eagle_layer_w* layer, const void* final_ln, const void* w_lm,

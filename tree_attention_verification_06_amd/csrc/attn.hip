@@ -89,8 +89,10 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
     k0 = 0;
     k1 = N;
   } else {
+    // the last prefix chunk takes every key up to P: the grid is planned for the host's
+    // max_prefix, and a longer device prefix is then still attended in full
     k0 = c * a.kch;
-    k1 = min(P, k0 + a.kch);
+    k1 = (c == a.n_chunks - 2) ? P : min(P, k0 + a.kch);
     if (k0 >= k1) return;
   }
 
@@ -393,9 +395,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int grid_re
   if (a.dbg) *(float4*)(a.dbg + oi) = out;
 }
 
-// fp32 path: one wave per (node, query head); scores staged in LDS.
+// fp32 path: one wave per (node, query head).  Keys are taken in blocks of F32_BLK: the
+// block's scores are staged in LDS (one lane per key), then every lane updates the running
+// max, the running sum and its own output dimensions (lane, lane + 64) over the block, so
+// the LDS footprint does not depend on the prefix length.
+constexpr int F32_BLK = 512;
 __global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnArgs a) {
-  extern __shared__ float sm[];
+  __shared__ float qs[128];
+  __shared__ float sc[F32_BLK];
   const int hq = a.hq, hd = a.hd;
   const int node_g = blockIdx.x / hq, h = blockIdx.x % hq;
   int b = 0;
@@ -404,11 +411,9 @@ __global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnArgs a) {
   const int N = a.tree_off[b + 1] - off;
   const int i = node_g - off;
   if (N > a.max_nodes) return;
-  const int P = min(min(max(a.prefix_len[b], 0), a.cap), a.max_prefix);
+  const int P = min(max(a.prefix_len[b], 0), a.cap);
   const int kvh = h / (hq / a.hkv);
   const int lane = threadIdx.x;
-  float* qs = sm;
-  float* sc = sm + hd;
   const float* q = (const float*)a.q + ((int64_t)node_g * hq + h) * hd;
   for (int d = lane; d < hd; d += 64) qs[d] = q[d];
   __syncthreads();
@@ -422,43 +427,55 @@ __global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnArgs a) {
   const float* ktr = (const float*)a.k_tree;
   const float* vtr = (const float*)a.v_tree;
   const float scale = rsqrtf((float)hd);
-  float mx = -INFINITY;
-  for (int j = lane; j < P + N; j += 64) {
-    float s = -INFINITY;
-    const float* kp = nullptr;
-    if (j < P) {
-      kp = kc + coff(j);
-    } else {
-      const int jn = j - P;
-      const uint64_t word = a.anc[(int64_t)(off + i) * a.mw + (jn >> 6)];
-      if ((word >> (jn & 63)) & 1ull) kp = ktr + ((int64_t)(off + jn) * a.hkv + kvh) * hd;
+  float m = -INFINITY, l = 0.f;
+  float acc[2] = {0.f, 0.f};
+  for (int j0 = 0; j0 < P + N; j0 += F32_BLK) {
+    const int nb = min(F32_BLK, P + N - j0);
+    float bm = -INFINITY;
+    for (int jj = lane; jj < nb; jj += 64) {
+      const int j = j0 + jj;
+      float s = -INFINITY;
+      const float* kp = nullptr;
+      if (j < P) {
+        kp = kc + coff(j);
+      } else {
+        const int jn = j - P;
+        const uint64_t word = a.anc[(int64_t)(off + i) * a.mw + (jn >> 6)];
+        if ((word >> (jn & 63)) & 1ull) kp = ktr + ((int64_t)(off + jn) * a.hkv + kvh) * hd;
+      }
+      if (kp) {
+        float dot = 0.f;
+        for (int d = 0; d < hd; ++d) dot += qs[d] * kp[d];
+        s = dot * scale;
+      }
+      sc[jj] = s;
+      bm = fmaxf(bm, s);
     }
-    if (kp) {
-      float acc = 0.f;
-      for (int d = 0; d < hd; ++d) acc += qs[d] * kp[d];
-      s = acc * scale;
+    bm = wave_max(bm);
+    __syncthreads();
+    const float mnew = fmaxf(m, bm);
+    if (mnew != -INFINITY) {  // else every key so far is masked: nothing to add
+      const float fac = m == -INFINITY ? 0.f : __expf(m - mnew);
+      l *= fac;
+      acc[0] *= fac;
+      acc[1] *= fac;
+      for (int jj = 0; jj < nb; ++jj) {
+        const float p = __expf(sc[jj] - mnew);
+        if (p == 0.f) continue;
+        l += p;
+        const int j = j0 + jj;
+        const float* vp = j < P ? vc + coff(j) : vtr + ((int64_t)(off + j - P) * a.hkv + kvh) * hd;
+        acc[0] += p * vp[lane];
+        if (lane + 64 < hd) acc[1] += p * vp[lane + 64];
+      }
+      m = mnew;
     }
-    sc[j] = s;
-    mx = fmaxf(mx, s);
+    __syncthreads();  // sc is refilled by the next block
   }
-  mx = wave_max(mx);
-  float sum = 0.f;
-  for (int j = lane; j < P + N; j += 64) {
-    const float p = __expf(sc[j] - mx);
-    sc[j] = p;
-    sum += p;
-  }
-  sum = wave_sum(sum);
-  __syncthreads();
-  for (int d = lane; d < hd; d += 64) {
-    float acc = 0.f;
-    for (int j = 0; j < P + N; ++j) {
-      const float p = sc[j];
-      if (p == 0.f) continue;
-      const float* vp = j < P ? vc + coff(j) : vtr + ((int64_t)(off + j - P) * a.hkv + kvh) * hd;
-      acc += p * vp[d];
-    }
-    const float out = acc / sum;
+  for (int u = 0; u < 2; ++u) {
+    const int d = lane + 64 * u;
+    if (d >= hd) break;
+    const float out = acc[u] / l;
     const int64_t oi = (int64_t)node_g * hq * hd + (int64_t)h * hd + d;
     ((float*)a.out)[oi] = out;
     if (a.dbg) a.dbg[oi] = out;
@@ -522,10 +539,9 @@ int launch_attn(AttnArgs& a, const AttnPlan& p, eagle_timer* timer, hipStream_t 
 }
 
 int launch_attn_f32(AttnArgs& a, int total_nodes, eagle_timer* timer, hipStream_t s) {
-  const size_t lds = (size_t)(a.hd + a.max_prefix + a.max_nodes) * sizeof(float);
-  if (lds > 60 * 1024) return EAGLE_ERR_UNSUPPORTED;
+  if (a.hd != 64 && a.hd != 128) return EAGLE_ERR_UNSUPPORTED;
   timer_begin(timer, ST_ATTN, s);
-  hipLaunchKernelGGL(tree_attn_f32_kernel, dim3(total_nodes * a.hq), dim3(64), lds, s, a);
+  hipLaunchKernelGGL(tree_attn_f32_kernel, dim3(total_nodes * a.hq), dim3(64), 0, s, a);
   timer_end(timer, s);
   return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
 }

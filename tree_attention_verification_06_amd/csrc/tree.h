@@ -44,7 +44,8 @@ struct AcceptArgs {
 };
 
 int launch_tree_build(int batch, const int32_t* tree_off, const int32_t* parent, const int32_t* prefix_len, int mw,
-                      uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* status, hipStream_t s);
+                      int max_nodes, int total_nodes, uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* status,
+                      hipStream_t s);
 int launch_accept_commit(const AcceptArgs& a, int batch, hipStream_t s);
 int launch_sample_prep(const int32_t* tree_off, const int32_t* parent, int batch, int total, int32_t* gparent,
                        int32_t* row_tree, hipStream_t s);

@@ -17,8 +17,9 @@ __device__ __forceinline__ void set_status(int32_t* st, int code) {
 
 // One workgroup (128 threads) per tree; node i handled by thread i, i + 128, ...
 __global__ __launch_bounds__(128) void tree_build_kernel(const int32_t* tree_off, const int32_t* parent,
-                                                         const int32_t* prefix_len, int mw, uint64_t* anc,
-                                                         int32_t* depth, int32_t* pos, int32_t* status) {
+                                                         const int32_t* prefix_len, int mw, int max_nodes,
+                                                         int total_nodes, uint64_t* anc, int32_t* depth,
+                                                         int32_t* pos, int32_t* status) {
   // the tree's parent array is staged in LDS (one round of loads) and every ancestor walk
   // runs there, instead of one dependent global load per level of depth
   __shared__ int s_bad;
@@ -26,7 +27,12 @@ __global__ __launch_bounds__(128) void tree_build_kernel(const int32_t* tree_off
   const int b = blockIdx.x;
   const int off = tree_off[b];
   const int N = tree_off[b + 1] - off;
-  if (threadIdx.x == 0) s_bad = (N < 1 || N > 64 * mw || N > 128) ? EAGLE_ERR_CAPACITY : 0;
+  // a tree outside the caller's rows, or larger than the mask words or max_nodes (which
+  // sizes the attention grid) is refused and nothing of it is written
+  if (threadIdx.x == 0)
+    s_bad = (off < 0 || N < 1 || off + N > total_nodes || N > 64 * mw || N > 128 || N > max_nodes)
+                ? EAGLE_ERR_CAPACITY
+                : 0;
   __syncthreads();
   for (int i = threadIdx.x; i < N && !s_bad; i += blockDim.x) {
     const int p = parent[off + i];
@@ -131,18 +137,15 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptArgs a) {
   __shared__ uint64_t s_match[2];
   __shared__ unsigned long long s_best;
   __shared__ int s_path[NMAX + 1];
-  __shared__ int s_L, s_leaf, s_P, s_ok;
+  __shared__ int s_L, s_leaf, s_P, s_ok, s_bad;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int off = a.tree_off[b];
   const int N = a.tree_off[b + 1] - off;
   const int mw = a.mw;
   if (N < 1 || N > 64 * mw || N > NMAX) {
-    if (tid == 0) {
-      set_status(a.status, EAGLE_ERR_CAPACITY);
-      a.accept_len[b] = -1;
-      a.next_token[b] = -1;
-    }
+    if (tid == 0) set_status(a.status, EAGLE_ERR_CAPACITY);
+    reject_sequence(a, b);
     return;
   }
   for (int i = tid; i < N; i += blockDim.x) {
@@ -158,8 +161,33 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(AcceptArgs a) {
   if (tid == 0) {
     s_best = 0ull;
     s_P = a.prefix_len[b];
+    s_bad = 0;
   }
   __syncthreads();
+  // the tree must be well formed (parent[0] = -1, parent[i] in [0, i)) and its depth and
+  // ancestor words must be the encoding of that parent array: a malformed tree leaves them
+  // zeroed or stale, and a stale depth would otherwise pick a leaf and commit a path
+  for (int i = tid; i < N; i += blockDim.x) {
+    const int p = s_par[i];
+    bool bad;
+    if (i == 0) {
+      bad = p != -1 || s_dep[0] != 0 || s_anc[0][0] != 1ull || s_anc[0][1] != 0ull;
+    } else {
+      bad = p < 0 || p >= i;
+      if (!bad) {
+        const uint64_t self0 = (i >> 6) == 0 ? 1ull << (i & 63) : 0ull;
+        const uint64_t self1 = (i >> 6) == 1 ? 1ull << (i & 63) : 0ull;
+        bad = s_dep[i] != s_dep[p] + 1 || s_anc[i][0] != (s_anc[p][0] | self0) || s_anc[i][1] != (s_anc[p][1] | self1);
+      }
+    }
+    if (bad) atomicCAS(&s_bad, 0, 1);
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0) set_status(a.status, EAGLE_ERR_TREE);
+    reject_sequence(a, b);
+    return;
+  }
   // match bits: the root always matches; node j matches iff its token is the target's
   // argmax at its parent
   for (int i = tid; i < N; i += blockDim.x) {
@@ -392,9 +420,10 @@ __global__ __launch_bounds__(256) void accept_sample_kernel(AcceptArgs a) {
 }  // namespace
 
 int launch_tree_build(int batch, const int32_t* tree_off, const int32_t* parent, const int32_t* prefix_len, int mw,
-                      uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* status, hipStream_t s) {
-  hipLaunchKernelGGL(tree_build_kernel, dim3(batch), dim3(128), 0, s, tree_off, parent, prefix_len, mw, anc, depth,
-                     pos, status);
+                      int max_nodes, int total_nodes, uint64_t* anc, int32_t* depth, int32_t* pos, int32_t* status,
+                      hipStream_t s) {
+  hipLaunchKernelGGL(tree_build_kernel, dim3(batch), dim3(128), 0, s, tree_off, parent, prefix_len, mw, max_nodes,
+                     total_nodes, anc, depth, pos, status);
   return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
 }
 
