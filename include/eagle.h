@@ -223,6 +223,31 @@ int eagle_tree_verify(const eagle_dims* dims, const eagle_layer_w* layer, const 
                       int32_t* argmax, float* maxlogit, float* dbg_attn, float* dbg_logits,
                       void* workspace, size_t ws_bytes, eagle_timer* timer, void* stream);
 
+/* eagle_tree_verify_noalloc: eagle_tree_verify for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments minus workspace and ws_bytes, same arithmetic,
+ * outputs and host errors.  Its scratch is a buffer of EAGLE_NOALLOC_MAX_BYTES (32 MiB)
+ * inside the library: one copy per GPU, held from the first call on that GPU until the
+ * process ends.  A call whose eagle_workspace_size(0, ...) exceeds that returns
+ * EAGLE_ERR_WORKSPACE and enqueues nothing (the 8B layer with one 60-node tree and
+ * max_prefix 2048 needs 21 MiB; the 70B layer or batch-16 shapes do not fit: use
+ * eagle_tree_verify with a workspace).  Every call on a GPU uses the same buffer, so calls
+ * that overlap on one GPU (different streams, threads or processes sharing no order) race
+ * and give wrong results; calls ordered on one stream are fine.  Each call clears the
+ * counters it needs with a fill kernel (no memset node).  The first call on each device
+ * resolves the buffer's address (hipGetSymbolAddress, no allocation); make it outside
+ * graph capture.  Errors: as eagle_tree_verify; EAGLE_ERR_HIP if the address cannot be
+ * resolved. */
+#define EAGLE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+int eagle_tree_verify_noalloc(const eagle_dims* dims, const eagle_layer_w* layer, const void* final_ln,
+                              const void* w_lm, int32_t batch, const int32_t* tree_off, int32_t total_nodes,
+                              int32_t max_nodes, const void* x_in, const void* embed, const int32_t* tokens,
+                              const uint64_t* anc, int32_t mask_words, const int32_t* pos,
+                              const int32_t* prefix_len, int32_t max_prefix, const void* k_cache,
+                              const void* v_cache, const eagle_cache_layout* cache, void* k_tree, void* v_tree,
+                              float* h_out, int32_t* argmax, float* maxlogit, float* dbg_attn, float* dbg_logits,
+                              eagle_timer* timer, void* stream);
+
 /* ---- acceptance and KV commit -------------------------------------------
  * Method: "Speculative decoding with EAGLE", Deep dive and FAQ (keep the
  * longest correct prefix; accepted tokens equal the target's choice, hence

@@ -282,3 +282,24 @@ def test_paged_cache_layout_host_errors():
                                    8, 128, 0, FAKE, None, 4096, None, 16, FAKE, FAKE, FAKE, FAKE, None, None)
         if want != A.EAGLE_OK:
             assert st == want, (kw, st)
+
+
+def test_verify_noalloc_refuses_oversized_requests_on_the_host():
+    """The entry point that allocates nothing refuses, before touching the GPU, any shape
+    whose scratch would exceed the library's per-GPU buffer (here the 8B layer with 16 trees
+    of 60 nodes: 162 MiB against 32 MiB), and runs the ordinary argument checks first."""
+    from workloads.configs import LLAMA8B
+    need = A.eagle_workspace_size(0, LLAMA8B, 16, 960, 60, 2048)
+    assert need > A.NOALLOC_MAX_BYTES
+    assert A.eagle_workspace_size(0, LLAMA8B, 1, 60, 60, 2048) <= A.NOALLOC_MAX_BYTES
+
+    def call(B, total, maxn, w_lm=FAKE):
+        d = A.dims_struct(LLAMA8B)
+        lw = A.EagleLayerW(4096, 4096, 4096, 4096, 4096, 4096, 4096, 0)
+        cl = A.EagleCacheLayout(1 << 20, 1 << 16, 128, 4096)
+        return E.lib().eagle_tree_verify_noalloc(ctypes.byref(d), ctypes.byref(lw), FAKE, w_lm, B, FAKE, total, maxn,
+                                                 FAKE, None, None, FAKE, 1, FAKE, FAKE, 2048, FAKE, FAKE,
+                                                 ctypes.byref(cl), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None)
+    assert call(16, 960, 60) == A.EAGLE_ERR_WORKSPACE
+    assert call(1, 60, 60, w_lm=None) == A.EAGLE_ERR_ARG
+    assert call(0, 60, 60) == A.EAGLE_ERR_ARG

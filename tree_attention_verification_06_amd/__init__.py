@@ -15,10 +15,12 @@ from ._abi import (EAGLE_BF16, EAGLE_F32, EAGLE_OK, EagleError, Timer, eagle_acc
                    eagle_accept_commit_sample, eagle_draft_expand, eagle_draft_pool, eagle_fuse_features,
                    eagle_pack_fragments, eagle_tree_build, eagle_tree_verify, eagle_tree_verify_sample,
                    eagle_workspace_init, eagle_workspace_size, lib, status_str, EagleDraftParams, STAGES, LIB_PATH,
-                   eagle_tree_verify_layers, eagle_accept_commit_layers, eagle_draft_kv_commit, PagedCache)
+                   eagle_tree_verify_layers, eagle_accept_commit_layers, eagle_draft_kv_commit, PagedCache,
+                   eagle_tree_verify_noalloc)
 
 __all__ = ["EAGLE_BF16", "EAGLE_F32", "EAGLE_OK", "EagleError", "Timer", "eagle_accept_commit",
            "eagle_accept_commit_sample", "eagle_draft_expand", "eagle_draft_pool", "eagle_fuse_features",
            "eagle_pack_fragments", "eagle_tree_build", "eagle_tree_verify", "eagle_tree_verify_sample",
            "eagle_workspace_init", "eagle_workspace_size", "lib", "status_str", "EagleDraftParams", "STAGES",
-           "LIB_PATH", "eagle_tree_verify_layers", "eagle_accept_commit_layers", "eagle_draft_kv_commit", "PagedCache"]
+           "LIB_PATH", "eagle_tree_verify_layers", "eagle_accept_commit_layers", "eagle_draft_kv_commit", "PagedCache",
+           "eagle_tree_verify_noalloc"]

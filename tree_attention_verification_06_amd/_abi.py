@@ -94,6 +94,9 @@ PROTOTYPES = {
     "eagle_tree_verify": (_I, [ctypes.POINTER(EagleDims), ctypes.POINTER(EagleLayerW), _P, _P, _I, _P, _I, _I,
                                _P, _P, _P, _P, _I, _P, _P, _I, _P, _P, ctypes.POINTER(EagleCacheLayout), _P, _P,
                                _P, _P, _P, _P, _P, _P, _S, _P, _P]),
+    "eagle_tree_verify_noalloc": (_I, [ctypes.POINTER(EagleDims), ctypes.POINTER(EagleLayerW), _P, _P, _I, _P, _I,
+                                       _I, _P, _P, _P, _P, _I, _P, _P, _I, _P, _P,
+                                       ctypes.POINTER(EagleCacheLayout), _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "eagle_accept_commit": (_I, [_I, _P, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
                                  ctypes.POINTER(EagleCacheLayout), _I, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P,
                                  _P, _P]),
@@ -226,6 +229,25 @@ def eagle_tree_verify(dims, layer, final_ln, w_lm, tree_off, x_in, embed, tokens
                                  _p(dbg_logits), _p(workspace), workspace.numel() * workspace.element_size(),
                                  _t(timer), _stream(stream))
     _check(st, "eagle_tree_verify")
+
+
+NOALLOC_MAX_BYTES = 32 << 20  # EAGLE_NOALLOC_MAX_BYTES
+
+
+def eagle_tree_verify_noalloc(dims, layer, final_ln, w_lm, tree_off, x_in, embed, tokens, anc, mask_words, pos,
+                              prefix_len, k_cache, v_cache, k_tree, v_tree, h_out, argmax, maxlogit, *, total_nodes,
+                              max_nodes, max_prefix, dbg_attn=None, dbg_logits=None, timer=None, stream=None):
+    """eagle_tree_verify without a workspace: the library's own per-GPU scratch is used."""
+    d = dims_struct(dims) if not isinstance(dims, EagleDims) else dims
+    lw = layer_struct(layer) if not isinstance(layer, EagleLayerW) else layer
+    cl = cache_struct(k_cache)
+    B = tree_off.numel() - 1
+    st = lib().eagle_tree_verify_noalloc(ctypes.byref(d), ctypes.byref(lw), _p(final_ln), _p(w_lm), B, _p(tree_off),
+                                         total_nodes, max_nodes, _p(x_in), _p(embed), _p(tokens), _p(anc),
+                                         mask_words, _p(pos), _p(prefix_len), max_prefix, _p(k_cache), _p(v_cache),
+                                         ctypes.byref(cl), _p(k_tree), _p(v_tree), _p(h_out), _p(argmax),
+                                         _p(maxlogit), _p(dbg_attn), _p(dbg_logits), _t(timer), _stream(stream))
+    _check(st, "eagle_tree_verify_noalloc")
 
 
 def layers_array(layers, layout=0):

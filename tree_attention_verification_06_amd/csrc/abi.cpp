@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "attn.h"
@@ -182,11 +183,11 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* layers, int n_layers, 
                 int max_prefix, const void* k_cache, const void* v_cache, const eagle_cache_layout* cache,
                 void* k_tree, void* v_tree, float* h_out, int32_t* argmax, float* maxlogit, float* dbg_attn,
                 float* dbg_logits, void* ws, size_t ws_bytes, eagle_timer* timer, hipStream_t s,
-                const SampleOut* so = nullptr) {
+                const SampleOut* so = nullptr, int (*scratch_of)(void**) = nullptr) {
   int rc = check_dims(d);
   if (rc) return rc;
   if (!layers || !w_lm || !tree_off || !anc || !pos || !prefix_len || !k_cache || !v_cache || !cache || !k_tree ||
-      !v_tree || !h_out || !ws)
+      !v_tree || !h_out || (!ws && !scratch_of))
     return EAGLE_ERR_ARG;
   if (n_layers < 1 || n_layers > 1024) return EAGLE_ERR_ARG;
   // a stack needs the pre-norm layer with an MLP: the residual stream of layer l > 0 is the
@@ -215,6 +216,10 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* layers, int n_layers, 
   if (check_cache_layout(cache)) return EAGLE_ERR_ARG;
   const VerifyLayout L = plan_verify(d, B, total_nodes, max_nodes, max_prefix, so != nullptr);
   if (ws_bytes < L.total) return EAGLE_ERR_WORKSPACE;
+  if (scratch_of) {  // the library's own buffer, resolved once every argument has passed
+    rc = scratch_of(&ws);
+    if (rc) return rc;
+  }
   char* w = (char*)ws;
   const int dt = d->dtype;
   const int H = d->hidden, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim, F = d->ffn, V = d->vocab;
@@ -242,6 +247,13 @@ int verify_impl(const eagle_dims* d, const eagle_layer_w* layers, int n_layers, 
     g.counters = counters;
   };
 
+  if (scratch_of) {
+    // the split-K counters, argmax keys and completion counter must start at zero; every
+    // call leaves them so, but a shared buffer is cleared anyway (a fill kernel, so the
+    // call can be captured into a graph)
+    rc = launch_fill_zero(w + L.counters, L.done + 4 - L.counters, s);
+    if (rc) return rc;
+  }
   int32_t* gparent = so ? (int32_t*)(w + L.gparent) : nullptr;
   int32_t* row_tree = so ? (int32_t*)(w + L.row_tree) : nullptr;
   float4* samp_part = so ? (float4*)(w + L.samp_part) : nullptr;
@@ -549,6 +561,33 @@ int commit_args(AcceptArgs& a, int batch, const int32_t* tree_off, int max_nodes
   return EAGLE_OK;
 }
 
+// ---- scratch of the entry point that allocates nothing ---------------------------------
+// One copy of this array exists on every GPU the library runs on, from the first use on
+// that GPU until the process ends.  In host code its name is only a stand-in: the device
+// address is taken once per device with hipGetSymbolAddress and kept in scratch_dev[].
+static __device__ __align__(256) unsigned char scratch[EAGLE_NOALLOC_MAX_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (resolved on the first call there).
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return EAGLE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return EAGLE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return EAGLE_ERR_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return EAGLE_OK;
+}
+}  // namespace
+
 }  // namespace eagle
 
 using namespace eagle;
@@ -592,6 +631,20 @@ int eagle_tree_verify(const eagle_dims* dims, const eagle_layer_w* layer, const 
   return verify_impl(dims, layer, 1, 0, final_ln, w_lm, batch, tree_off, total_nodes, max_nodes, x_in, embed,
                      tokens, anc, mask_words, pos, prefix_len, max_prefix, k_cache, v_cache, cache, k_tree, v_tree,
                      h_out, argmax, maxlogit, dbg_attn, dbg_logits, workspace, ws_bytes, timer, (hipStream_t)stream);
+}
+
+int eagle_tree_verify_noalloc(const eagle_dims* dims, const eagle_layer_w* layer, const void* final_ln,
+                              const void* w_lm, int32_t batch, const int32_t* tree_off, int32_t total_nodes,
+                              int32_t max_nodes, const void* x_in, const void* embed, const int32_t* tokens,
+                              const uint64_t* anc, int32_t mask_words, const int32_t* pos,
+                              const int32_t* prefix_len, int32_t max_prefix, const void* k_cache,
+                              const void* v_cache, const eagle_cache_layout* cache, void* k_tree, void* v_tree,
+                              float* h_out, int32_t* argmax, float* maxlogit, float* dbg_attn, float* dbg_logits,
+                              eagle_timer* timer, void* stream) {
+  return verify_impl(dims, layer, 1, 0, final_ln, w_lm, batch, tree_off, total_nodes, max_nodes, x_in, embed,
+                     tokens, anc, mask_words, pos, prefix_len, max_prefix, k_cache, v_cache, cache, k_tree, v_tree,
+                     h_out, argmax, maxlogit, dbg_attn, dbg_logits, nullptr, EAGLE_NOALLOC_MAX_BYTES, timer,
+                     (hipStream_t)stream, nullptr, scratch_ptr);
 }
 
 int eagle_tree_verify_layers(const eagle_dims* dims, int32_t n_layers, const eagle_layer_w* layers,
