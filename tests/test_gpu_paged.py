@@ -3,10 +3,16 @@ reads or writes a cache gives bit-identical results whether the cache is contigu
 pool of pages addressed through a block table (the same arithmetic in the same order; only
 the addresses differ), commits land in the right pages and nowhere else, a sequence that
 joins a running batch can reuse the pages of one that left, and a bad page id is refused
-on the device instead of being written through."""
+on the device instead of being written through.  The verification and the continuous-
+batching steps on pages are also compared with the fp64 oracle directly: verify outputs
+within the bf16 tolerance, acceptance exact, and the pool read back through the block
+table equal to the oracle's committed cache (committed slots within the tolerance, every
+other slot unchanged)."""
 import numpy as np
 import pytest
 
+import oracle
+from tests._gpu import TOL_BF16, check_verify, np_of, rel_err
 from workloads import DraftParams, make_workload, mini_dims, stack_workload, trees as T
 from workloads.configs import TID, normal_tensor
 from workloads.device import to_tensor, upload
@@ -65,13 +71,52 @@ def _tables(B, cap, n_pages, seed):
     return torch.tensor(perm, dtype=torch.int32, device="cuda"), maxb
 
 
+def _plant_from_oracle(parents, tokens, tree_off, ref, b, depth):
+    """Set the tokens on the root path of tree b's first node of the given depth whose
+    parents' oracle argmax are all decisive (top-2 gap > 0.05) to that argmax."""
+    par = parents[b]
+    o = int(tree_off[b])
+    dep = T.depths(par)
+    for j in [i for i in range(len(par)) if dep[i] == depth]:
+        path = []
+        k = j
+        while k > 0:
+            path.append(k)
+            k = par[k]
+        if all(ref["gap"][o + par[k]] > 0.05 for k in path):
+            for k in path:
+                tokens[o + k] = ref["argmax"][o + par[k]]
+            return j
+    raise AssertionError("no decisive path to plant")
+
+
+def _gpu_outputs(v, dbg_attn):
+    return dict(k_tree=np_of(v.k_tree), v_tree=np_of(v.v_tree), attn=np_of(dbg_attn), h=np_of(v.h),
+                maxlogit=np_of(v.maxlogit), argmax=np_of(v.argmax))
+
+
+def _check_commit_against_oracle(pool_readback, ref_cache, committed, label, limit=None):
+    """pool_readback, ref_cache [B][Hkv][cap][D] (GPU values as float, oracle fp64);
+    committed[b] = the slots the step committed for sequence b.  Committed slots within
+    the bf16 tolerance, every other slot below limit[b] (default: all) identical (past it,
+    a page taken over from another sequence may still hold that sequence's values)."""
+    got = np.asarray(pool_readback, dtype=np.float64)
+    for b, slots in enumerate(committed):
+        lim = got.shape[2] if limit is None else max(limit[b], max(slots, default=-1) + 1)
+        others = [s for s in range(lim) if s not in slots]
+        assert np.array_equal(got[b][:, others], ref_cache[b][:, others]), (label, b)
+        if slots:
+            e = rel_err(got[b][:, slots], ref_cache[b][:, slots])
+            assert e <= TOL_BF16, (label, b, e)
+
+
 def test_paged_verify_and_commit_bit_identical():
     import torch
     from tree_attention_verification_06_amd._abi import PagedCache
     from tree_attention_verification_06_amd.runner import TreeVerifier
     dims = mini_dims()
     parents = [T.static_tree_60(), T.random_tree(np.random.default_rng(3), 25), T.chain(10)]
-    wl = make_workload(2, seed=31, dims=dims, batch=3, prefix=[200, 77, 130], parents=parents)
+    wl = make_workload(2, seed=32, dims=dims, batch=3, prefix=[200, 77, 130], parents=parents)
     t = upload(wl)
     M, cap = wl.n_nodes, wl.cache_cap
     table, maxb = _tables(3, cap, 3 * (-(-cap // PS)) + 5, 31)
@@ -87,21 +132,21 @@ def test_paged_verify_and_commit_bit_identical():
                       max_prefix=cap)
     vpg = TreeVerifier(dims, t["weights"], PagedCache(kp, table, PS), PagedCache(vp, table, PS), batch=3,
                        max_total_nodes=M, max_nodes=60, max_prefix=cap)
+    dbg = torch.zeros(M, dims.n_q_heads * dims.head_dim, dtype=torch.float32, device="cuda")
     for v, pl in ((vc, plen_c), (vpg, plen_p)):
         v.encode(t["tree_off"], t["parent"], pl, M)
-        v.verify(t["tree_off"], t["tokens"], pl, M, x=t["x"])
+        v.verify(t["tree_off"], t["tokens"], pl, M, x=t["x"], dbg_attn=dbg if v is vpg else None)
     torch.cuda.synchronize()
     for k in ("h", "argmax", "maxlogit", "k_tree", "v_tree"):
         assert torch.equal(getattr(vc, k), getattr(vpg, k)), k
-    # plant a depth-3 path in tree 0 from the GPU's argmax (node inputs are given, so tokens
+    # the paged run against the oracle on the same (contiguous) inputs
+    ref = oracle.verify_forward(dims, wl.weights, wl.x, parents, wl.prefix_len, wl.k_cache, wl.v_cache,
+                                want_logits=False)
+    _log(check_verify(_gpu_outputs(vpg, dbg), ref, dims, label="paged-verify"))
+    # plant a depth-3 path in tree 0 from the oracle's argmax (node inputs are given, so tokens
     # do not change the target's choices), then accept and commit in both layouts
-    g = vc.argmax.cpu().numpy()
     tok = wl.tokens.copy()
-    dep = T.depths(parents[0])
-    j = [i for i in range(60) if dep[i] == 3][0]
-    while j > 0:
-        tok[j] = g[parents[0][j]]
-        j = parents[0][j]
+    _plant_from_oracle(parents, tok, wl.tree_off, ref, 0, 3)
     tt = to_tensor(tok)
     for v, pl in ((vc, plen_c), (vpg, plen_p)):
         v.accept(t["tree_off"], t["parent"], tt, pl)
@@ -114,6 +159,21 @@ def test_paged_verify_and_commit_bit_identical():
     assert torch.equal(_from_pages(kp, table, cap), t["k_cache"])
     assert torch.equal(_from_pages(vp, table, cap), t["v_cache"])
     assert torch.equal(kp[spare], kp0[spare])
+    # acceptance and commit against the oracle's own: its argmax, its K/V in its cache copy
+    acc = vpg.accept_len.cpu().numpy()
+    path = vpg.path.cpu().numpy()
+    outt = vpg.out_tokens.cpu().numpy()
+    ref_k = oracle.as_f64(wl.k_cache).copy()
+    ref_v = oracle.as_f64(wl.v_cache).copy()
+    committed = []
+    for b, (L, pth, out, nt, leaf) in enumerate(oracle.accept_batch(parents, tok, ref["argmax"], ref["encs"])):
+        o, P = int(wl.tree_off[b]), int(wl.prefix_len[b])
+        assert acc[b] == L and path[b, :L + 1].tolist() == pth and outt[b, :L + 1].tolist() == out, b
+        assert int(plen_p[b]) == oracle.commit_sequence(ref_k[b], ref_v[b], ref["k_tree"][o:], ref["v_tree"][o:],
+                                                        pth, P)
+        committed.append(list(range(P, P + L + 1)))
+    _check_commit_against_oracle(_from_pages(kp, table, cap).float().cpu().numpy(), ref_k, committed, "paged-k")
+    _check_commit_against_oracle(_from_pages(vp, table, cap).float().cpu().numpy(), ref_v, committed, "paged-v")
 
 
 def test_paged_stack_and_draft_kv_bit_identical():
@@ -199,7 +259,11 @@ def test_paged_draft_expand_bit_identical():
 def test_continuous_batching_reuses_pages():
     """Step 1 verifies {A, B}; A leaves and C joins on A's freed pages; step 2 verifies
     {B, C} on the paged pool and must equal a contiguous run of the same batch, whose caches
-    hold B after step 1 and C's prefix."""
+    hold B after step 1 and C's prefix.  Both steps are also checked against the oracle run
+    as its own decode loop: its verification of {A, B}, its acceptance and commit into its
+    own caches, then its verification of {B, C} on B's cache as it committed it and C's
+    prefix; the pool read back through the block tables must equal the oracle's caches
+    (committed slots within the tolerance, all others unchanged)."""
     import torch
     from tree_attention_verification_06_amd.runner import PagePool, TreeVerifier
     dims = mini_dims()
@@ -209,11 +273,21 @@ def test_continuous_batching_reuses_pages():
         wl = make_workload(2, seed=seed, dims=dims, batch=1, prefix=[P],
                            parents=[T.random_tree(np.random.default_rng(seed), 20)])
         seqs[name] = wl
-    w = upload(seqs["A"])["weights"]  # one model for every sequence
+    weights = seqs["A"].weights  # one model for every sequence
+    w = upload(seqs["A"])["weights"]
     pool = PagePool(n_pages=10, page_size=PS, max_blocks=cap // PS)
     Hkv, D = dims.n_kv_heads, dims.head_dim
     kpool = torch.zeros(10, Hkv, PS, D, dtype=torch.bfloat16, device="cuda")
     vpool = torch.zeros_like(kpool)
+    # the oracle's caches, one per sequence, [Hkv][cap][D] fp64
+    ocache = {}
+    for name, wl in seqs.items():
+        kk = np.zeros((Hkv, cap, D))
+        vv = np.zeros((Hkv, cap, D))
+        n = wl.k_cache.shape[2]
+        kk[:, :n] = oracle.as_f64(wl.k_cache[0])
+        vv[:, :n] = oracle.as_f64(wl.v_cache[0])
+        ocache[name] = [kk, vv, int(wl.prefix_len[0])]
 
     def admit(name):
         wl = seqs[name]
@@ -224,7 +298,7 @@ def test_continuous_batching_reuses_pages():
         _to_pages(src_k[:, :, :n], kpool, tb, n)
         _to_pages(src_v[:, :, :n], vpool, tb, n)
 
-    def step(names, caches, plen):
+    def step(names, caches, plen, dbg=None):
         wls = [seqs[n] for n in names]
         parents = [wl.parents[0] for wl in wls]
         sizes = [len(p) for p in parents]
@@ -236,33 +310,74 @@ def test_continuous_batching_reuses_pages():
         v = TreeVerifier(dims, w, caches[0], caches[1], batch=len(names), max_total_nodes=M, max_nodes=20,
                          max_prefix=cap)
         v.encode(off, par, plen, M)
-        v.verify(off, tok, plen, M, x=x)
+        v.verify(off, tok, plen, M, x=x, dbg_attn=dbg)
         v.accept(off, par, tok, plen)
         torch.cuda.synchronize()
         assert int(v.status.item()) == 0
         return v
 
+    def oracle_step(names, v, dbg, label):
+        """The oracle's step over its own caches; checks the GPU step v against it and
+        commits into the oracle's caches.  Returns the slots committed per sequence."""
+        wls = [seqs[n] for n in names]
+        parents = [wl.parents[0] for wl in wls]
+        kc = np.stack([ocache[n][0] for n in names])
+        vc = np.stack([ocache[n][1] for n in names])
+        plen = np.array([ocache[n][2] for n in names], dtype=np.int32)
+        x = np.concatenate([wl.x for wl in wls])
+        tok = np.concatenate([wl.tokens for wl in wls]).astype(np.int32)
+        ref = oracle.verify_forward(dims, weights, x, parents, plen, kc, vc, want_logits=False)
+        _log(check_verify(_gpu_outputs(v, dbg), ref, dims, label=label))
+        acc = v.accept_len.cpu().numpy()
+        path = v.path.cpu().numpy()
+        nxt = v.next_token.cpu().numpy()
+        sizes = np.concatenate([[0], np.cumsum([len(p) for p in parents])])
+        committed = []
+        for b, (L, pth, out, nt, leaf) in enumerate(oracle.accept_batch(parents, tok, ref["argmax"], ref["encs"])):
+            assert acc[b] == L and path[b, :L + 1].tolist() == pth and nxt[b] == nt, (label, b)
+            o, n = int(sizes[b]), names[b]
+            P = ocache[n][2]
+            ocache[n][2] = oracle.commit_sequence(ocache[n][0], ocache[n][1], ref["k_tree"][o:], ref["v_tree"][o:],
+                                                  pth, P)
+            committed.append(list(range(P, P + L + 1)))
+        return committed
+
+    def check_pool(names, committed, label):
+        tb = pool.table(names)
+        for which, src in ((0, kpool), (1, vpool)):
+            got = _from_pages(src, tb, cap).float().cpu().numpy()
+            want = np.stack([ocache[n][which] for n in names])
+            _check_commit_against_oracle(got, want, committed, f"{label}-{'kv'[which]}",
+                                         limit=[seqs[n].k_cache.shape[2] for n in names])
+
+    dbg = torch.zeros(40, dims.n_q_heads * dims.head_dim, dtype=torch.float32, device="cuda")
     admit("A")
     admit("B")
     tb1 = pool.table(["A", "B"])
     plen1 = to_tensor(np.array([200, 77], dtype=np.int32))
-    step(["A", "B"], (pool.paged(kpool, tb1), pool.paged(vpool, tb1)), plen1)
+    v1 = step(["A", "B"], (pool.paged(kpool, tb1), pool.paged(vpool, tb1)), plen1, dbg)
+    c1 = oracle_step(["A", "B"], v1, dbg, "cb-step1")
+    check_pool(["A", "B"], c1, "cb-step1")
     a_pages = list(pool.owned["A"])
     pool.release("A")
     admit("C")
     assert set(pool.owned["C"]) & set(a_pages), "C should reuse pages A released"
     tb2 = pool.table(["B", "C"])
     plen2 = to_tensor(np.array([int(plen1[1]), 130], dtype=np.int32))
+    assert int(plen1[1]) == ocache["B"][2]
     # contiguous reference of the same batch: B's cache after step 1 and C's prefix
     kc = _from_pages(kpool, tb2, cap)
     vc = _from_pages(vpool, tb2, cap)
     plen2c = plen2.clone()
-    vp = step(["B", "C"], (pool.paged(kpool, tb2), pool.paged(vpool, tb2)), plen2)
+    vp = step(["B", "C"], (pool.paged(kpool, tb2), pool.paged(vpool, tb2)), plen2, dbg)
+    c2 = oracle_step(["B", "C"], vp, dbg, "cb-step2")
     vcnt = step(["B", "C"], (kc, vc), plen2c)
     for k in ("h", "argmax", "k_tree", "accept_len", "path", "next_token"):
         assert torch.equal(getattr(vp, k), getattr(vcnt, k)), k
     assert torch.equal(plen2, plen2c)
     assert torch.equal(_from_pages(kpool, tb2, cap), kc)
+    # B carries step 1's committed slots too; C only step 2's
+    check_pool(["B", "C"], [c1[1] + c2[0], c2[1]], "cb-step2")
     _log("continuous batching: C reused pages", sorted(set(pool.owned["C"]) & set(a_pages)))
 
 
