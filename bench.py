@@ -2,15 +2,22 @@
 """Benchmark of the EAGLE tree-verification step on one MI355X.
 
 One step = eagle_tree_build + eagle_tree_verify + eagle_accept_commit over one batch of
-synthetic trees (the whole verification hot path), on the seeded random-init workload
-of the chosen configuration (default: the Llama-3-8B-shaped layer, 60-node static
-tree, 2048-token prefix, batch 1).  Prints one JSON line:
-  value        = tree-verify nodes/s (nodes verified per second of step time)
+synthetic trees (the whole verification hot path) on the seeded random-init workload of a
+configuration; the headline is the Llama-3-8B-shaped layer with one 60-node static tree and
+a 2048-token prefix.  The step is captured once into a HIP graph and replayed (its eager
+launch sequence is timed too); each timed step sits between two HIP events, and the mean,
+median and p90 of the step times are reported.  Prints one JSON line:
+  value          = tree-verify nodes/s of the headline configuration (nodes / mean step time)
   accepted_tok_s = accepted tokens (L + 1 per sequence) per second, measured
-  roofline     = the dominant kernel (LM head + fused argmax): algorithmic bytes per
-                 launch / its mean launch time from HIP events recorded in the timed
-                 region, against 8 TB/s
-  cpu_baseline = the fp64 CPU oracle on one full step of the same workload.
+  roofline       = the dominant kernel (LM head + fused argmax): algorithmic bytes per launch
+                   / its mean launch time from HIP events recorded in the timed region
+  step_roofline  = the step: sum over its kernels of max(bytes / 8 TB/s, flops / 2.5 PFLOP/s)
+                   against the measured step time
+  configs        = the same measurements for the other single-layer configurations (the tiny
+                   fp32 layer, the ragged batch of four dynamic trees, the 70B-shaped layer
+                   with a 32768-token prefix)
+  eagle_step     = the full EAGLE step (draft + verify + accept) at batch 16
+  cpu_baseline   = the fp64 CPU oracle on whole steps of the headline workload.
 Inputs are resident in HBM before timing starts; the KV cache grows by the committed
 tokens as a real decode loop does.
 """
@@ -24,6 +31,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
 
 
 def parse():
@@ -32,6 +40,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--other-configs", default="1,3,4",
+                    help="single-layer configurations measured besides --config ('' for none)")
+    ap.add_argument("--min-steps", type=int, default=50,
+                    help="timed steps per configuration are max(--steps, this)")
+    ap.add_argument("--no-graph", action="store_true", help="time the eager launch sequence only")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-nodes", type=int, default=0, help="0: one full step")
@@ -89,23 +102,55 @@ def measured_traffic(workload_name, layout):
     return None
 
 
-def step_roofline_bytes_flops(dims, wl):
-    """Algorithmic bytes and flops of one verification step (every weight once, KV prefix once,
-    tree K/V written once and read once, activations in and out once)."""
+def step_roofline_parts(dims, wl):
+    """Algorithmic bytes and flops of each kernel of one verification step: every weight once,
+    the KV prefix once, activations read once and written once (bf16 between GEMMs, the
+    residual stream in fp32), tree K/V written once and read once; flops 2 per MAC over the
+    real rows, attention 4 * Hq * D per visible key of each node (prefix + depth + 1)."""
     es = 2 if dims.dtype == "bf16" else 4
     H, Hq, Hkv, D, F, V = dims.hidden, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.ffn, dims.vocab
     M = wl.n_nodes
-    w = (Hq + 2 * Hkv) * D * H + H * Hq * D + 3 * F * H + V * H
-    kv = sum(int(p) for p in wl.prefix_len) * Hkv * D * 2 * es
-    act = M * H * es * 2 + M * (Hq + 2 * Hkv) * D * es * 2 + M * H * 4 * 2
-    byts = w * es + kv + act
-    flops = 2 * M * w
+    qkv = (Hq + 2 * Hkv) * D
+    parts = {}
+    parts["qkv"] = (qkv * H * es + M * H * es + M * qkv * es, 2 * M * qkv * H)
+    att_flops = 0
     for b, par in enumerate(wl.parents):
         d = np.zeros(len(par), dtype=np.int64)
         for i in range(1, len(par)):
             d[i] = d[par[i]] + 1
-        flops += int(np.sum(4 * Hq * D * (int(wl.prefix_len[b]) + d + 1)))
-    return byts, flops
+        att_flops += int(np.sum(4 * Hq * D * (int(wl.prefix_len[b]) + d + 1)))
+    kv = sum(int(p) for p in wl.prefix_len) * Hkv * D * 2 * es
+    parts["attention"] = (kv + M * qkv * es + M * Hq * D * es, att_flops)
+    parts["o_proj"] = (H * Hq * D * es + M * Hq * D * es + M * H * es + M * H * 4, 2 * M * H * Hq * D)
+    if F > 0:
+        parts["gate_up"] = (2 * F * H * es + M * H * es + M * F * es, 4 * M * F * H)
+        parts["down"] = (F * H * es + M * F * es + M * H * 4 + M * H * 4, 2 * M * F * H)
+    parts["lm_head"] = (V * H * es + M * H * es + M * 8, 2 * M * V * H)
+    return parts
+
+
+def step_roofline(dims, wl, ms_step):
+    """T_roof = sum over kernels of max(bytes / HBM peak, flops / bf16 MFMA peak) (the fp32
+    layer uses the fp32 vector peak, 157.3 TFLOP/s), against the measured step time."""
+    peak_f = MFMA_BF16_PEAK_TFLOPS if dims.dtype == "bf16" else FP32_PEAK_TFLOPS
+    parts = step_roofline_parts(dims, wl)
+    kern = {}
+    t_hbm = t_mfma = 0.0
+    for k, (b, f) in parts.items():
+        tb = b / (HBM_PEAK_GBS * 1e9) * 1e3
+        tf = f / (peak_f * 1e12) * 1e3
+        kern[k] = {"bytes": int(b), "flops": int(f), "bound": "hbm" if tb >= tf else "mfma",
+                   "t_roof_ms": round(max(tb, tf), 6)}
+        if tb >= tf:
+            t_hbm += tb
+        else:
+            t_mfma += tf
+    t_roof = t_hbm + t_mfma
+    return {"bound": "hbm" if t_hbm >= t_mfma else "mfma",
+            "algorithmic_bytes": int(sum(b for b, _ in parts.values())),
+            "algorithmic_flops": int(sum(f for _, f in parts.values())),
+            "t_roof_ms": round(t_roof, 5), "t_roof_hbm_ms": round(t_hbm, 5), "t_roof_mfma_ms": round(t_mfma, 5),
+            "frac": round(t_roof / ms_step, 4), "kernels": kern}
 
 
 def draft_roofline_bytes_flops(dims, p, batch, prefix_len):
@@ -550,13 +595,18 @@ def bench_eagle3(args, wl, st, t, prefix0, feat, tok):
 def cpu_baseline(wl, sample_nodes, min_seconds=10.0, max_steps=100):
     """The fp64 oracle (as it is) on the same workload, on this host's cores: whole
     verification steps (tree encode, layer forward, LM-head argmax, accept, commit)
-    repeated until at least min_seconds of CPU work have been timed."""
+    repeated until at least min_seconds of CPU work have been timed.  The commit writes into
+    cache copies made once before the timed loop (each step commits the same slots)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
     except Exception:
         threads = 1
+    try:
+        host_cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        host_cores = os.cpu_count() or 1
     parents = wl.parents
     x = wl.x
     tokens = wl.tokens
@@ -565,6 +615,8 @@ def cpu_baseline(wl, sample_nodes, min_seconds=10.0, max_steps=100):
         x = x[:sample_nodes]
         tokens = tokens[:sample_nodes]
     n = sum(len(p) for p in parents)
+    kc = wl.k_cache.copy()
+    vc = wl.v_cache.copy()
     steps = 0
     acc = 0
     t0 = time.perf_counter()
@@ -572,8 +624,6 @@ def cpu_baseline(wl, sample_nodes, min_seconds=10.0, max_steps=100):
         out = oracle.verify_forward(wl.dims, wl.weights, x, parents, wl.prefix_len[:len(parents)], wl.k_cache,
                                     wl.v_cache, want_logits=False)
         res = oracle.accept_batch(parents, tokens, out["argmax"], out["encs"])
-        kc = wl.k_cache.copy()
-        vc = wl.v_cache.copy()
         off = 0
         for b, (L, path, *_rest) in enumerate(res):
             oracle.commit_sequence(kc[b], vc[b], out["k_tree"][off:off + len(parents[b])],
@@ -582,10 +632,174 @@ def cpu_baseline(wl, sample_nodes, min_seconds=10.0, max_steps=100):
         acc += sum(r[0] + 1 for r in res)
         steps += 1
     dt = time.perf_counter() - t0
-    return dict(value=n * steps / dt, unit="nodes/s", cores=threads, kind="oracle",
+    return dict(value=n * steps / dt, unit="nodes/s", cores=threads, host_cores=host_cores,
+                blas_threads=threads, kind="oracle",
                 sample=f"{steps} full verification steps of the same workload ({n} nodes each: tree encode, "
-                       f"fp64 layer forward, LM-head argmax, accept, commit)",
+                       f"fp64 layer forward, LM-head argmax, accept, commit into cache copies made once)",
                 seconds=round(dt, 2), accepted_tok_s=acc / dt)
+
+
+def _stats(ms):
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 5), "median": round(float(np.median(a)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "min": round(float(a.min()), 5), "n": int(len(a))}
+
+
+def _timed_steps(run_one, n, stream):
+    """Per-step times (ms) of n steps, each between two HIP events on `stream`; returns the
+    list and the time from the first event to the last."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        run_one()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)], ev[0].elapsed_time(ev[n])
+
+
+def bench_verify(cfg, args, *, steps, warmup, headline=False):
+    """Tree build + verify + accept/commit on configuration cfg: the eager launch sequence
+    (with HIP events around the LM head for its per-launch roofline) and the same step
+    captured once into a HIP graph and replayed; per-kernel diagnostic times; accepted
+    tokens per step, measured and with one planted depth-3 path."""
+    import torch
+    import tree_attention_verification_06_amd as E
+    from tree_attention_verification_06_amd.runner import TreeVerifier
+    from workloads import make_workload, trees as T
+    from workloads.device import upload
+
+    n_stats = max(steps, args.min_steps)
+    t0 = time.perf_counter()
+    wl = make_workload(cfg, seed=args.seed, cache_slack=(max(warmup, n_stats) + 24) * 2)
+    dims = wl.dims
+    log(f"workload {wl.name}: {wl.n_nodes} nodes, batch {wl.batch}, generated in {time.perf_counter() - t0:.1f}s")
+    t = upload(wl)
+    torch.cuda.synchronize()
+    M = wl.n_nodes
+    max_nodes = max(len(p) for p in wl.parents)
+    weights, layout = laid_out(t["weights"], args) if dims.dtype == "bf16" else (t["weights"], 0)
+    v = TreeVerifier(dims, weights, t["k_cache"], t["v_cache"], batch=wl.batch, max_total_nodes=M,
+                     max_nodes=max_nodes, max_prefix=int(wl.prefix_len.max()), lm_layout=layout,
+                     weight_layout=layout)
+    prefix0 = t["prefix_len"].clone()
+    stream = torch.cuda.current_stream()
+
+    def step(timer=None):
+        v.step(t["tree_off"], t["parent"], t["tokens"], t["prefix_len"], M, x=t.get("x"), timer=timer)
+
+    def check_status(where):
+        st = int(v.status.item())
+        if st != 0:
+            raise RuntimeError(f"{wl.name} {where}: device status {st} ({E.status_str(st)})")
+
+    for _ in range(warmup):
+        step()
+    t["prefix_len"].copy_(prefix0)
+    # eager launches; HIP events around the dominant kernel (the LM head) only
+    timer = None if args.no_timer else E.Timer(capacity=4 * (n_stats + 1), stages=["lm_head"])
+    eager_ms, _ = _timed_steps(lambda: step(timer), n_stats, stream)
+    stages = timer.collect() if timer else {}
+    if timer:
+        timer.close()
+    check_status("eager")
+    # the step as one HIP graph, replayed
+    graph_ms = None
+    g_total = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        t["prefix_len"].copy_(prefix0)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(graph, stream=cs):
+                step()
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            graph.replay()
+        t["prefix_len"].copy_(prefix0)
+        graph_ms, g_total = _timed_steps(graph.replay, steps, stream)   # exactly `steps` timed steps
+        stats_ms = graph_ms
+        if n_stats > steps:
+            t["prefix_len"].copy_(prefix0)
+            stats_ms, _ = _timed_steps(graph.replay, n_stats, stream)
+        check_status("graph")
+        del graph
+    # per-kernel breakdown: a separate pass with events around every kernel (diagnostic)
+    t["prefix_len"].copy_(prefix0)
+    diag = E.Timer(capacity=16 * 11)
+    for _ in range(10):
+        step(diag)
+    torch.cuda.synchronize()
+    diag_stages = diag.collect()
+    diag.close()
+    # accepted tokens per step: the same steps again, reading accept_len after each (untimed)
+    t["prefix_len"].copy_(prefix0)
+    accepted = []
+    for _ in range(10):
+        step()
+        accepted.append(int((v.accept_len + 1).sum().item()))
+    acc_per_step = float(np.mean(accepted))
+    # planted variant: tokens along one depth-3 root path per tree set to the target's greedy
+    # choice (node inputs are given hidden states, so tokens do not change the target's argmax)
+    t["prefix_len"].copy_(prefix0)
+    step()
+    torch.cuda.synchronize()
+    g = v.argmax.cpu().numpy()
+    tokens = wl.tokens.copy()
+    for b, par in enumerate(wl.parents):
+        o = int(wl.tree_off[b])
+        d = T.depths(par)
+        cands = [i for i in range(len(par)) if d[i] == 3] or [max(range(len(par)), key=lambda i: d[i])]
+        j = cands[0]
+        while j > 0:
+            tokens[o + j] = g[o + par[j]]
+            j = par[j]
+    t_tokens = torch.from_numpy(tokens).cuda()
+    t["prefix_len"].copy_(prefix0)
+    v.step(t["tree_off"], t["parent"], t_tokens, t["prefix_len"], M, x=t.get("x"))
+    planted = int((v.accept_len + 1).sum().item())
+    check_status("planted")
+
+    timed = graph_ms if graph_ms is not None else eager_ms[:steps]
+    ms_per_step = float(np.mean(timed))
+    lm_ms, lm_n = stages.get("lm_head", (0.0, 0))
+    roof = None
+    if lm_n:
+        lm_avg = lm_ms / lm_n
+        ach = lm_head_bytes(dims, M) / (lm_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name, layout_name(args)),
+                "kernel": "gemm_bf16_kernel (LM head + fused row argmax)" if dims.dtype == "bf16" else
+                "gemm_f32_kernel (LM head + fused row argmax)",
+                "kernel_ms": round(lm_avg, 5), "bytes_per_launch": lm_head_bytes(dims, M),
+                "flops_per_launch": 2 * M * dims.hidden * dims.vocab,
+                "mfma_frac": round(2 * M * dims.hidden * dims.vocab / (lm_avg * 1e-3) / 1e12 /
+                                   (MFMA_BF16_PEAK_TFLOPS if dims.dtype == "bf16" else FP32_PEAK_TFLOPS), 4)}
+    out = {
+        "workload": wl.name, "batch": wl.batch, "tree_nodes": M, "max_tree_nodes": max_nodes,
+        "tree_sizes": [len(p) for p in wl.parents], "prefix": [int(p) for p in wl.prefix_len],
+        "dtype": "bf16" if dims.dtype == "bf16" else "f32",
+        "shape": {"hidden": dims.hidden, "q_heads": dims.n_q_heads, "kv_heads": dims.n_kv_heads,
+                  "head_dim": dims.head_dim, "ffn": dims.ffn, "vocab": dims.vocab},
+        "timed_steps": len(timed), "launch": "hip_graph" if graph_ms is not None else "eager",
+        "ms_per_step": round(ms_per_step, 5), "us_per_step": round(ms_per_step * 1e3, 2),
+        "step_ms": _stats(stats_ms if graph_ms is not None else eager_ms),
+        "eager_step_ms": _stats(eager_ms),
+        "nodes_s": round(M / (ms_per_step * 1e-3), 1),
+        "accepted_per_step": acc_per_step,
+        "accepted_tok_s": round(acc_per_step / (ms_per_step * 1e-3), 1),
+        "accepted_tok_s_planted_depth3": round(planted / (ms_per_step * 1e-3), 1),
+        "step_roofline": step_roofline(dims, wl, ms_per_step),
+        "lm_head_roofline": roof,
+        "stage_ms_per_step": {k: round(ms / max(n, 1), 5) for k, (ms, n) in diag_stages.items()},
+    }
+    if headline:
+        out["_wl"] = wl
+    del v, t
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -596,9 +810,6 @@ def main():
         sys.exit(2)
     import torch
     import tree_attention_verification_06_amd as E
-    from tree_attention_verification_06_amd.runner import TreeVerifier
-    from workloads import make_workload, trees as T
-    from workloads.device import upload
 
     E.lib()  # fail loudly if the HIP library is not built
     if args.eagle_only:
@@ -607,135 +818,50 @@ def main():
     if args.decode_only:
         print(json.dumps({"decode": bench_decode(args)}), flush=True)
         return
-    cfg = args.config
-    extra = args.warmup + args.steps + 8
-    t0 = time.perf_counter()
-    wl = make_workload(cfg, seed=args.seed, cache_slack=extra * 10)
-    dims = wl.dims
-    log(f"workload {wl.name}: {wl.n_nodes} nodes, batch {wl.batch}, generated in {time.perf_counter() - t0:.1f}s")
-    t = upload(wl)
-    torch.cuda.synchronize()
-    M = wl.n_nodes
-    max_nodes = max(len(p) for p in wl.parents)
-    cap = wl.cache_cap
-    weights, layout = laid_out(t["weights"], args)
-    v = TreeVerifier(dims, weights, t["k_cache"], t["v_cache"], batch=wl.batch, max_total_nodes=M,
-                     max_nodes=max_nodes, max_prefix=cap, lm_layout=layout, weight_layout=layout)
-    prefix0 = t["prefix_len"].clone()
-
-    def step(timer=None):
-        v.step(t["tree_off"], t["parent"], t["tokens"], t["prefix_len"], M, x=t.get("x"), timer=timer)
-
-    # warmup
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t["prefix_len"].copy_(prefix0)
-    torch.cuda.synchronize()
-
-    # the timed region records HIP events around the dominant kernel (LM head) only: an
-    # event pair around every kernel would itself slow the step down
-    timer = None if args.no_timer else E.Timer(capacity=4 * (args.steps + 1), stages=["lm_head"])
-    stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step(timer)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
-    ms_per_step = total_ms / args.steps
-    stages = timer.collect() if timer else {}
-    if timer:
-        timer.close()
-    st = int(v.status.item())
-    if st != 0:
-        raise RuntimeError(f"device status {st} ({E.status_str(st)})")
-
-    # per-kernel breakdown: a separate pass with events around every kernel (diagnostic)
-    t["prefix_len"].copy_(prefix0)
-    diag = E.Timer(capacity=16 * 11)
-    for _ in range(10):
-        step(diag)
-    torch.cuda.synchronize()
-    diag_stages = diag.collect()
-    diag.close()
-
-    # accepted tokens per step: the same steps again, reading accept_len after each (untimed)
-    t["prefix_len"].copy_(prefix0)
-    accepted = []
-    for _ in range(min(args.steps, 10)):
-        step()
-        accepted.append(int((v.accept_len + 1).sum().item()))
-    acc_per_step = float(np.mean(accepted))
-
-    # planted variant: tokens along one depth-3 root path set to the target's greedy choice
-    # (node inputs are given hidden states, so tokens do not change the target's argmax)
-    g = v.argmax.cpu().numpy()
-    tokens = wl.tokens.copy()
-    for b, par in enumerate(wl.parents):
-        o = int(wl.tree_off[b])
-        d = T.depths(par)
-        cands = [i for i in range(len(par)) if d[i] == 3] or [max(range(len(par)), key=lambda i: d[i])]
-        j = cands[0]
-        path = []
-        while j != -1:
-            path.append(j)
-            j = par[j]
-        for node in path[::-1][1:]:
-            tokens[o + node] = g[o + par[node]]
-    t_tokens = torch.from_numpy(tokens).cuda()
-    t["prefix_len"].copy_(prefix0)
-    v.step(t["tree_off"], t["parent"], t_tokens, t["prefix_len"], M, x=t.get("x"))
-    planted = int((v.accept_len + 1).sum().item())
-
-    nodes_per_s = M / (ms_per_step * 1e-3)
-    byts, flops = step_roofline_bytes_flops(dims, wl)
-    t_roof_ms = max(byts / (HBM_PEAK_GBS * 1e9), 0) * 1e3  # step is HBM-bound at these shapes
-    lm_ms, lm_n = stages.get("lm_head", (0.0, 0))
-    roof = None
-    if lm_n:
-        lm_avg = lm_ms / lm_n
-        ach = lm_head_bytes(dims, M) / (lm_avg * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name, layout_name(args)),
-                "kernel": "gemm_bf16_kernel (LM head + fused row argmax)" if dims.dtype == "bf16" else
-                "gemm_f32_kernel (LM head + fused row argmax)",
-                "kernel_ms": round(lm_avg, 4), "bytes_per_launch": lm_head_bytes(dims, M)}
+    head = bench_verify(args.config, args, steps=args.steps, warmup=args.warmup, headline=True)
+    wl = head.pop("_wl")
+    log(f"{head['workload']}: {head['ms_per_step']:.4f} ms/step ({head['launch']}), "
+        f"step roofline {head['step_roofline']['frac']:.3f}")
+    configs = {}
+    for c in [int(c) for c in args.other_configs.split(",") if c.strip()]:
+        if c == args.config:
+            continue
+        r = bench_verify(c, args, steps=max(args.steps, args.min_steps), warmup=max(args.warmup, 10))
+        log(f"{r['workload']}: {r['ms_per_step']:.4f} ms/step ({r['launch']}), "
+            f"step roofline {r['step_roofline']['frac']:.3f}")
+        configs[r["workload"]] = r
 
     out = {
         "metric": "tree-verify nodes/sec + accepted tok/s at 1 GPU; % of HBM/MFMA roofline",
-        "value": round(nodes_per_s, 1),
+        "value": head["nodes_s"],
         "unit": "nodes/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if dims.dtype == "bf16" else "f32",
+        "dtype": head["dtype"],
         "data": "synthetic: seeded random-init weights N(0,0.02), KV prefix and node states N(0,1), uniform tokens",
-        "config": {"workload": wl.name, "batch": wl.batch, "tree_nodes": M, "max_tree_nodes": max_nodes,
-                   "prefix": int(wl.prefix_len.max()), "hidden": dims.hidden, "q_heads": dims.n_q_heads,
-                   "kv_heads": dims.n_kv_heads, "head_dim": dims.head_dim, "ffn": dims.ffn, "vocab": dims.vocab,
-                   "step": "tree_build + tree_verify + accept_commit",
+        "config": {"workload": head["workload"], "batch": head["batch"], "tree_nodes": head["tree_nodes"],
+                   "max_tree_nodes": head["max_tree_nodes"], "prefix": max(head["prefix"]), **head["shape"],
+                   "step": "tree_build + tree_verify + accept_commit", "launch": head["launch"],
                    "weight_layout": layout_name(args)},
-        "accepted_tok_s": round(acc_per_step / (ms_per_step * 1e-3), 1),
-        "accepted_per_step": acc_per_step,
-        "accepted_tok_s_planted_depth3": round(planted / (ms_per_step * 1e-3), 1),
-        "step_roofline": {"bound": "hbm", "algorithmic_bytes": byts, "algorithmic_flops": flops,
-                          "t_roof_ms": round(t_roof_ms, 5), "frac": round(t_roof_ms / ms_per_step, 4)},
-        "roofline": roof,
-        "stage_ms_per_step": {k: round(ms / max(n, 1), 5) for k, (ms, n) in diag_stages.items()},
+        "roofline": head["lm_head_roofline"],
+        "step_roofline": head["step_roofline"],
+        "step_ms": head["step_ms"],
+        "eager_step_ms": head["eager_step_ms"],
+        "accepted_tok_s": head["accepted_tok_s"],
+        "accepted_per_step": head["accepted_per_step"],
+        "accepted_tok_s_planted_depth3": head["accepted_tok_s_planted_depth3"],
+        "stage_ms_per_step": head["stage_ms_per_step"],
+        "configs": configs,
     }
-    if not args.no_eagle_step and dims.dtype == "bf16":
-        del v, t
+    if not args.no_eagle_step and head["dtype"] == "bf16":
         torch.cuda.empty_cache()
         out["eagle_step"] = bench_eagle_step(args)
-    if not args.no_decode and dims.dtype == "bf16":
+    if not args.no_decode and head["dtype"] == "bf16":
         torch.cuda.empty_cache()
         out["decode"] = bench_decode(args)
     if args.pmc_calibration:
