@@ -182,12 +182,16 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
       vreg[slot][u] = *(const uint4*)(vb + off);
     }
   };
-  auto store_kv = [&](int slot, int buf, int kt0) {
+  // ZERO: keys past the chunk end are stored as zeros.  They are masked to weight 0 either
+  // way (and hold finite copies of the chunk's last key), so tiles that are full by
+  // construction store the registers as they are.
+  auto store_kv = [&](int slot, int buf, int kt0, auto ZC) {
+    constexpr bool ZERO = decltype(ZC)::value;
 #pragma unroll
     for (int u = 0; u < GPT; ++u) {
       const int i = tid + u * NWA * 64;
       const int kk = i >> 4, gd = i & 15;
-      const bool ok = kt0 + kk < k1;
+      const bool ok = !ZERO || kt0 + kk < k1;
       *(uint4*)(ks[buf] + kk * KS + gd * 8) = ok ? kreg[slot][u] : make_uint4(0u, 0u, 0u, 0u);
       *(uint4*)(vs[buf] + kk * VS + gd * 8) = ok ? vreg[slot][u] : make_uint4(0u, 0u, 0u, 0u);
     }
@@ -196,12 +200,15 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
   const int ntile = (k1 - k0 + KT - 1) / KT;
   load_kv(0, k0);
   load_kv(1, min(k0 + KT, k1 - 1));
-  store_kv(0, 0, k0);
+  store_kv(0, 0, k0, std::true_type{});
   __syncthreads();
   // one tile: SL (compile-time, so the register ring never needs dynamic indexing) is the
-  // register slot and LDS buffer of tile it
-  auto tile_step = [&](auto SLC, int it) {
+  // register slot and LDS buffer of tile it.  MASKED: the tile has keys a row may not see
+  // (tree keys, or keys past the chunk end); an unmasked tile (a full tile of prefix keys)
+  // skips the visibility bits and scales each score inside the exponential's FMA.
+  auto tile_step = [&](auto SLC, auto MC, int it) {
     constexpr int SL = decltype(SLC)::value;
+    constexpr bool MASKED = decltype(MC)::value;
     const int kt0 = k0 + it * KT;
     // tile it + 2 into the slot tile it came through
     load_kv(SL, min(kt0 + 2 * KT, k1 - 1));
@@ -215,14 +222,18 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
     uint32_t vlo[RBW], vhi[RBW];
 #pragma unroll
     for (int j = 0; j < RBW; ++j) {
-      // bits 0 .. n-1 set, n = the tile's keys before the chunk end, in [0, 64]; shift
-      // arithmetic only (no select that could become a branch after the score MFMAs)
-      const int n = min(max(k1 - kt0, 0), 64);
-      const uint64_t bound = (~0ull >> ((64 - n) & 63)) & (0ull - (uint64_t)(n != 0));
-      const uint64_t ws = (((kt0 & 64) ? vis1[j] : vis0[j]) & bound) >> (lq * 4);
-      vlo[j] = (uint32_t)ws;
-      vhi[j] = (uint32_t)(ws >> 32);
+      vlo[j] = vhi[j] = ~0u;
+      if constexpr (MASKED) {
+        // bits 0 .. n-1 set, n = the tile's keys before the chunk end, in [0, 64]; shift
+        // arithmetic only (no select that could become a branch after the score MFMAs)
+        const int n = min(max(k1 - kt0, 0), 64);
+        const uint64_t bound = (~0ull >> ((64 - n) & 63)) & (0ull - (uint64_t)(n != 0));
+        const uint64_t ws = (((kt0 & 64) ? vis1[j] : vis0[j]) & bound) >> (lq * 4);
+        vlo[j] = (uint32_t)ws;
+        vhi[j] = (uint32_t)(ws >> 32);
+      }
     }
+    // MASKED: scores in log2 units, -inf where hidden; unmasked: the raw q.k
     float s[RBW][4][4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -236,8 +247,12 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
         for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[j][kk], acc, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool vis = ((st < 2 ? vlo[j] : vhi[j]) >> ((st & 1) * 16 + i)) & 1u;
-          s[j][st][i] = vis ? acc[i] * sl2 : -INFINITY;
+          if constexpr (MASKED) {
+            const bool vis = ((st < 2 ? vlo[j] : vhi[j]) >> ((st & 1) * 16 + i)) & 1u;
+            s[j][st][i] = vis ? acc[i] * sl2 : -INFINITY;
+          } else {
+            s[j][st][i] = acc[i];
+          }
         }
       }
     }
@@ -251,6 +266,7 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][st][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if constexpr (!MASKED) mx *= sl2;  // sl2 > 0: the scaled maximum is the maximum scaled
       const float mnew = fmaxf(mrow[j], mx);
       const float mbase = (mnew == -INFINITY) ? 0.f : mnew;
       const float fac = __builtin_amdgcn_exp2f(mrow[j] - mbase);
@@ -260,7 +276,8 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[j][st][i] - mbase);
+          const float p = MASKED ? __builtin_amdgcn_exp2f(s[j][st][i] - mbase)
+                                 : __builtin_amdgcn_exp2f(fmaf(s[j][st][i], sl2, -mbase));
           s[j][st][i] = p;
           ps += p;
         }
@@ -302,12 +319,23 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
     }
     // next tile (loaded one step ago) into the other LDS buffer; the barrier also ends
     // every wave's reads of this buffer before it is refilled
-    if (it + 1 < ntile) store_kv(1 - SL, 1 - SL, kt0 + KT);
+    if (it + 1 < ntile) store_kv(1 - SL, 1 - SL, kt0 + KT, MC);
     __syncthreads();
   };
-  for (int it = 0; it < ntile; it += 2) {
-    tile_step(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < ntile) tile_step(std::integral_constant<int, 1>{}, it + 1);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using Unmasked = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  // full prefix tiles (an even count, so every loop keeps the slot order) run unmasked;
+  // the tree chunk's tiles and a prefix chunk's last tiles run masked
+  const int nu = tree_chunk ? 0 : ((k1 - k0) / KT) & ~1;
+  for (int it = 0; it < nu; it += 2) {
+    tile_step(S0{}, Unmasked{}, it);
+    tile_step(S1{}, Unmasked{}, it + 1);
+  }
+  for (int it = nu; it < ntile; it += 2) {
+    tile_step(S0{}, Masked{}, it);
+    if (it + 1 < ntile) tile_step(S1{}, Masked{}, it + 1);
   }
 
   const int rmax = a.max_nodes * g;
