@@ -423,88 +423,125 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int grid_re
   if (a.dbg) *(float4*)(a.dbg + oi) = out;
 }
 
-// fp32 path: one wave per (node, query head).  Keys are taken in blocks of F32_BLK: the
-// block's scores are staged in LDS (one lane per key), then every lane updates the running
-// max, the running sum and its own output dimensions (lane, lane + 64) over the block, so
-// the LDS footprint does not depend on the prefix length.
-constexpr int F32_BLK = 512;
-__global__ __launch_bounds__(64) void tree_attn_f32_kernel(AttnArgs a) {
-  __shared__ float qs[128];
-  __shared__ float sc[F32_BLK];
+// fp32 path: one workgroup per (sequence, query head, group of 8 nodes), one node per wave.
+// Keys (the prefix, then the tree nodes) are taken in blocks of F32_KB: the block's K and V
+// rows are staged in LDS with 16-byte loads by the whole workgroup; each wave then scores the
+// block's keys for its node (a lane per key, dot products from LDS), folds the block into its
+// running max and sum, and each lane accumulates output dimensions lane and lane + 64 from
+// the V rows in LDS.  The LDS footprint does not depend on the prefix length.
+constexpr int F32_KB = 128;   // keys per block
+constexpr int F32_NG = 8;     // nodes (waves) per workgroup
+constexpr int F32_KP = 132;   // LDS row stride (floats): 16-byte aligned rows
+__global__ __launch_bounds__(F32_NG * 64) void tree_attn_f32_kernel(AttnArgs a, int groups) {
+  __shared__ __align__(16) float ks[F32_KB * F32_KP];
+  __shared__ __align__(16) float vs[F32_KB * F32_KP];
+  __shared__ __align__(16) float qs[F32_NG][128];
+  __shared__ float ps[F32_NG][F32_KB];
   const int hq = a.hq, hd = a.hd;
-  const int node_g = blockIdx.x / hq, h = blockIdx.x % hq;
-  int b = 0;
-  while (b + 1 < a.batch && a.tree_off[b + 1] <= node_g) ++b;
+  int t = blockIdx.x;
+  const int grp = t % groups;
+  t /= groups;
+  const int h = t % hq;
+  const int b = t / hq;
   const int off = a.tree_off[b];
   const int N = a.tree_off[b + 1] - off;
-  const int i = node_g - off;
-  if (N > a.max_nodes) return;
+  if (N > a.max_nodes || grp * F32_NG >= N) return;
   const int P = min(max(a.prefix_len[b], 0), a.cap);
   const int kvh = h / (hq / a.hkv);
-  const int lane = threadIdx.x;
-  const float* q = (const float*)a.q + ((int64_t)node_g * hq + h) * hd;
-  for (int d = lane; d < hd; d += 64) qs[d] = q[d];
-  __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = grp * F32_NG + w;  // this wave's node
+  const bool live = i < N;
+  const int ic = live ? i : N - 1;
+  const float* q = (const float*)a.q + ((int64_t)(off + ic) * hq + h) * hd;
+  for (int d = lane; d < hd; d += 64) qs[w][d] = q[d];
+  const uint64_t anc0 = a.anc[(int64_t)(off + ic) * a.mw];
+  const uint64_t anc1 = a.mw > 1 ? a.anc[(int64_t)(off + ic) * a.mw + 1] : 0ull;
   const CacheView cv{a.cb, a.ch, a.ct, a.table, a.ps, a.maxb, a.npages};
-  auto coff = [&](int t) {
-    bool ok;
-    return cache_offset(cv, b, kvh, t, ok);
-  };
   const float* kc = (const float*)a.k_cache;
   const float* vc = (const float*)a.v_cache;
   const float* ktr = (const float*)a.k_tree;
   const float* vtr = (const float*)a.v_tree;
   const float scale = rsqrtf((float)hd);
+  const int c4 = hd / 4;  // 16-byte pieces per row
   float m = -INFINITY, l = 0.f;
   float acc[2] = {0.f, 0.f};
-  for (int j0 = 0; j0 < P + N; j0 += F32_BLK) {
-    const int nb = min(F32_BLK, P + N - j0);
-    float bm = -INFINITY;
-    for (int jj = lane; jj < nb; jj += 64) {
-      const int j = j0 + jj;
-      float s = -INFINITY;
-      const float* kp = nullptr;
+  for (int j0 = 0; j0 < P + N; j0 += F32_KB) {
+    const int nb = min(F32_KB, P + N - j0);
+    __syncthreads();  // the previous block's rows are no longer read
+    for (int e = tid; e < nb * c4; e += blockDim.x) {
+      const int r = e / c4, c = e % c4;
+      const int j = j0 + r;
+      int64_t ko;
+      const float *kb, *vb;
       if (j < P) {
-        kp = kc + coff(j);
+        bool ok;
+        ko = cache_offset(cv, b, kvh, j, ok);
+        kb = kc;
+        vb = vc;
       } else {
-        const int jn = j - P;
-        const uint64_t word = a.anc[(int64_t)(off + i) * a.mw + (jn >> 6)];
-        if ((word >> (jn & 63)) & 1ull) kp = ktr + ((int64_t)(off + jn) * a.hkv + kvh) * hd;
+        ko = ((int64_t)(off + j - P) * a.hkv + kvh) * hd;
+        kb = ktr;
+        vb = vtr;
       }
-      if (kp) {
-        float dot = 0.f;
-        for (int d = 0; d < hd; ++d) dot += qs[d] * kp[d];
-        s = dot * scale;
-      }
-      sc[jj] = s;
-      bm = fmaxf(bm, s);
+      *(float4*)&ks[r * F32_KP + 4 * c] = *(const float4*)(kb + ko + 4 * c);
+      *(float4*)&vs[r * F32_KP + 4 * c] = *(const float4*)(vb + ko + 4 * c);
     }
-    bm = wave_max(bm);
     __syncthreads();
-    const float mnew = fmaxf(m, bm);
-    if (mnew != -INFINITY) {  // else every key so far is masked: nothing to add
-      const float fac = m == -INFINITY ? 0.f : __expf(m - mnew);
-      l *= fac;
-      acc[0] *= fac;
-      acc[1] *= fac;
-      for (int jj = 0; jj < nb; ++jj) {
-        const float p = __expf(sc[jj] - mnew);
-        if (p == 0.f) continue;
-        l += p;
+    if (live) {
+      // scores of keys jj = lane and lane + 64 of the block
+      float sc[2];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int jj = lane + 64 * u;
         const int j = j0 + jj;
-        const float* vp = j < P ? vc + coff(j) : vtr + ((int64_t)(off + j - P) * a.hkv + kvh) * hd;
-        acc[0] += p * vp[lane];
-        if (lane + 64 < hd) acc[1] += p * vp[lane + 64];
+        bool vis = jj < nb;
+        if (vis && j >= P) {
+          const int jn = j - P;
+          vis = (((jn < 64 ? anc0 : anc1) >> (jn & 63)) & 1ull) != 0ull;
+        }
+        float dot = 0.f;
+        if (vis) {
+          for (int d = 0; d < hd; d += 4) {
+            const float4 kv = *(const float4*)&ks[jj * F32_KP + d];
+            const float4 qv = *(const float4*)&qs[w][d];
+            dot += qv.x * kv.x + qv.y * kv.y + qv.z * kv.z + qv.w * kv.w;
+          }
+        }
+        sc[u] = vis ? dot * scale : -INFINITY;
+        bm = fmaxf(bm, sc[u]);
       }
-      m = mnew;
+      bm = wave_max(bm);
+      const float mnew = fmaxf(m, bm);
+      if (mnew != -INFINITY) {  // else every key so far is hidden: nothing to add
+        const float fac = m == -INFINITY ? 0.f : __expf(m - mnew);
+        float bs = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float pu = __expf(sc[u] - mnew);
+          ps[w][lane + 64 * u] = pu;
+          bs += pu;
+        }
+        l = l * fac + wave_sum(bs);
+        acc[0] *= fac;
+        acc[1] *= fac;
+        m = mnew;
+        __builtin_amdgcn_wave_barrier();
+        for (int jj = 0; jj < nb; ++jj) {
+          const float pj = ps[w][jj];
+          acc[0] += pj * vs[jj * F32_KP + lane];
+          if (lane + 64 < hd) acc[1] += pj * vs[jj * F32_KP + lane + 64];
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
     }
-    __syncthreads();  // sc is refilled by the next block
   }
+  if (!live) return;
   for (int u = 0; u < 2; ++u) {
     const int d = lane + 64 * u;
     if (d >= hd) break;
     const float out = acc[u] / l;
-    const int64_t oi = (int64_t)node_g * hq * hd + (int64_t)h * hd + d;
+    const int64_t oi = (int64_t)(off + i) * hq * hd + (int64_t)h * hd + d;
     ((float*)a.out)[oi] = out;
     if (a.dbg) a.dbg[oi] = out;
   }
@@ -567,9 +604,12 @@ int launch_attn(AttnArgs& a, const AttnPlan& p, eagle_timer* timer, hipStream_t 
 }
 
 int launch_attn_f32(AttnArgs& a, int total_nodes, eagle_timer* timer, hipStream_t s) {
+  (void)total_nodes;
   if (a.hd != 64 && a.hd != 128) return EAGLE_ERR_UNSUPPORTED;
+  if ((a.cb | a.ch | a.ct) % 4) return EAGLE_ERR_ARG;  // rows are read with 16-byte loads
+  const int groups = (a.max_nodes + F32_NG - 1) / F32_NG;
   timer_begin(timer, ST_ATTN, s);
-  hipLaunchKernelGGL(tree_attn_f32_kernel, dim3(total_nodes * a.hq), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(tree_attn_f32_kernel, dim3(a.batch * a.hq * groups), dim3(F32_NG * 64), 0, s, a, groups);
   timer_end(timer, s);
   return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
 }

@@ -948,12 +948,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
 // ---------------------------------------------------------------------------------
 // fp32 VALU kernel (fp32 layers): tile of 64 weight rows x 32 tokens, whole K.
 // ---------------------------------------------------------------------------------
+// K goes through LDS in chunks of F32_KC: a chunk's W (64 x 64) and X (32 x 64) are read with
+// 16-byte loads, and the next chunk's loads are issued before this chunk's math (register
+// double buffering), so the chunk loop costs one memory round trip in total rather than one
+// per chunk.  Thread (tr = tid % 16, tt = tid / 16) accumulates weight rows tr + 16 i (i < 4)
+// for tokens tt and tt + 16 from 16-byte LDS reads along k: 6 reads feed 32 FMAs.
 constexpr int F32_NT = 64, F32_MT = 32, F32_KC = 64;
 
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d, int grid_real) {
   constexpr int TS = F32_MT + 4;
-  __shared__ float xs[F32_MT][F32_KC + 1];
-  __shared__ float ws[F32_NT][F32_KC + 1];
+  constexpr int KP = F32_KC + 4;  // LDS row stride (floats): rows stay 16-byte aligned, reads conflict-free
+  __shared__ __align__(16) float xs[F32_MT][KP];
+  __shared__ __align__(16) float ws[F32_NT][KP];
   __shared__ float tile[F32_NT * TS];
   __shared__ float s_scale[F32_MT];
   __shared__ float s_ssq[F32_MT];
@@ -966,42 +972,81 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d, int grid_real
   const int mt_i = bid % m_tiles, nt_i = bid / m_tiles;
   const int col0 = nt_i * F32_NT, m0 = mt_i * F32_MT;
   const int mv = min(F32_MT, d.m - m0);
-  // thread computes rows r = tid % 64 and tokens t = tid / 64 + 4 * i
-  const int r = tid % F32_NT, t0 = tid / F32_NT;
-  float acc[F32_MT / 4];
-  for (int i = 0; i < F32_MT / 4; ++i) acc[i] = 0.f;
-  if (tid < F32_MT) s_ssq[tid] = 0.f;
+  // staging: W piece u (< 4) of this thread = row tid / 16 + 16 u, columns 4 (tid % 16) .. + 3;
+  // X = token tid / 8, columns 8 (tid % 8) .. + 7
+  const int wg = tid % 16, wr0 = tid / 16;
+  const float* wrow[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int rr = wr0 + 16 * u;
+    const bool second = d.dual && rr >= F32_NT / 2;
+    const int row = d.dual ? (col0 / 2 + (rr % (F32_NT / 2))) : col0 + rr;
+    const int nrows = d.n;
+    wrow[u] = row < nrows ? (const float*)(second ? d.w1 : d.w0) + (int64_t)row * d.ldw : nullptr;
+  }
+  const int xt = tid / 8, xg = tid % 8;
+  const bool xlive = m0 + xt < d.m;
+  float4 wv[4];
+  float xv[8];
+  float ssq = 0.f;
+  auto load = [&](int kc) {
+    const int kw = kc + 4 * wg;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      wv[u] = (wrow[u] && kw < d.k) ? *(const float4*)(wrow[u] + kw) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int kx = kc + 8 * xg;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xv[q] = 0.f;
+    if (xlive && kx < d.k) load_x8(d.x, m0 + xt, kx, xv);
+  };
+  auto store = [&](int kc) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *(float4*)&ws[wr0 + 16 * u][4 * wg] = wv[u];
+    const int kx = kc + 8 * xg;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ssq += xv[q] * xv[q];
+    if (kx < d.k) apply_gain8(d.x, kx, xv);
+    *(float4*)&xs[xt][8 * xg] = make_float4(xv[0], xv[1], xv[2], xv[3]);
+    *(float4*)&xs[xt][8 * xg + 4] = make_float4(xv[4], xv[5], xv[6], xv[7]);
+  };
+  const int tr = tid % 16, tt = tid / 16;
+  float acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = 0.f;
+  load(0);
+  store(0);
+  __syncthreads();
   for (int kc = 0; kc < d.k; kc += F32_KC) {
-    __syncthreads();
-    for (int i = tid; i < F32_MT * (F32_KC / 8); i += 256) {
-      const int rr = i / (F32_KC / 8), g = i % (F32_KC / 8);
-      const int m = m0 + rr, k = kc + g * 8;
-      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (m < d.m && k < d.k) {
-        load_x8(d.x, m, k, v);
-        float sq = 0.f;
-        for (int q = 0; q < 8; ++q) sq += v[q] * v[q];
-        atomicAdd(&s_ssq[rr], sq);
-        apply_gain8(d.x, k, v);
-      }
-      for (int q = 0; q < 8; ++q) xs[rr][g * 8 + q] = v[q];
-    }
-    for (int i = tid; i < F32_NT * F32_KC; i += 256) {
-      const int rr = i / F32_KC, kk = i % F32_KC;
-      const int c = col0 + rr;
-      const bool second = d.dual && rr >= F32_NT / 2;
-      const int row = d.dual ? (col0 / 2 + (rr % (F32_NT / 2))) : c;
-      const float* wsrc = (const float*)(second ? d.w1 : d.w0);
-      const int nrows = d.n;
-      ws[rr][kk] = (row < nrows && kc + kk < d.k) ? wsrc[(int64_t)row * d.ldw + kc + kk] : 0.f;
+    const bool more = kc + F32_KC < d.k;
+    if (more) load(kc + F32_KC);
+#pragma unroll 4
+    for (int kk = 0; kk < F32_KC; kk += 4) {
+      float4 w4[4], x4[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w4[i] = *(const float4*)&ws[tr + 16 * i][kk];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) x4[j] = *(const float4*)&xs[tt + 16 * j][kk];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] += w4[i].x * x4[j].x + w4[i].y * x4[j].y + w4[i].z * x4[j].z + w4[i].w * x4[j].w;
     }
     __syncthreads();
-    for (int kk = 0; kk < F32_KC; ++kk) {
-      const float wv = ws[r][kk];
-      for (int i = 0; i < F32_MT / 4; ++i) acc[i] += wv * xs[t0 + 4 * i][kk];
+    if (more) {
+      store(kc + F32_KC);
+      __syncthreads();
     }
   }
-  for (int i = 0; i < F32_MT / 4; ++i) tile[r * TS + t0 + 4 * i] = acc[i];
+  // row sums of squares: the 8 staging threads of a token are adjacent lanes
+  ssq += __shfl_xor(ssq, 1, 64);
+  ssq += __shfl_xor(ssq, 2, 64);
+  ssq += __shfl_xor(ssq, 4, 64);
+  if (xg == 0) s_ssq[xt] = ssq;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) tile[(tr + 16 * i) * TS + tt + 16 * j] = acc[i][j];
   __syncthreads();
   if (tid < F32_MT) s_scale[tid] = d.x.norm ? rsqrtf(s_ssq[tid] / (float)d.k + d.x.eps) : 1.f;
   __syncthreads();
