@@ -802,7 +802,9 @@ int draft_expand_impl(const eagle_dims* d, const eagle_draft_params* pr, const v
       if ((rc = gemm(g, L.p_lm[i], ST_LM_HEAD))) return rc;
     }
     timer_begin(timer, ST_DRAFT_TOPK, s);
-    if (pr->top_k <= 12)
+    if (pr->top_k <= 10)
+      hipLaunchKernelGGL(draft_topk_merge_kernel<10>, dim3(Rl), dim3(256), 0, s, st);
+    else if (pr->top_k <= 12)
       hipLaunchKernelGGL(draft_topk_merge_kernel<12>, dim3(Rl), dim3(256), 0, s, st);
     else
       hipLaunchKernelGGL(draft_topk_merge_kernel<16>, dim3(Rl), dim3(256), 0, s, st);
