@@ -332,3 +332,36 @@ def test_tree_build_refuses_tree_beyond_max_nodes():
     a = anc.cpu().numpy().view(np.uint64)[:, 0]
     assert a[:5].tolist() == [1, 3, 7, 15, 31]       # the tree within max_nodes is encoded
     assert (a[5:] == np.uint64(0xFFFFFFFFFFFFFFFF)).all()  # the other is not written
+
+
+def test_verify_fp32_ragged_batch_several_key_blocks():
+    """The fp32 layer on a ragged batch: three trees (one past the 64-node single mask word,
+    so two mask words) with prefixes that span one, two and three 128-key blocks of the
+    fp32 attention, against the oracle; then acceptance with a planted path, bit-exact on
+    the GPU's own argmax."""
+    from workloads.configs import TINY
+    rng = np.random.default_rng(12)
+    parents = [T.random_tree(rng, 70), T.chain(9), T.static_tree_26()]
+    wl = make_workload(1, seed=47, dims=TINY, batch=3, prefix=[100, 250, 300], parents=parents)
+    assert wl.mask_words == 2
+    _print("verify fp32 ragged", wl.tree_off.tolist(), wl.prefix_len.tolist())
+    g = GpuRun(wl).run().outputs()
+    ref = oracle_verify(wl)
+    _print(check_verify(g, ref, wl.dims, label="fp32-ragged"))
+    tokens = wl.tokens.copy()
+    o = wl.tree_off[1]
+    for i in range(1, 9):
+        tokens[o + i] = g["argmax"][o + i - 1]
+    wl.tokens = tokens
+    run = GpuRun(wl, want_logits=False)
+    run.run(accept=True)
+    g2 = run.outputs()
+    acc = run.v.accept_len.cpu().numpy()
+    assert g2["status"] == 0
+    for b, par in enumerate(parents):
+        ob = wl.tree_off[b]
+        n = len(par)
+        L, pth, out, nt, leaf = oracle.accept_sequence(par, tokens[ob:ob + n], g2["argmax"][ob:ob + n],
+                                                      g2["depth"][ob:ob + n])
+        assert acc[b] == L
+    assert acc[1] == 8
