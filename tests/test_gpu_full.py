@@ -21,9 +21,9 @@ def _log(*a):
     print(*a, flush=True)
 
 
-def _run_full(cfg, prefix=None):
+def _run_full(cfg, prefix=None, **kw):
     t0 = time.time()
-    wl = make_workload(cfg, prefix=prefix)
+    wl = make_workload(cfg, prefix=prefix, **kw)
     _log(f"cfg {wl.name}: {wl.n_nodes} nodes, generated in {time.time() - t0:.1f}s")
     g = GpuRun(wl).run(accept=True)
     out = g.outputs()
@@ -54,6 +54,14 @@ def test_full_llama8b_layer_60_nodes_prefix_2048():
 
 def test_full_llama70b_layer_60_nodes_prefix_32768():
     _run_full(4)
+
+
+def test_full_ragged_six_trees_wide_lm_head_tiles():
+    """Six dynamic trees, 583 rows: the LM head runs the four-wave tile of 160 tokens with
+    32x32x16 MFMAs (the ragged four-tree batch and the 960-row batch run the 192-token one);
+    every output against the oracle."""
+    wl, g, out, ref = _run_full(3, batch=6, prefix=[4096, 1500, 300, 2048, 64, 777])
+    assert wl.n_nodes == 583
 
 
 def test_full_ragged_dynamic_batch_prefix_4096():
