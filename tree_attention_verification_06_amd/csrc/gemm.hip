@@ -164,6 +164,30 @@ __device__ __forceinline__ void epi_store_rows(const GemmDesc& d, const float* t
   }
 }
 
+// Top-k keys as doubles: the 52 mantissa bits hold (order-preserving bits of the fp32 value)
+// << 20 | (2^20 - 1 - column), and the exponent field is 1, so every key is a positive
+// normal double and doubles compare exactly like the packed integers (larger value first,
+// then smaller column).  A compare-and-swap step of the sorted insertion is then one
+// v_max_f64 and one v_min_f64 (inline: in IEEE mode the compiler would otherwise add a
+// quieting max per operand).  0.0 sorts below every key and marks an empty slot.
+__device__ __forceinline__ double topk_key(float v, uint32_t col) {
+  const unsigned long long k = (((unsigned long long)f2ord(v) << 20) | (unsigned long long)(0xfffffu - col)) +
+                               (1ull << 52);
+  return __longlong_as_double((long long)k);
+}
+__device__ __forceinline__ float topk_key_value(unsigned long long bits) {
+  return ord2f((uint32_t)((bits - (1ull << 52)) >> 20));
+}
+__device__ __forceinline__ int32_t topk_key_col(unsigned long long bits) {
+  return (int32_t)(0xfffffu - (uint32_t)((bits - (1ull << 52)) & 0xfffffull));
+}
+// l = max(k, l), k = min(k, l) (l is updated in place)
+__device__ __forceinline__ void topk_cas(double& k, double& l) {
+  double lo;
+  asm("v_min_f64 %1, %2, %0\n\tv_max_f64 %0, %2, %0" : "+v"(l), "=&v"(lo) : "v"(k));
+  k = lo;
+}
+
 // EPI_TOPK with per-thread candidate lists of KL entries (KL >= k): the branch-free sorted
 // insertion costs KL compare-and-swap steps per column, so the list is no longer than needed.
 template <int KL>
@@ -183,9 +207,9 @@ __device__ __forceinline__ void epi_topk(const GemmDesc& d, const float* tile, i
   const int t = tid % mt, part = tid / mt;
   const bool active = part < P;
   const int ncol = min(tc, d.n - col0);
-  unsigned long long lst[KL];
+  double lst[KL];
 #pragma unroll
-  for (int q = 0; q < KL; ++q) lst[q] = 0ull;
+  for (int q = 0; q < KL; ++q) lst[q] = 0.0;
   float mx = -INFINITY, se = 0.f;
   if (active && t < mv) {
     const float sc = scale[t];
@@ -201,13 +225,9 @@ __device__ __forceinline__ void epi_topk(const GemmDesc& d, const float* tile, i
     for (int r = part; r < ncol; r += P) {
       const float v = sc * tile[r * ts + t];
       se += __expf(v - mx);
-      unsigned long long key = argmax_key(v, (uint32_t)(col0 + r));
+      double key = topk_key(v, (uint32_t)(col0 + r));
 #pragma unroll
-      for (int q = 0; q < KL; ++q) {
-        const unsigned long long hi = key > lst[q] ? key : lst[q];
-        key = key > lst[q] ? lst[q] : key;
-        lst[q] = hi;
-      }
+      for (int q = 0; q < KL; ++q) topk_cas(key, lst[q]);
     }
   }
   __syncthreads();  // every read of the tile is done: its LDS is reused below
@@ -215,7 +235,7 @@ __device__ __forceinline__ void epi_topk(const GemmDesc& d, const float* tile, i
   float* sm = (float*)(sl + (size_t)P * mt * KL);             // [P][mt][2]
   if (active) {
 #pragma unroll
-    for (int q = 0; q < KL; ++q) sl[((size_t)part * mt + t) * KL + q] = lst[q];
+    for (int q = 0; q < KL; ++q) sl[((size_t)part * mt + t) * KL + q] = (unsigned long long)__double_as_longlong(lst[q]);
     sm[(part * mt + t) * 2] = mx;
     sm[(part * mt + t) * 2 + 1] = se;
   }
@@ -251,8 +271,8 @@ __device__ __forceinline__ void epi_topk(const GemmDesc& d, const float* tile, i
 #pragma unroll
       for (int p2 = 0; p2 < 8; ++p2) head[p2] += (p2 == bp && best != 0ull);
       const bool valid = best != 0ull;
-      e.topk_val[ob * K + q] = valid ? ord2f((uint32_t)(best >> 32)) : -INFINITY;
-      e.topk_idx[ob * K + q] = valid ? (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull)) : -1;
+      e.topk_val[ob * K + q] = valid ? topk_key_value(best) : -INFINITY;
+      e.topk_idx[ob * K + q] = valid ? topk_key_col(best) : -1;
     }
   }
 }
@@ -1351,6 +1371,7 @@ int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s) {
   if (d.k % 32 || (d.x.ka % 8) || p.cfg < 0) return EAGLE_ERR_UNSUPPORTED;
   if (p.cfg != 100 && (d.x.a.dtype != EAGLE_BF16 || d.x.b.dtype != EAGLE_BF16)) return EAGLE_ERR_UNSUPPORTED;
   if (p.cfg == 100 && d.epi.kind == EPI_TOPK) return EAGLE_ERR_UNSUPPORTED;  // its LDS tile is too small
+  if (d.epi.kind == EPI_TOPK && d.n > (1 << 20)) return EAGLE_ERR_UNSUPPORTED;  // 20-bit columns in the keys
   if (p.cfg == 100 && d.w_layout) return EAGLE_ERR_UNSUPPORTED;              // fragment blocks are bf16
   if (d.dual && d.epi.kind == EPI_SAMPLE) return EAGLE_ERR_UNSUPPORTED;
   const int grid = p.w_tiles * p.m_tiles * p.splits;
