@@ -72,6 +72,21 @@ def test_verify_packed_weights_bit_identical_8b_no_logits():
     assert np.array_equal(c["maxlogit"], c["logits"].max(axis=1))
 
 
+@pytest.mark.parametrize("batch", [4, 6])
+def test_register_argmax_equals_tile_argmax_wide_lm_head(batch):
+    """Ragged batches of 362 and 583 rows (the LM head on the 192- and 160-token four-wave
+    tiles): the argmax reduced from the accumulators (no debug logits) equals the one scanned
+    from the fp32 tile of the debug-logits run, bit for bit, and that one is the row maximum
+    of the logits it wrote."""
+    wl = make_workload(3, batch=batch, prefix=[4096, 1500, 300, 2048, 64, 777][:batch])
+    _log(f"{wl.name} batch {batch}: {wl.n_nodes} nodes")
+    a = GpuRun(wl, layout=1, want_logits=False).run(accept=True).outputs()
+    c = GpuRun(wl, layout=1, want_logits=True).run(accept=True).outputs()
+    for k in ("maxlogit", "argmax"):
+        assert np.array_equal(a[k], c[k]), k
+    assert np.array_equal(c["maxlogit"], c["logits"].max(axis=1))
+
+
 def test_draft_packed_weights_bit_identical():
     from tree_attention_verification_06_amd.runner import TreeDrafter, with_packed_weights
     params = DraftParams(depth=4, top_k=4, frontier=3, max_nodes=16)

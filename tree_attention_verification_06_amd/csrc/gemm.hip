@@ -368,6 +368,36 @@ __device__ __forceinline__ void epi_sample(const GemmDesc& d, float* tile, int t
   }
 }
 
+// Row argmax, after this workgroup's atomicMax of its keys: the last workgroup of the launch
+// (n_epi of them) unpacks the keys and clears them (keys are only touched by device-scope
+// atomics, so no cache maintenance is needed).
+__device__ __forceinline__ void argmax_finish(const GemmDesc& d, int* s_flag, int n_epi) {
+  const Epi& e = d.epi;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  wait_memory();
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(e.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = (old == n_epi - 1);
+  }
+  __syncthreads();
+  if (*s_flag) {
+    for (int m = tid; m < d.m; m += nth) {
+      const unsigned long long key = __hip_atomic_load(&e.keys[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      e.argmax_out[m] = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+      if (e.max_out) e.max_out[m] = ord2f((uint32_t)(key >> 32));
+      __hip_atomic_store(&e.keys[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0) __hip_atomic_store(e.done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
 // Fused epilogue over a finished fp32 tile in LDS: tile[r * ts + t] is output column
 // col0 + r (for dual tiles: gate columns r < tc, up columns r >= tc) of token m0 + t,
 // before the per-row norm scale scale[t].
@@ -487,24 +517,7 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
         }
         atomicMax(&e.keys[m0 + tid], b2);
       }
-      // the last workgroup of the launch unpacks the keys and clears them (keys are
-      // only touched by device-scope atomics, so no cache maintenance is needed)
-      wait_memory();
-      __syncthreads();
-      if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(e.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_flag = (old == n_epi - 1);
-      }
-      __syncthreads();
-      if (*s_flag) {
-        for (int m = tid; m < d.m; m += nth) {
-          const unsigned long long key = __hip_atomic_load(&e.keys[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          e.argmax_out[m] = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
-          if (e.max_out) e.max_out[m] = ord2f((uint32_t)(key >> 32));
-          __hip_atomic_store(&e.keys[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (tid == 0) __hip_atomic_store(e.done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      argmax_finish(d, s_flag, n_epi);
       break;
     }
     case EPI_SAMPLE:
@@ -644,6 +657,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   static_assert(NSTEP % PD == 0, "prefetch depth must divide the chunk steps");
   static_assert(LPR <= 64 && 64 % LPR == 0 && MT % (NW * RPP) == 0, "X staging layout");
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(NW * MT * 8 <= LDS, "argmax reduction buffer");
   static_assert(MT <= NTH && MT <= 256, "token tile");
 
   __shared__ __align__(16) unsigned char smem[LDS];
@@ -1072,6 +1086,64 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
       sc = rsqrtf(v / (float)d.k + d.x.eps);
     }
     s_scale[tid] = sc;
+  }
+  if (d.epi.kind == EPI_ARGMAX && !d.epi.dbg_logits && d.splits == 1 && !DUAL && !SAMPLE) {
+    // Row argmax straight from the accumulators: each lane keeps the best key of its
+    // tokens over its own columns, the lanes holding the same token combine by cross-lane
+    // swaps and the waves through LDS, and one atomicMax per token leaves the workgroup
+    // (no fp32 tile in LDS, no epilogue halves).  Same keys as the tile path: the scaled
+    // value of each logit and its column.
+    __syncthreads();  // s_scale is ready; every wave is done with the X buffers
+    unsigned long long* red = (unsigned long long*)smem;  // [NW][MT]
+    if constexpr (W32) {
+#pragma unroll
+      for (int t = 0; t < MT / 32; ++t) {
+        const float sc = s_scale[t * 32 + (lane & 31)];
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int p = 0; p < RB / 2; ++p)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int c = col0 + wid * RB * 16 + p * 32 + 8 * (q >> 2) + (lane >> 5) * 4 + (q & 3);
+            const unsigned long long key = c < d.n ? argmax_key(sc * acc32[p][t][q], (uint32_t)c) : 0ull;
+            best = key > best ? key : best;
+          }
+        const unsigned long long o = shfl_xor_u64(best, 32);
+        best = o > best ? o : best;
+        if (lane < 32) red[wid * MT + t * 32 + lane] = best;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < MT / 16; ++t) {
+        const float sc = s_scale[t * 16 + lr];
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = col0 + wid * RB * 16 + rb * 16 + lq * 4 + i;
+            const unsigned long long key = c < d.n ? argmax_key(sc * acc[rb][t][i], (uint32_t)c) : 0ull;
+            best = key > best ? key : best;
+          }
+        unsigned long long o = shfl_xor_u64(best, 16);
+        best = o > best ? o : best;
+        o = shfl_xor_u64(best, 32);
+        best = o > best ? o : best;
+        if (lane < 16) red[wid * MT + t * 16 + lane] = best;
+      }
+    }
+    __syncthreads();
+    if (tid < mv) {
+      unsigned long long b2 = red[tid];
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) {
+        const unsigned long long o = red[w2 * MT + tid];
+        b2 = o > b2 ? o : b2;
+      }
+      atomicMax(&d.epi.keys[m0 + tid], b2);
+    }
+    argmax_finish(d, &s_flag, ((d.n + TC - 1) / TC) * m_tiles);
+    return;
   }
   constexpr int TCH = TC / EH;  // output columns of one epilogue half
   const int n_epi = ((d.n + TC - 1) / TC) * m_tiles * EH;
