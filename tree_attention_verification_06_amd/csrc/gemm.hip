@@ -1352,24 +1352,25 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
     p.m_tiles = (m + F32_MT - 1) / F32_MT;
     return p;
   }
-  // Cost model (microseconds), fitted to measured launch times of every tile configuration
-  // and split count at the 8B- and 70B-shaped projections with 16..960 tokens, each launch
-  // timed with cold caches (a 768 MB read first evicts the 256 MB Infinity Cache, as the
-  // rest of a step does); rms error ~12%, MFMA rates bounded by the chip's peak.  Each
-  // workgroup needs most of a CU's LDS, so workgroups run in rounds of 256.  Per
-  // workgroup: its weight slice streams at min(31 GB/s, 7.4 TB/s / resident workgroups)
-  // while its MFMAs run (~4.5 TFLOP/s per CU), plus its X slice from L2 at 49 GB/s, a
-  // fixed ~10 us (launch, pipeline fill, epilogue) and the write of its split-K partial.
-  // Split-K adds a serial tail: the last workgroup of a tile reads every partial tile at
-  // ~64 GB/s, plus ~3.6 us.  The top-k epilogue costs ~1.2 us per 1000 (token, column)
-  // pairs of a tile.
-  constexpr double kBcu = 30.5e3, kBchip = 7.38e6, kBx = 48.7e3, kP1 = 4.61e6, kP2 = 4.45e6, kF0 = 10.0,
-                   kBfix = 64.4e3, kFsplit = 3.63, kTopk = 11.8e-4;  // bytes/us, flop/us, us
+  // Cost model (microseconds), fitted (least squares on log time) to the measured launch
+  // times of every tile configuration and K split at the 8B- and 70B-shaped projections
+  // with 16..960 tokens.  Workgroups run in rounds of 256 (each needs most of a CU's LDS).
+  // Eight-wave tiles, per workgroup: its weight slice streams at min(45 GB/s, 7.4 TB/s /
+  // resident workgroups) while its MFMAs run (2.4 TFLOP/s per CU with one 16-row block
+  // per wave, 3.3 with more), plus a fixed ~4 us; split-K adds a serial tail: the last
+  // workgroup of a tile reads every partial tile at ~40 GB/s, plus ~12 us.  Four-wave wide
+  // tiles (one K split): 30 GB/s, 5.1 TFLOP/s per CU and ~40 us fixed, so they only pay
+  // for themselves with hundreds of rows.  (The activation reads never limited the fit.)
+  // The top-k epilogue costs ~0.75 us per 1000 (token, column) pairs of a tile.
+  constexpr double kBcu = 44.7e3, kBchip = 7.38e6, kP1 = 2.36e6, kP2 = 3.33e6, kF0 = 3.9, kBfix = 39.5e3,
+                   kFsplit = 12.2, kTopk = 7.5e-4;                   // bytes/us, flop/us, us
+  constexpr double kBcuW = 29.9e3, kPW = 5.08e6, kF0W = 40.3;        // wide tiles
   double best = 1e30;
   int best_c = -1, best_s = 1;
   for (int c = 0; c < kNumCfgs; ++c) {
     const CfgInfo& cf = kCfgs[c];
-    if (c >= 7) continue;  // wide tiles: chosen below
+    const bool wide = c >= 7;
+    if (wide && (m < 192 || epi_kind == EPI_TOPK)) continue;  // never faster below a few hundred rows
     const int nt = cf.nw * cf.rb * 16;
     const int tc = dual ? nt / 2 : nt;
     if (epi_kind == EPI_QKV && (tc / cf.eh) % head_dim) continue;
@@ -1377,18 +1378,17 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
     const int m_tiles = (m + cf.mt - 1) / cf.mt;
     const int kchunks = (k + cf.kc - 1) / cf.kc;
     const int tiles = ((n + tc - 1) / tc) * m_tiles;
-    for (int s = 1; s <= std::min(kchunks, 8); ++s) {
+    for (int s = 1; s <= (wide ? 1 : std::min(kchunks, 8)); ++s) {
       const int cps = (kchunks + s - 1) / s;  // chunks per split
       const int se = (kchunks + cps - 1) / cps;
       if (se != s) continue;
       const double kps = (double)cps * cf.kc;
       const int G = tiles * se;
       const int rounds = (G + 255) / 256;
-      const double bw = std::min(kBcu, kBchip / std::min(G, 256));
+      const double bw = std::min(wide ? kBcuW : kBcu, kBchip / std::min(G, 256));
       const double flops = 2.0 * nt * cf.mt * kps;
       const double part = (double)nt * cf.mt * 4;
-      double per = std::max(nt * kps * 2 / bw, flops / (cf.rb == 1 ? kP1 : kP2)) + cf.mt * kps * 2 / kBx + kF0;
-      if (se > 1) per += part / kBx;
+      double per = std::max(nt * kps * 2 / bw, flops / (wide ? kPW : cf.rb == 1 ? kP1 : kP2)) + (wide ? kF0W : kF0);
       if (epi_kind == EPI_TOPK) per += kTopk * cf.mt * tc;
       double cost = rounds * per;
       if (se > 1) cost += se * part / kBfix + kFsplit;
@@ -1399,9 +1399,9 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
       }
     }
   }
-  // Wide tiles (four waves of 32x32x16 MFMAs) for LM-head shapes with a few hundred rows:
-  // measured 3-7% faster than the best eight-wave tile from 360 to 960 rows and no faster
-  // below.  Of the two token tiles, the one that pads fewer rows (ties: the wider one).
+  // LM heads of 320+ rows (argmax or sampling epilogue): the wide tiles were measured
+  // 1.5-2% faster than the best eight-wave tile from 360 to 960 rows; of the two token
+  // tiles, the one that pads fewer rows (ties: the wider one).
   if (!dual && n >= 32768 && m >= 320 && (epi_kind == EPI_ARGMAX || epi_kind == EPI_SAMPLE)) {
     const int pad7 = (m + kCfgs[7].mt - 1) / kCfgs[7].mt * kCfgs[7].mt;
     const int pad8 = (m + kCfgs[8].mt - 1) / kCfgs[8].mt * kCfgs[8].mt;
@@ -1466,12 +1466,12 @@ int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s) {
       case 6: dual ? launch_cfg<8, 2, 4, true, 160, 128, 2, 2>(d, grid, s) : launch_cfg<8, 2, 4, false, 160, 128, 2, 2>(d, grid, s); break;
       case 7:
       case 8:
-        // wide tiles: single-pass K only, no gate/up instance
-        if (dual || p.splits != 1) return EAGLE_ERR_UNSUPPORTED;
+        // wide tiles: a single K split only
+        if (p.splits != 1) return EAGLE_ERR_UNSUPPORTED;
         if (p.cfg == 7)
-          launch_cfg<4, 4, 4, false, 192, 128, 2, 2>(d, grid, s);
+          dual ? launch_cfg<4, 4, 4, true, 192, 128, 2, 2>(d, grid, s) : launch_cfg<4, 4, 4, false, 192, 128, 2, 2>(d, grid, s);
         else
-          launch_cfg<4, 4, 4, false, 160, 128, 2, 2>(d, grid, s);
+          dual ? launch_cfg<4, 4, 4, true, 160, 128, 2, 2>(d, grid, s) : launch_cfg<4, 4, 4, false, 160, 128, 2, 2>(d, grid, s);
         break;
       default: return EAGLE_ERR_UNSUPPORTED;
     }
