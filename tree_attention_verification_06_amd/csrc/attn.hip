@@ -40,7 +40,9 @@ constexpr int RBW = 1;                  // 16-row query blocks per wave
 constexpr int ROWS_WG = NWA * RBW * 16; // query rows per workgroup
 constexpr int KT = 64;                  // keys per LDS tile
 constexpr int HD = 128;
-constexpr int KS = HD + 8;              // LDS row stride of the K tile (bf16)
+constexpr int KS = HD + 16;             // LDS row stride of the K tile (bf16): 288 bytes, an
+                                        // odd multiple of 32, keeps the score reads (16 rows x
+                                        // four 16-byte groups) free of bank conflicts
 constexpr int VS = HD + 16;             // LDS row stride of the V tile (bf16): the four keys
                                         // of one transpose read land in distinct banks
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -51,6 +53,15 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 // low half.
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+// Maximum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes that hold one query row)
+// with the gfx950 lane swaps, which stay in the VALU (a shuffle would be an LDS round trip).
+__device__ __forceinline__ float max_xor16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ int remap_xcd(int b, int total) {
@@ -235,16 +246,21 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
     }
     // MASKED: scores in log2 units, -inf where hidden; unmasked: the raw q.k
     float s[RBW][4][4];
+    // all 16 K fragments of the tile are requested before the first score MFMA, so the
+    // LDS latency is paid once per tile rather than once per fragment
+    bf16x8_t kf[4][4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kf[st][kk] = *(const bf16x8_t*)(ksb + (st * 16 + lr) * KS + kk * 32 + lq * 8);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      bf16x8_t kf[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kf[kk] = *(const bf16x8_t*)(ksb + (st * 16 + lr) * KS + kk * 32 + lq * 8);
 #pragma unroll
       for (int j = 0; j < RBW; ++j) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[j][kk], acc, 0, 0, 0);
+        for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[st][kk], qf[j][kk], acc, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (MASKED) {
@@ -264,8 +280,7 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][st][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max_xor16_32(mx);
       if constexpr (!MASKED) mx *= sl2;  // sl2 > 0: the scaled maximum is the maximum scaled
       const float mnew = fmaxf(mrow[j], mx);
       const float mbase = (mnew == -INFINITY) ? 0.f : mnew;
