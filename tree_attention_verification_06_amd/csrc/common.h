@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/eagle.h"
 
 namespace eagle {
@@ -41,6 +43,68 @@ __device__ __forceinline__ float ord2f(uint32_t k) {
 // unsigned maximum is the largest value and, among equal values, the lowest index.
 __device__ __forceinline__ unsigned long long argmax_key(float v, uint32_t idx) {
   return ((unsigned long long)f2ord(v) << 32) | (unsigned long long)(0xffffffffu - idx);
+}
+
+// Top-k keys as doubles: the 52 mantissa bits hold (order-preserving bits of the fp32 value)
+// << 20 | (2^20 - 1 - column), and the exponent field is 1, so every key is a positive
+// normal double and doubles compare exactly like the packed integers (larger value first,
+// then smaller column).  A compare-and-swap step of the sorted insertion is then one
+// v_max_f64 and one v_min_f64 (inline: in IEEE mode the compiler would otherwise add a
+// quieting max per operand).  0.0 sorts below every key and marks an empty slot.
+__device__ __forceinline__ double topk_key(float v, uint32_t col) {
+  const unsigned long long k = (((unsigned long long)f2ord(v) << 20) | (unsigned long long)(0xfffffu - col)) +
+                               (1ull << 52);
+  return __longlong_as_double((long long)k);
+}
+__device__ __forceinline__ float topk_key_value(unsigned long long bits) {
+  return ord2f((uint32_t)((bits - (1ull << 52)) >> 20));
+}
+__device__ __forceinline__ int32_t topk_key_col(unsigned long long bits) {
+  return (int32_t)(0xfffffu - (uint32_t)((bits - (1ull << 52)) & 0xfffffull));
+}
+// l = max(k, l), k = min(k, l) (l is updated in place)
+__device__ __forceinline__ void topk_cas(double& k, double& l) {
+  double lo;
+  asm("v_min_f64 %1, %2, %0\n\tv_max_f64 %0, %2, %0" : "+v"(l), "=&v"(lo) : "v"(k));
+  k = lo;
+}
+
+// Maximum of a top-k key over the 64 lanes of the wave, in the VALU only (no LDS round
+// trips): DPP quad swaps (xor 1, xor 2), the half-row and row mirrors (combining the
+// quads of each 8- and 16-lane row), then the 16- and 32-lane swaps of gfx950.  Every
+// lane ends with the maximum.
+__device__ __forceinline__ double wave_max_key(double x) {
+  auto step = [](double v, double w) {
+    double r;
+    asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(v), "v"(w));
+    return r;
+  };
+  auto dpp = [](double v, auto ctrl) -> double {
+    constexpr int C = decltype(ctrl)::value;
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, C, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), C, 0xf, 0xf, false);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+  };
+  x = step(x, dpp(x, std::integral_constant<int, 0xb1>{}));   // quad_perm [1,0,3,2]
+  x = step(x, dpp(x, std::integral_constant<int, 0x4e>{}));   // quad_perm [2,3,0,1]
+  x = step(x, dpp(x, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+  x = step(x, dpp(x, std::integral_constant<int, 0x140>{}));  // row_mirror
+  {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+    const auto l = __builtin_amdgcn_permlane16_swap((uint32_t)b, (uint32_t)b, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+    x = step(__longlong_as_double((long long)(((unsigned long long)h[0] << 32) | l[0])),
+             __longlong_as_double((long long)(((unsigned long long)h[1] << 32) | l[1])));
+  }
+  {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+    const auto l = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+    x = step(__longlong_as_double((long long)(((unsigned long long)h[0] << 32) | l[0])),
+             __longlong_as_double((long long)(((unsigned long long)h[1] << 32) | l[1])));
+  }
+  return x;
 }
 
 // Cross-workgroup hand-off without whole-cache maintenance: data meant for another

@@ -281,9 +281,11 @@ __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
   __syncthreads();
   const float lse = mx + __logf((fred[0] + fred[1]) + (fred[2] + fred[3]));
 
-  unsigned long long lst[KL];
+  // candidate keys as doubles (see topk_key): one v_max_f64 / v_min_f64 pair per
+  // insertion step, and a wave maximum that stays in the VALU
+  double lst[KL];
 #pragma unroll
-  for (int i = 0; i < KL; ++i) lst[i] = 0ull;
+  for (int i = 0; i < KL; ++i) lst[i] = 0.0;
   // thread tid scans tiles tid, tid + 256, ... (the K candidates of a (tile, row) are
   // adjacent); a tile's K candidates are loaded together (unconditional, clamped loads),
   // so each tile costs one round trip
@@ -300,31 +302,22 @@ __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
 #pragma unroll
     for (int q = 0; q < KL; ++q) {
       if (q >= s.K) break;
-      unsigned long long key = ii[q] < 0 ? 0ull : argmax_key(vv[q], (uint32_t)ii[q]);
+      double key = ii[q] < 0 ? 0.0 : topk_key(vv[q], (uint32_t)ii[q]);
 #pragma unroll
-      for (int i = 0; i < KL; ++i) {
-        const unsigned long long hi = key > lst[i] ? key : lst[i];
-        key = key > lst[i] ? lst[i] : key;
-        lst[i] = hi;
-      }
+      for (int i = 0; i < KL; ++i) topk_cas(key, lst[i]);
     }
   }
   // each wave: K rounds of a wave maximum over its lanes' list heads (no barriers); the
   // winner pops its head (keys are unique: one per vocabulary id)
   __shared__ unsigned long long wtop[4][KMAX];
   for (int q = 0; q < s.K; ++q) {
-    unsigned long long best = lst[0];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long other = __shfl_xor(best, o, 64);
-      best = other > best ? other : best;
-    }
-    if (best != 0ull && lst[0] == best) {
+    const double best = wave_max_key(lst[0]);
+    if (best != 0.0 && lst[0] == best) {  // keys are unique: one lane pops its head
 #pragma unroll
       for (int i = 0; i < KL - 1; ++i) lst[i] = lst[i + 1];
-      lst[KL - 1] = 0ull;
+      lst[KL - 1] = 0.0;
     }
-    if (lane == 0) wtop[w][q] = best;
+    if (lane == 0) wtop[w][q] = (unsigned long long)__double_as_longlong(best);
   }
   __syncthreads();
   if (tid == 0) {
@@ -342,8 +335,8 @@ __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
       }
       if (best != 0ull) head[bw]++;
       const bool ok = best != 0ull;
-      s.row_val[(int64_t)r * s.K + q] = ok ? ord2f((uint32_t)(best >> 32)) : -INFINITY;
-      s.row_idx[(int64_t)r * s.K + q] = ok ? (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffull)) : -1;
+      s.row_val[(int64_t)r * s.K + q] = ok ? topk_key_value(best) : -INFINITY;
+      s.row_idx[(int64_t)r * s.K + q] = ok ? topk_key_col(best) : -1;
     }
     s.row_lse[r] = lse;
   }

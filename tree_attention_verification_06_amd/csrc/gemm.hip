@@ -164,30 +164,6 @@ __device__ __forceinline__ void epi_store_rows(const GemmDesc& d, const float* t
   }
 }
 
-// Top-k keys as doubles: the 52 mantissa bits hold (order-preserving bits of the fp32 value)
-// << 20 | (2^20 - 1 - column), and the exponent field is 1, so every key is a positive
-// normal double and doubles compare exactly like the packed integers (larger value first,
-// then smaller column).  A compare-and-swap step of the sorted insertion is then one
-// v_max_f64 and one v_min_f64 (inline: in IEEE mode the compiler would otherwise add a
-// quieting max per operand).  0.0 sorts below every key and marks an empty slot.
-__device__ __forceinline__ double topk_key(float v, uint32_t col) {
-  const unsigned long long k = (((unsigned long long)f2ord(v) << 20) | (unsigned long long)(0xfffffu - col)) +
-                               (1ull << 52);
-  return __longlong_as_double((long long)k);
-}
-__device__ __forceinline__ float topk_key_value(unsigned long long bits) {
-  return ord2f((uint32_t)((bits - (1ull << 52)) >> 20));
-}
-__device__ __forceinline__ int32_t topk_key_col(unsigned long long bits) {
-  return (int32_t)(0xfffffu - (uint32_t)((bits - (1ull << 52)) & 0xfffffull));
-}
-// l = max(k, l), k = min(k, l) (l is updated in place)
-__device__ __forceinline__ void topk_cas(double& k, double& l) {
-  double lo;
-  asm("v_min_f64 %1, %2, %0\n\tv_max_f64 %0, %2, %0" : "+v"(l), "=&v"(lo) : "v"(k));
-  k = lo;
-}
-
 // EPI_TOPK with per-thread candidate lists of KL entries (KL >= k): the branch-free sorted
 // insertion costs KL compare-and-swap steps per column, so the list is no longer than needed.
 template <int KL>
