@@ -374,8 +374,15 @@ __global__ __launch_bounds__(NWA * 64) void tree_attn_bf16_kernel(AttnArgs a, in
 
 // Combine the chunks of every query row in fixed order: o = sum_c 2^(m_c - M) o_c / L.
 // A workgroup takes MROWS rows; 32 threads per row, each with 4 consecutive d (16-byte
-// partial loads, one 8-byte bf16 store).
+// partial loads, one 8-byte bf16 store).  The partial loads do not wait for the prefix
+// length: all MB chunks of a batch are loaded at once (clamped addresses, so they stay
+// inside the workspace) and the chunks without data are dropped by selects afterwards, so
+// a batch costs one round trip to memory.  MB is the smallest of 2, 4, 8, 12, 16 that covers
+// the chunks (clamped duplicates would only add traffic); with more than 16 chunks the
+// running (M, L, O) are rescaled between batches, otherwise the result is the two-pass
+// one, bit for bit.
 constexpr int MROWS = 8;
+template <int MB>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int grid_real) {
   const int bid = blockIdx.x;
   if (bid >= grid_real) return;
@@ -387,49 +394,58 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int grid_re
   t /= rgroups;
   const int kvh = t % a.hkv;
   const int b = t / a.hkv;
+  const int row = rg * MROWS + threadIdx.x / 32;
+  const int lrow = min(row, rmax - 1);  // address of the loads (rows past rmax exit below)
+  const int d4 = (threadIdx.x % 32) * 4;
+  const int nc = a.n_chunks;
+  const int64_t base = (int64_t)(b * a.hkv + kvh) * nc;
+  // scalars of the sequence (their loads overlap those of the first batch)
   const int off = a.tree_off[b];
   const int N = a.n_nodes ? a.n_nodes[b] : a.tree_off[b + 1] - off;
   const int qlo = a.q_lo ? a.q_lo[b] : 0;
-  const int row = rg * MROWS + threadIdx.x / 32;
-  const int d4 = (threadIdx.x % 32) * 4;
-  if (row >= (N - qlo) * g || N - qlo > a.max_nodes || N > 64 * a.mw) return;
   const int P = min(max(a.prefix_len[b], 0), a.cap);
-  const int n_pref = min((P + a.kch - 1) / a.kch, a.n_chunks - 1);
-  const int64_t base = (int64_t)(b * a.hkv + kvh) * a.n_chunks;
-  // chunks with data: prefix chunks 0..n_pref-1, then the tree chunk; read four at a
-  // time with clamped (unconditional) loads so the round trips overlap
-  const int cnt = n_pref + 1;
-  auto chunk_of = [&](int j) { return j < n_pref ? j : a.n_chunks - 1; };
-  float M = -INFINITY;
-  for (int j0 = 0; j0 < cnt; j0 += 4) {
-    float m4[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) m4[u] = a.part_ml[((base + chunk_of(min(j0 + u, cnt - 1))) * rmax + row) * 2];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) M = fmaxf(M, m4[u]);
-  }
-  float L = 0.f;
+  float M = -INFINITY, L = 0.f;
   float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j0 = 0; j0 < cnt; j0 += 4) {
-    float m4[4], l4[4];
-    float4 o4[4];
+  for (int j0 = 0; j0 < nc; j0 += MB) {
+    float2 ml[MB];
+    float4 o4[MB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t pi = (base + chunk_of(min(j0 + u, cnt - 1))) * rmax + row;
-      m4[u] = a.part_ml[pi * 2];
-      l4[u] = a.part_ml[pi * 2 + 1];
+    for (int u = 0; u < MB; ++u) {
+      const int64_t pi = (base + min(j0 + u, nc - 1)) * rmax + lrow;
+      ml[u] = *(const float2*)(a.part_ml + pi * 2);
       o4[u] = *(const float4*)(a.part_o + pi * HD + d4);
     }
+    // chunks with data: prefix chunks 0..n_pref-1, then the tree chunk (the last)
+    const int n_pref = min((P + a.kch - 1) / a.kch, nc - 1);
+    bool ok[MB];
+    float mb = M;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float f = (j0 + u < cnt) ? exp2f(m4[u] - M) : 0.f;
-      L += f * l4[u];
+    for (int u = 0; u < MB; ++u) {
+      const int j = j0 + u;
+      ok[u] = j < nc && (j < n_pref || j == nc - 1);
+      mb = ok[u] ? fmaxf(mb, ml[u].x) : mb;
+    }
+    if (j0 > 0) {  // rescale what earlier batches summed (M = -inf: nothing summed yet)
+      const float r = M > -INFINITY ? exp2f(M - mb) : 0.f;
+      L *= r;
+      O.x *= r;
+      O.y *= r;
+      O.z *= r;
+      O.w *= r;
+    }
+    M = mb;
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      if (!ok[u]) continue;
+      const float f = exp2f(ml[u].x - M);
+      L += f * ml[u].y;
       O.x += f * o4[u].x;
       O.y += f * o4[u].y;
       O.z += f * o4[u].z;
       O.w += f * o4[u].w;
     }
   }
+  if (row >= (N - qlo) * g || N - qlo > a.max_nodes || N > 64 * a.mw) return;
   const float4 out = make_float4(O.x / L, O.y / L, O.z / L, O.w / L);
   const int node = qlo + row / g, hh = row % g;
   const int64_t orow = a.q_stride ? (int64_t)b * a.q_stride + (node - qlo) : (int64_t)(off + node);
@@ -613,7 +629,16 @@ int launch_attn(AttnArgs& a, const AttnPlan& p, eagle_timer* timer, hipStream_t 
   const int g = a.hq / a.hkv;
   const int mgrid = a.batch * a.hkv * ((a.max_nodes * g + MROWS - 1) / MROWS);
   timer_begin(timer, ST_ATTN_MERGE, s);
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(mgrid), dim3(256), 0, s, a, mgrid);
+  if (p.n_chunks <= 2)
+    hipLaunchKernelGGL(attn_merge_kernel<2>, dim3(mgrid), dim3(256), 0, s, a, mgrid);
+  else if (p.n_chunks <= 4)
+    hipLaunchKernelGGL(attn_merge_kernel<4>, dim3(mgrid), dim3(256), 0, s, a, mgrid);
+  else if (p.n_chunks <= 8)
+    hipLaunchKernelGGL(attn_merge_kernel<8>, dim3(mgrid), dim3(256), 0, s, a, mgrid);
+  else if (p.n_chunks <= 12)
+    hipLaunchKernelGGL(attn_merge_kernel<12>, dim3(mgrid), dim3(256), 0, s, a, mgrid);
+  else
+    hipLaunchKernelGGL(attn_merge_kernel<16>, dim3(mgrid), dim3(256), 0, s, a, mgrid);
   timer_end(timer, s);
   return hipGetLastError() == hipSuccess ? EAGLE_OK : EAGLE_ERR_HIP;
 }
