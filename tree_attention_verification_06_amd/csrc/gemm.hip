@@ -207,11 +207,17 @@ __device__ __forceinline__ void epi_topk(const GemmDesc& d, const float* tile, i
     }
   }
   __syncthreads();  // every read of the tile is done: its LDS is reused below
-  unsigned long long* sl = (unsigned long long*)tile;          // [P][mt][KL]
+  // lists token-minor, [P][KL][mt]: the lanes of a wave (consecutive tokens) store and
+  // read consecutive 8-byte words, and since mt * 2 words is a multiple of the 64 banks
+  // the merge's reads stay conflict-free whatever list position each lane is at
+  unsigned long long* sl = (unsigned long long*)tile;
   float* sm = (float*)(sl + (size_t)P * mt * KL);             // [P][mt][2]
   if (active) {
+    if (part > 0 || P > 4) {  // (with P <= 4 part 0 keeps its list in registers)
 #pragma unroll
-    for (int q = 0; q < KL; ++q) sl[((size_t)part * mt + t) * KL + q] = (unsigned long long)__double_as_longlong(lst[q]);
+      for (int q = 0; q < KL; ++q)
+        sl[((size_t)part * KL + q) * mt + t] = (unsigned long long)__double_as_longlong(lst[q]);
+    }
     sm[(part * mt + t) * 2] = mx;
     sm[(part * mt + t) * 2 + 1] = se;
   }
@@ -227,21 +233,52 @@ __device__ __forceinline__ void epi_topk(const GemmDesc& d, const float* tile, i
     const int64_t ob = (int64_t)tile_i * d.m + m0 + t;  // tile-major: coalesced per workgroup
     e.lse_part[ob * 2] = M;
     e.lse_part[ob * 2 + 1] = S;
-    // P-way merge of the sorted lists (keys are unique: one per column)
+    if (P <= 4) {
+      // part 0 inserts the other parts' candidates into its own register list (KL
+      // compare-and-swap steps each, no LDS round trip between them)
+      for (int p2 = 1; p2 < P; ++p2)
+        for (int q = 0; q < KL; ++q) {
+          double key = __longlong_as_double((long long)sl[((size_t)p2 * KL + q) * mt + t]);
+#pragma unroll
+          for (int i = 0; i < KL; ++i) topk_cas(key, lst[i]);
+        }
+#pragma unroll
+      for (int q = 0; q < KL; ++q) {
+        if (q >= K) break;
+        const unsigned long long best = (unsigned long long)__double_as_longlong(lst[q]);
+        const bool valid = best != 0ull;
+        e.topk_val[ob * K + q] = valid ? topk_key_value(best) : -INFINITY;
+        e.topk_idx[ob * K + q] = valid ? topk_key_col(best) : -1;
+      }
+      return;
+    }
+    // P-way merge of the sorted lists (keys are unique: one per column).  The heads of a
+    // round are read unconditionally (clamped list and position, dropped by a select), so
+    // a round costs one LDS round trip rather than one per list.
     int head[8];
 #pragma unroll
     for (int p2 = 0; p2 < 8; ++p2) head[p2] = 0;
     for (int q = 0; q < K; ++q) {
+      unsigned long long c[8];
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2)
+        c[p2] = sl[((size_t)min(p2, P - 1) * KL + min(head[p2], KL - 1)) * mt + t];
+      if (P > 4) {
+#pragma unroll
+        for (int p2 = 4; p2 < 8; ++p2)
+          c[p2] = sl[((size_t)min(p2, P - 1) * KL + min(head[p2], KL - 1)) * mt + t];
+      } else {
+#pragma unroll
+        for (int p2 = 4; p2 < 8; ++p2) c[p2] = 0ull;
+      }
       unsigned long long best = 0ull;
       int bp = 0;
 #pragma unroll
       for (int p2 = 0; p2 < 8; ++p2) {
-        if (p2 < P && head[p2] < KL) {
-          const unsigned long long c = sl[((size_t)p2 * mt + t) * KL + head[p2]];
-          if (c > best) {
-            best = c;
-            bp = p2;
-          }
+        const unsigned long long v = (p2 < P && head[p2] < KL) ? c[p2] : 0ull;
+        if (v > best) {
+          best = v;
+          bp = p2;
         }
       }
 #pragma unroll
@@ -378,7 +415,7 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
 // col0 + r (for dual tiles: gate columns r < tc, up columns r >= tc) of token m0 + t,
 // before the per-row norm scale scale[t].
 // CPLC: output columns per lane of the store epilogue, ceil(tc / 64) at most.
-template <int CPLC, bool WITH_SAMPLE>
+template <int CPLC, bool WITH_SAMPLE, bool WITH_TOPK = true>
 __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int tc, int col0, int m0, int mv,
                              int mt, const float* scale, float* red_scratch, int* s_flag, int n_epi) {
   const Epi& e = d.epi;
@@ -500,12 +537,16 @@ __device__ void run_epilogue(const GemmDesc& d, const float* tile, int ts, int t
       if constexpr (WITH_SAMPLE) epi_sample(d, const_cast<float*>(tile), ts, tc, col0, m0, mv, mt, scale);
       break;
     case EPI_TOPK: {
-      // (one more list length here would be inlined into every GEMM instance and push the
-      // widest ones into register spills)
-      if (e.topk <= 12)
-        epi_topk<12>(d, tile, ts, tc, col0, m0, mv, mt, scale);
-      else
-        epi_topk<16>(d, tile, ts, tc, col0, m0, mv, mt, scale);
+      // (every list length is inlined into each tile instance that carries the top-k
+      // epilogue: the eight-wave tiles of up to 160 tokens, which have the registers)
+      if constexpr (WITH_TOPK) {
+        if (e.topk <= 10)
+          epi_topk<10>(d, tile, ts, tc, col0, m0, mv, mt, scale);
+        else if (e.topk <= 12)
+          epi_topk<12>(d, tile, ts, tc, col0, m0, mv, mt, scale);
+        else
+          epi_topk<16>(d, tile, ts, tc, col0, m0, mv, mt, scale);
+      }
       break;
     }
     default:
@@ -628,6 +669,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
   // file for its accumulators.  The weight fragments stay in the 16-row layout; a lane
   // swap turns two of them into the operands of two 32-row MFMAs (below).
   constexpr bool W32 = NW == 4;
+  // the top-k epilogue is compiled into the eight-wave tiles of up to 160 tokens only (the
+  // planner never gives it the others)
+  constexpr bool TOPK_TILE = !W32 && MT <= 160;
   static_assert(!W32 || (RB % 2 == 0 && MT % 32 == 0), "wide tiles pair 16-row blocks and use 32-token blocks");
   static_assert(!W32 || (XB == 2 && NSTEP >= 2 && RPW == MT / 16), "wide tiles stage one X row per MFMA group");
   static_assert(NSTEP % PD == 0, "prefetch depth must divide the chunk steps");
@@ -1169,7 +1213,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
     if constexpr (SAMPLE)
       epi_sample(d, tile, TS, TCH, col0 + h * TCH, m0, mv, MT, s_scale);
     else
-      run_epilogue<(TCH + 63) / 64, false>(d, tile, TS, TCH, col0 + h * TCH, m0, mv, MT, s_scale, (float*)s_red,
+      run_epilogue<(TCH + 63) / 64, false, TOPK_TILE>(d, tile, TS, TCH, col0 + h * TCH, m0, mv, MT, s_scale, (float*)s_red,
                                            &s_flag, n_epi);
   }
 }
@@ -1281,7 +1325,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmDesc d, int grid_real
   __syncthreads();
   const int tc = d.dual ? F32_NT / 2 : F32_NT;
   const int c0 = d.dual ? col0 / 2 : col0;
-  run_epilogue<(F32_NT + 63) / 64, true>(d, tile, TS, tc, c0, m0, mv, F32_MT, s_scale, (float*)s_red, &s_flag,
+  run_epilogue<(F32_NT + 63) / 64, true, false>(d, tile, TS, tc, c0, m0, mv, F32_MT, s_scale, (float*)s_red, &s_flag,
                                          grid_real);
 }
 
@@ -1347,6 +1391,7 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
     const CfgInfo& cf = kCfgs[c];
     const bool wide = c >= 7;
     if (wide && (m < 192 || epi_kind == EPI_TOPK)) continue;  // never faster below a few hundred rows
+    if (epi_kind == EPI_TOPK && cf.mt > 160) continue;  // the top-k epilogue is not compiled into these
     const int nt = cf.nw * cf.rb * 16;
     const int tc = dual ? nt / 2 : nt;
     if (epi_kind == EPI_QKV && (tc / cf.eh) % head_dim) continue;
@@ -1420,6 +1465,7 @@ int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s) {
   if (p.cfg != 100 && (d.x.a.dtype != EAGLE_BF16 || d.x.b.dtype != EAGLE_BF16)) return EAGLE_ERR_UNSUPPORTED;
   if (p.cfg == 100 && d.epi.kind == EPI_TOPK) return EAGLE_ERR_UNSUPPORTED;  // its LDS tile is too small
   if (d.epi.kind == EPI_TOPK && d.n > (1 << 20)) return EAGLE_ERR_UNSUPPORTED;  // 20-bit columns in the keys
+  if (d.epi.kind == EPI_TOPK && (p.cfg >= 7 || kCfgs[p.cfg].mt > 160)) return EAGLE_ERR_UNSUPPORTED;
   if (p.cfg == 100 && d.w_layout) return EAGLE_ERR_UNSUPPORTED;              // fragment blocks are bf16
   if (d.dual && d.epi.kind == EPI_SAMPLE) return EAGLE_ERR_UNSUPPORTED;
   const int grid = p.w_tiles * p.m_tiles * p.splits;
