@@ -193,3 +193,18 @@ def test_full_eagle_step_llama8b_b16():
     assert (np.diff(tree["tree_off"]) == wl.draft.max_nodes).all()
     check_draft_numerics(wl, wl.draft, pool, sample, label=wl.name)
     _log(f"  draft checked {time.time() - t0:.1f}s")
+
+
+@pytest.mark.parametrize("seqs", [(1, 2, 3, 4), (5, 6, 7, 8), (10, 11, 12), (13, 14, 15)])
+def test_full_eagle_step_llama8b_b16_other_sequences(seqs):
+    """The same step; the oracle checks the other fourteen sequences, a few per test (the
+    teacher-forced draft of one sequence takes the fp64 oracle ~5 s), so that every one of
+    the 16 drafted and verified trees is compared element-wise with the oracle."""
+    t0 = time.time()
+    wl = make_workload(5)
+    acc = _step_check(wl, seqs, wl.name + f" seqs {seqs}", layout=1)
+    _log(f"  step checked {time.time() - t0:.1f}s, accept lengths {acc.tolist()}")
+    t, d, tree, pool = _draft(wl)
+    check_draft_structure(tree, pool, wl.draft, wl.batch)
+    check_draft_numerics(wl, wl.draft, pool, list(seqs), label=wl.name)
+    _log(f"  draft checked {time.time() - t0:.1f}s")
