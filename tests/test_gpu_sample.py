@@ -297,6 +297,15 @@ def test_sample_llama8b_batch16():
     _check(wl, r, 0.3, "8b batch16")
 
 
+@pytest.mark.parametrize("trees", [(1, 2, 3, 4, 5), (6, 7, 8, 10, 11), (12, 13, 14, 15)])
+def test_sample_llama8b_batch16_other_trees(trees):
+    """The same batch; the oracle computes the other fourteen trees, a few per test, so that
+    every tree of the 960-row launch is compared with the oracle."""
+    wl = make_workload(2, batch=16, parents=[T.static_tree_60() for _ in range(16)])
+    r = _run(wl, temperature=0.3, layout=1, trees=list(trees))
+    _check(wl, r, 0.3, f"8b batch16 trees {trees}")
+
+
 def test_sample_duplicate_siblings_rejected():
     """Two children of one node with the same token: the tree is refused on the device
     (status EAGLE_ERR_TREE), that sequence gets accept_len -1 and nothing is committed."""
