@@ -52,11 +52,15 @@ def _draft(wl):
 
 CASES = [
     # (seed, B, prefix, params, lm scale): peaked full trees; near-uniform draft with many
-    # near-ties; pruning at 0.3 that leaves short trees (padded outputs); a wide frontier
+    # near-ties; pruning at 0.3 that leaves short trees (padded outputs); a wide frontier;
+    # top_k 12 and 16
     (11, 3, [37, 100, 0], DraftParams(depth=4, top_k=4, frontier=3, max_nodes=16), 16),
     (12, 2, [64, 5], DraftParams(depth=3, top_k=5, frontier=4, max_nodes=20), 1),
     (11, 3, [37, 100, 0], DraftParams(depth=4, top_k=4, frontier=3, max_nodes=16, conf_threshold=0.3), 8),
     (13, 2, [130, 257], DraftParams(depth=6, top_k=10, frontier=10, max_nodes=60), 16),
+    # the 12- and 16-entry candidate lists of the LM-head epilogue and of the per-row merge
+    (14, 2, [40, 90], DraftParams(depth=3, top_k=12, frontier=8, max_nodes=40), 16),
+    (15, 2, [70, 20], DraftParams(depth=3, top_k=16, frontier=6, max_nodes=48), 16),
 ]
 
 
@@ -68,7 +72,9 @@ def test_draft_mini_teacher_forced(case):
     t, d, tree, pool = _draft(wl)
     check_draft_structure(tree, pool, params, B)
     _, frac = check_draft_numerics(wl, params, pool, range(B), label=f"case {case}")
-    assert frac > 0.1  # enough decisive ranks for the top-k check to bite
+    # enough decisive ranks for the top-k check to bite (a gap counts relative to the row's
+    # largest logit, so deep ranks of a top-16 list are decisive less often)
+    assert frac > (0.05 if params.top_k > 12 else 0.1)
 
 
 def test_draft_pruned_trees_are_short_and_padded():
