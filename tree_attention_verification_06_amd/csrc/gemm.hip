@@ -176,7 +176,8 @@ __device__ __forceinline__ void epi_topk(const GemmDesc& d, const float* tile, i
   // (P = nth / mt parts per token): a wave reads one column for 64 consecutive tokens,
   // which is conflict-free in the column-major tile.  Each thread keeps its best
   // candidates as a sorted register list (branch-free insertion, static indices); the
-  // lists and partial (max, sum) pairs of a token are then merged through LDS.
+  // partial (max, sum) pairs of a token and the lists of its parts then meet through LDS,
+  // where the first part merges the others into its own list.
   const int K = e.topk;
   const int tile_i = col0 / tc;
   const int P = nth / mt;  // parts per token; threads past P * mt (mt not dividing nth) sit out
