@@ -248,22 +248,11 @@ __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
   const int Rl = s.B * s.FL;
   const float* lp = s.tk_lse + (int64_t)r * 2;
   const int64_t ls = (int64_t)Rl * 2;
-  // both passes over the tiles issue 4 loads per thread per round (clamped, unconditional)
+  // one pass over the tiles' (max, sum) pairs, 4 loads per thread per round (clamped,
+  // unconditional), summed with a running maximum; waves, then the workgroup, combine their
+  // (max, sum) pairs the same way
   const int nth = blockDim.x;
-  float mx = -INFINITY;
-  for (int t0 = tid; t0 < s.n_tk; t0 += 4 * nth) {
-    float m4[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) m4[u] = lp[min(t0 + u * nth, s.n_tk - 1) * ls];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) mx = fmaxf(mx, m4[u]);  // clamped repeats change no maximum
-  }
-  mx = wave_max(mx);
-  if (lane == 0) fred[w] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
-  __syncthreads();
-  float se = 0.f;
+  float mx = -INFINITY, se = 0.f;
   for (int t0 = tid; t0 < s.n_tk; t0 += 4 * nth) {
     float m4[4], s4[4];
 #pragma unroll
@@ -273,13 +262,27 @@ __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
       s4[u] = lp[o + 1];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (t0 + u * nth < s.n_tk) se += s4[u] * __expf(m4[u] - mx);
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = t0 + u * nth < s.n_tk && m4[u] > -INFINITY;
+      const float mn = ok ? fmaxf(mx, m4[u]) : mx;
+      const float add = ok ? s4[u] * __expf(m4[u] - mn) : 0.f;
+      se = (mx > -INFINITY ? se * __expf(mx - mn) : 0.f) + add;
+      mx = mn;
+    }
   }
-  se = wave_sum(se);
-  if (lane == 0) fred[w] = se;
+  const float wm = wave_max(mx);
+  se = wave_sum(mx > -INFINITY ? se * __expf(mx - wm) : 0.f);
+  __shared__ float fsum[4];
+  if (lane == 0) {
+    fred[w] = wm;
+    fsum[w] = se;
+  }
   __syncthreads();
-  const float lse = mx + __logf((fred[0] + fred[1]) + (fred[2] + fred[3]));
+  const float M = fmaxf(fmaxf(fred[0], fred[1]), fmaxf(fred[2], fred[3]));
+  float S = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) S += fred[i] > -INFINITY ? fsum[i] * __expf(fred[i] - M) : 0.f;
+  const float lse = M + __logf(S);
 
   // candidate keys as doubles (see topk_key): one v_max_f64 / v_min_f64 pair per
   // insertion step, and a wave maximum that stays in the VALU
