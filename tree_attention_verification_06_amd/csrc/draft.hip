@@ -244,10 +244,9 @@ __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
   if (j >= s.cnt[C_NF * s.B + b]) return;
   __shared__ float fred[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // per-tile outputs are stored tile-major: [tile][row][...] with Rl rows per tile
-  const int Rl = s.B * s.FL;
-  const float* lp = s.tk_lse + (int64_t)r * 2;
-  const int64_t ls = (int64_t)Rl * 2;
+  // per-tile outputs are stored row-major: [row][tile][...], so this row's are contiguous
+  const float* lp = s.tk_lse + (int64_t)r * s.n_tk * 2;
+  const int64_t ls = 2;
   // one pass over the tiles' (max, sum) pairs, 4 loads per thread per round (clamped,
   // unconditional), summed with a running maximum; waves, then the workgroup, combine their
   // (max, sum) pairs the same way
@@ -289,23 +288,24 @@ __global__ __launch_bounds__(256) void draft_topk_merge_kernel(DraftState s) {
   double lst[KL];
 #pragma unroll
   for (int i = 0; i < KL; ++i) lst[i] = 0.0;
-  // thread tid scans tiles tid, tid + 256, ... (the K candidates of a (tile, row) are
-  // adjacent); a tile's K candidates are loaded together (unconditional, clamped loads),
-  // so each tile costs one round trip
-  for (int t = tid; t < s.n_tk; t += blockDim.x) {
-    const int64_t o0 = ((int64_t)t * Rl + r) * s.K;
-    float vv[KL];
-    int ii[KL];
+  // the row's n_tk * K candidates are contiguous: thread tid takes candidates tid, tid +
+  // 256, ... (coalesced), CU of them per round with unconditional, clamped loads (a
+  // candidate past the end repeats the last one and is dropped, inserting the empty key 0)
+  constexpr int CU = 16;
+  const int64_t ob = (int64_t)r * s.n_tk * s.K;
+  const int ne = s.n_tk * s.K;
+  for (int e0 = tid; e0 < ne; e0 += CU * nth) {
+    float vv[CU];
+    int ii[CU];
 #pragma unroll
-    for (int q = 0; q < KL; ++q) {
-      const int64_t o = o0 + min(q, s.K - 1);
-      vv[q] = s.tk_val[o];
-      ii[q] = s.tk_idx[o];
+    for (int u = 0; u < CU; ++u) {
+      const int64_t o = ob + min(e0 + u * nth, ne - 1);
+      vv[u] = s.tk_val[o];
+      ii[u] = s.tk_idx[o];
     }
 #pragma unroll
-    for (int q = 0; q < KL; ++q) {
-      if (q >= s.K) break;
-      double key = ii[q] < 0 ? 0.0 : topk_key(vv[q], (uint32_t)ii[q]);
+    for (int u = 0; u < CU; ++u) {
+      double key = (e0 + u * nth < ne && ii[u] >= 0) ? topk_key(vv[u], (uint32_t)ii[u]) : 0.0;
 #pragma unroll
       for (int i = 0; i < KL; ++i) topk_cas(key, lst[i]);
     }
@@ -795,6 +795,7 @@ int draft_expand_impl(const eagle_dims* d, const eagle_draft_params* pr, const v
       g.epi.topk_idx = (int32_t*)(w + L.tk_idx);
       g.epi.lse_part = (float*)(w + L.tk_lse);
       g.epi.topk = K;
+      g.epi.n_part = L.p_lm[i].n_tiles;
       if ((rc = gemm(g, L.p_lm[i], ST_LM_HEAD))) return rc;
     }
     timer_begin(timer, ST_DRAFT_TOPK, s);

@@ -70,10 +70,12 @@ struct Epi {
   int32_t* argmax_out;
   float* max_out;
   int* done;
-  // EPI_TOPK: per (tile, row) the tile's top-k (value, index) and its (max, sum exp) pair
-  float* topk_val;   // [n_tiles][m][topk]
-  int32_t* topk_idx; // [n_tiles][m][topk]
-  float* lse_part;   // [n_tiles][m][2]
+  // EPI_TOPK: per (row, tile) the tile's top-k (value, index) and its (max, sum exp) pair,
+  // row-major so that a row's candidates are contiguous for the per-row merge (n_part =
+  // the launch's column tiles)
+  float* topk_val;   // [m][n_part][topk]
+  int32_t* topk_idx; // [m][n_part][topk]
+  float* lse_part;   // [m][n_part][2]
   int topk;
   // EPI_SAMPLE: tempered logits v = inv_t * logit.  For every row c with a parent row
   // gparent[c] (-1: none) in the tile, the tile's value at (gparent[c], ctoken[c]), if
@@ -92,7 +94,7 @@ struct Epi {
   int max_nodes;
   float* child_logit;
   float4* samp_part;
-  int n_part;
+  int n_part;  // column tiles of the launch (EPI_SAMPLE, EPI_TOPK)
 };
 
 struct GemmDesc {

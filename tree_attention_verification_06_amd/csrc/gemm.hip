@@ -232,7 +232,7 @@ __device__ __forceinline__ void epi_topk(const GemmDesc& d, const float* tile, i
       const float m2 = sm[(p2 * mt + t) * 2];
       if (m2 > -INFINITY) S += sm[(p2 * mt + t) * 2 + 1] * __expf(m2 - M);
     }
-    const int64_t ob = (int64_t)tile_i * d.m + m0 + t;  // tile-major: coalesced per workgroup
+    const int64_t ob = (int64_t)(m0 + t) * e.n_part + tile_i;  // row-major: a row's tiles adjacent
     e.lse_part[ob * 2] = M;
     e.lse_part[ob * 2 + 1] = S;
     if (P <= 4) {
