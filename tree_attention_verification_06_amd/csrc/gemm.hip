@@ -1425,15 +1425,17 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
   // Shapes where the model's pick was measured well behind the best (tile configuration,
   // K split) of a sweep over all of them (the 8B- and 70B-shaped projections, rows 16..960),
   // confirmed by alternating runs of both picks: the measured best is taken for row counts
-  // within 25% of the swept one.  All in the 160..256-row range, where the model rates the
-  // 128-row tile with few K splits too well (QKV 19-23%, O 6-20%, down 15% faster).
+  // within 25% of the swept one.  All in the 160..256-row range of the draft's levels: QKV
+  // 19-23%, O 6-20% and down 15% faster than the model's 128-row tiles with few K splits;
+  // gate/up (128-token tiles instead of 160) and the draft's feature FC 3-4%.
   struct TunedPick {
     int n, k, dual, epi, m, cfg, splits;
   };
   static constexpr TunedPick kTuned[] = {
       {6144, 4096, 0, EPI_QKV, 160, 1, 3},    {6144, 4096, 0, EPI_QKV, 256, 1, 2},
       {4096, 4096, 0, EPI_RESID, 256, 2, 2},  {4096, 14336, 0, EPI_RESID, 160, 1, 5},
-      {10240, 8192, 0, EPI_QKV, 160, 1, 2},   {8192, 8192, 0, EPI_RESID, 160, 3, 4}};
+      {10240, 8192, 0, EPI_QKV, 160, 1, 2},   {8192, 8192, 0, EPI_RESID, 160, 3, 4},
+      {14336, 4096, 1, EPI_SILU, 160, 3, 1},  {4096, 8192, 0, EPI_RESID, 160, 1, 4}};
   {
     double bestd = 0.2232;  // |ln(m / swept m)| <= ln 1.25
     for (const TunedPick& t : kTuned) {
