@@ -33,13 +33,14 @@ struct AttnArgs {
   float* dbg;            // optional [sum N][hq * hd] f32
   // split-KV plan and partials (bf16 path)
   int kch, n_chunks;     // prefix chunk length; chunks including the tree chunk
-  int row_groups;        // groups of 128 query rows per (b, kv head)
+  int row_groups;        // groups of query rows (16 per wave) per (b, kv head)
   float* part_o;         // [B][hkv][n_chunks][rmax][hd]
   float* part_ml;        // [B][hkv][n_chunks][rmax][2]
 };
 
 struct AttnPlan {
   int kch, n_chunks, row_groups, rmax;
+  int nwa;  // waves per workgroup of the bf16 kernel (4 or 8)
 };
 
 AttnPlan plan_attn(int dtype, int batch, int hq, int hkv, int hd, int max_nodes, int max_prefix);

@@ -27,6 +27,7 @@ __global__ __launch_bounds__(128) void tree_build_kernel(const int32_t* tree_off
   const int b = blockIdx.x;
   const int off = tree_off[b];
   const int N = tree_off[b + 1] - off;
+  const int P = prefix_len[b];  // (requested with the offsets: one round trip fewer)
   // a tree outside the caller's rows, or larger than the mask words or max_nodes (which
   // sizes the attention grid) is refused and nothing of it is written
   if (threadIdx.x == 0)
@@ -46,7 +47,6 @@ __global__ __launch_bounds__(128) void tree_build_kernel(const int32_t* tree_off
     for (int i = threadIdx.x; i < N * mw && bad == EAGLE_ERR_TREE; i += blockDim.x) anc[(int64_t)off * mw + i] = 0ull;
     return;
   }
-  const int P = prefix_len[b];
   for (int i = threadIdx.x; i < N; i += blockDim.x) {
     uint64_t words[2] = {0ull, 0ull};
     int d = 0;
@@ -84,31 +84,91 @@ __device__ void commit_path(const AcceptArgs& a, int b, int off, const int* s_pa
     a.accept_len[b] = L;
     a.next_token[b] = bonus;
   }
+  // 16-byte pieces: the K and V rows of the path and the leaf's feature.  Loads are
+  // issued in batches before their stores (a load-store pair per piece would cost one
+  // memory round trip each: the stores may alias later loads), and a thread's indices
+  // are formed once, without a division per piece (integer division is tens of VALU
+  // instructions, which at one workgroup per sequence cost as much as a round trip).
+  const int nthr = blockDim.x;
   const int row_bytes = a.hd * a.elem;
   const int chunks = row_bytes / 16;
-  const int per_node = a.hkv * chunks;
-  const int total = (L + 1) * per_node;
-  for (int i = tid; i < 2 * total; i += blockDim.x) {
-    const int which = i / total;  // 0: K, 1: V
-    const int r = i % total;
-    const int d = r / per_node;
-    const int h = (r % per_node) / chunks;
-    const int ch = r % chunks;
-    const char* src = (const char*)(which ? a.v_tree : a.k_tree) +
-                      ((int64_t)(off + s_path[d]) * a.hkv + h) * row_bytes + ch * 16;
-    bool ok;
-    const int64_t co = cache_offset(a.cv, b, h, P + d, ok);
-    if (!ok) {  // a bad page id: never written through
-      set_status(a.status, EAGLE_ERR_ARG);
-      continue;
-    }
-    char* dst = (char*)(which ? a.v_cache : a.k_cache) + co * a.elem + ch * 16;
-    *(uint4*)dst = *(const uint4*)src;
+  const int per_node = a.hkv * chunks;  // pieces of one node's K (or V) rows
+  const int nf = a.next_feature ? a.hidden / 4 : 0;
+  const f32x4* feat_src = (const f32x4*)(a.h_nodes + (int64_t)(off + leaf) * a.hidden);
+  f32x4* feat_dst = (f32x4*)(a.next_feature + (int64_t)b * a.hidden);
+  // the first four feature pieces of this thread are requested ahead of the K/V rows
+  constexpr int UF = 4;
+  f32x4 fv[UF];
+  if (nf > 0) {
+#pragma unroll
+    for (int u = 0; u < UF; ++u) fv[u] = feat_src[min(tid + u * nthr, nf - 1)];
   }
-  if (a.next_feature) {
-    for (int i = tid * 4; i < a.hidden; i += blockDim.x * 4)
-      *(float4*)(a.next_feature + (int64_t)b * a.hidden + i) =
-          *(const float4*)(a.h_nodes + (int64_t)(off + leaf) * a.hidden + i);
+  if (per_node <= nthr) {
+    // thread: piece j of a node's rows (head h, chunk ch) for the path depths d = g,
+    // g + G, ... (G groups of per_node threads), K and V together, DU depths per round
+    const int G = nthr / per_node;
+    const int g = tid / per_node, jn = tid - g * per_node;
+    const int h = jn / chunks, ch = jn - h * chunks;
+    const char* kt = (const char*)a.k_tree + (int64_t)h * row_bytes + ch * 16;
+    const char* vt = (const char*)a.v_tree + (int64_t)h * row_bytes + ch * 16;
+    const int64_t node_bytes = (int64_t)a.hkv * row_bytes;
+    constexpr int DU = 4;
+    if (g < G) {
+      for (int d0 = g; d0 <= L; d0 += DU * G) {
+        f32x4 kv[DU][2];
+        int64_t co[DU];
+        bool st[DU];
+#pragma unroll
+        for (int u = 0; u < DU; ++u) {
+          const int d = d0 + u * G;
+          const int dc = min(d, L);  // past the path: re-read its last node, store nothing
+          const int64_t src = (int64_t)(off + s_path[dc]) * node_bytes;
+          kv[u][0] = *(const f32x4*)(kt + src);
+          kv[u][1] = *(const f32x4*)(vt + src);
+          bool ok;
+          co[u] = cache_offset(a.cv, b, h, P + dc, ok);
+          st[u] = d <= L && ok;
+          if (d <= L && !ok) set_status(a.status, EAGLE_ERR_ARG);  // a bad page id: never written through
+        }
+#pragma unroll
+        for (int u = 0; u < DU; ++u)
+          if (st[u]) {
+            *(f32x4*)((char*)a.k_cache + co[u] * a.elem + ch * 16) = kv[u][0];
+            *(f32x4*)((char*)a.v_cache + co[u] * a.elem + ch * 16) = kv[u][1];
+          }
+      }
+    }
+  } else {
+    // wide rows (more pieces per node than threads): one piece per iteration
+    const int total = (L + 1) * per_node;
+    for (int i = tid; i < 2 * total; i += nthr) {
+      const int which = i / total;  // 0: K, 1: V
+      const int r = i - which * total;
+      const int d = r / per_node;
+      const int h = (r - d * per_node) / chunks;
+      const int ch = r % chunks;
+      const char* src = (const char*)(which ? a.v_tree : a.k_tree) +
+                        ((int64_t)(off + s_path[d]) * a.hkv + h) * row_bytes + ch * 16;
+      bool ok;
+      const int64_t co = cache_offset(a.cv, b, h, P + d, ok);
+      if (!ok) {  // a bad page id: never written through
+        set_status(a.status, EAGLE_ERR_ARG);
+        continue;
+      }
+      *(f32x4*)((char*)(which ? a.v_cache : a.k_cache) + co * a.elem + ch * 16) = *(const f32x4*)src;
+    }
+  }
+  if (nf > 0) {
+#pragma unroll
+    for (int u = 0; u < UF; ++u)
+      if (tid + u * nthr < nf) feat_dst[tid + u * nthr] = fv[u];
+    for (int f0 = tid + UF * nthr; f0 < nf; f0 += UF * nthr) {
+#pragma unroll
+      for (int u = 0; u < UF; ++u) fv[u] = feat_src[min(f0 + u * nthr, nf - 1)];
+#pragma unroll
+      for (int u = 0; u < UF; ++u)
+        if (f0 + u * nthr < nf) feat_dst[f0 + u * nthr] = fv[u];
+    }
   }
   if (tid == 0) a.prefix_len[b] = P + L + 1;
 }
@@ -431,7 +491,7 @@ int launch_tree_build(int batch, const int32_t* tree_off, const int32_t* parent,
 // has already chosen the path, committed layer 0 and advanced prefix_len, so workgroup
 // (b, l - 1) reads accept_len[b] and path[b] and copies layer l's tree K/V of the path into
 // that layer's cache slots P .. P + L with P = prefix_len[b] - L - 1.  A rejected sequence
-// (accept_len -1) is skipped.  Each thread issues up to four independent 16-byte loads
+// (accept_len -1) is skipped.  Each thread issues up to eight independent 16-byte loads
 // before its stores, so the copy is not one load latency per chunk.
 __global__ __launch_bounds__(256) void commit_layers_kernel(AcceptArgs a) {
   const int b = blockIdx.x, l = blockIdx.y + 1;
@@ -448,9 +508,9 @@ __global__ __launch_bounds__(256) void commit_layers_kernel(AcceptArgs a) {
   const char* vt = (const char*)a.v_tree + (size_t)l * a.tree_ls * a.elem;
   char* kc = (char*)a.k_cache + (size_t)l * a.cache_ls * a.elem;
   char* vc = (char*)a.v_cache + (size_t)l * a.cache_ls * a.elem;
-  constexpr int U = 4;
+  constexpr int U = 8;
   for (int i0 = threadIdx.x; i0 < total; i0 += U * blockDim.x) {
-    uint4 v[U];
+    f32x4 v[U];  // (16 raw bytes; a vector type keeps the array in registers)
     char* dst[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -463,7 +523,7 @@ __global__ __launch_bounds__(256) void commit_layers_kernel(AcceptArgs a) {
         const int h = (r % per_node) / chunks;
         const int ch = r % chunks;
         const int node = a.path[(int64_t)b * stride + d];
-        v[u] = *(const uint4*)((which ? vt : kt) + ((int64_t)(off + node) * a.hkv + h) * row_bytes + ch * 16);
+        v[u] = *(const f32x4*)((which ? vt : kt) + ((int64_t)(off + node) * a.hkv + h) * row_bytes + ch * 16);
         bool ok;
         const int64_t co = cache_offset(a.cv, b, h, P + d, ok);
         if (ok)
@@ -474,7 +534,7 @@ __global__ __launch_bounds__(256) void commit_layers_kernel(AcceptArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (dst[u]) *(uint4*)dst[u] = v[u];
+      if (dst[u]) *(f32x4*)dst[u] = v[u];
   }
 }
 
