@@ -102,6 +102,22 @@ def test_verify_mini_ragged_batch_dynamic_trees():
     _print(errs)
 
 
+def test_verify_mini_small_trees_four_wave_attention():
+    """Trees of at most 16 nodes: with 4 query heads per KV head a (sequence, KV head) pair
+    has at most 64 query rows, so the attention runs its four-wave workgroups; a ragged
+    batch with an empty prefix and prefixes over several key chunks."""
+    dims = mini_dims()
+    rng = np.random.default_rng(8)
+    parents = [T.random_tree(rng, 16), T.chain(7), [-1], T.star(12)]
+    wl = make_workload(2, seed=41, dims=dims, batch=4, prefix=[300, 1000, 0, 513], parents=parents)
+    assert max(len(p) for p in parents) * dims.n_q_heads // dims.n_kv_heads <= 64
+    _print("verify small trees", wl.tree_off)
+    g = GpuRun(wl).run().outputs()
+    ref = oracle_verify(wl)
+    errs = check_verify(g, ref, dims, label="small-trees")
+    _print(errs)
+
+
 def test_verify_mini_random_gains_and_embedding_input():
     dims = mini_dims()
     wl = make_workload(2, seed=11, dims=dims, batch=2, prefix=[129, 400], parents=[T.static_tree_60(),

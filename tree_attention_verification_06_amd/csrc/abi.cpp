@@ -23,17 +23,18 @@ struct eagle_timer {
 
 namespace eagle {
 
+// A stage whose event cannot be recorded is left out of the timer (its slot is reused).
 void timer_begin(eagle_timer* t, int stage, hipStream_t s) {
   if (!t || t->n >= t->cap || !((t->mask >> stage) & 1u)) return;
-  hipEventRecord(t->ev[2 * t->n], s);
+  if (hipEventRecord(t->ev[2 * t->n], s) != hipSuccess) return;
   t->stage[t->n] = stage;
   t->open = true;
 }
 void timer_end(eagle_timer* t, hipStream_t s) {
   if (!t || !t->open) return;
-  hipEventRecord(t->ev[2 * t->n + 1], s);
-  t->n++;
   t->open = false;
+  if (hipEventRecord(t->ev[2 * t->n + 1], s) != hipSuccess) return;
+  t->n++;
 }
 
 namespace {
@@ -820,7 +821,7 @@ eagle_timer* eagle_timer_create(int32_t capacity) {
 
 void eagle_timer_destroy(eagle_timer* t) {
   if (!t) return;
-  for (auto& e : t->ev) hipEventDestroy(e);
+  for (auto& e : t->ev) (void)hipEventDestroy(e);  // nothing to do on failure at teardown
   delete t;
 }
 
