@@ -591,22 +591,29 @@ AttnPlan plan_attn(int dtype, int batch, int hq, int hkv, int hd, int max_nodes,
     p.row_groups = 0;
     return p;
   }
-  // four-wave workgroups (two per CU) when a (b, kv head) pair has at most 64 query rows:
-  // the draft's levels (16 sequences x 40 rows per kv head) measured 12% faster, shapes
-  // with hundreds of rows 8-10% slower (each row group re-reads its chunk's keys)
-  p.nwa = p.rmax <= 64 ? 4 : 8;
   // prefix chunks: about 512 (b, kv head, chunk, row group) workgroups, with at least 256
   // keys and at most 32 chunks per (b, kv head)
-  p.row_groups = (p.rmax + p.nwa * 16 - 1) / (p.nwa * 16);
-  const int units = std::max(1, batch * hkv * p.row_groups);
-  int nch = std::max(1, (512 + units - 1) / units);
-  nch = std::min(nch, std::max(1, (max_prefix + 255) / 256));
-  nch = std::min(nch, 32);
-  int kch = (max_prefix + nch - 1) / nch;
-  kch = std::max(KT, (kch + KT - 1) / KT * KT);
-  nch = std::max(1, (max_prefix + kch - 1) / kch);
-  p.kch = kch;
-  p.n_chunks = nch + 1;  // + the tree chunk
+  auto chunks = [&](int nwa) {
+    p.nwa = nwa;
+    p.row_groups = (p.rmax + nwa * 16 - 1) / (nwa * 16);
+    const int units = std::max(1, batch * hkv * p.row_groups);
+    int nch = std::max(1, (512 + units - 1) / units);
+    nch = std::min(nch, std::max(1, (max_prefix + 255) / 256));
+    nch = std::min(nch, 32);
+    int kch = (max_prefix + nch - 1) / nch;
+    kch = std::max(KT, (kch + KT - 1) / KT * KT);
+    nch = std::max(1, (max_prefix + kch - 1) / kch);
+    p.kch = kch;
+    p.n_chunks = nch + 1;  // + the tree chunk
+    return units * p.n_chunks;
+  };
+  // Four-wave workgroups (64 query rows, two per CU) when a (b, kv head) pair has at most
+  // 64 query rows, or when eight-wave ones would not cover the CUs once: the draft's levels
+  // (16 sequences x 40 rows per kv head) measured 12% faster and one 60-node tree at
+  // prefix 2048 9% faster; where eight-wave workgroups fill the chip (hundreds of rows per
+  // pair, or many sequences) four-wave ones were 8-10% slower, since each row group
+  // re-reads its chunk's keys.
+  if (p.rmax <= 64 || chunks(8) < 256) chunks(4);
   (void)hd;
   return p;
 }
