@@ -1340,12 +1340,14 @@ struct CfgInfo {
 // Config 5 has no gate/up instance (it would spill registers).  7, 8: wide tiles (four
 // waves, 32x32x16 MFMAs, 256 weight rows x 192 / 160 tokens) for LM heads only, one K split.
 // 9: 16-token tiles for up to 16 rows (decode steps, small draft levels): a quarter of the
-// X staging and of the split-K partials of the 64-token tile.
-constexpr int kNumCfgs = 10;
+// X staging and of the split-K partials of the 64-token tile.  10: 32-token tiles, taken
+// from the measured table only (two token tiles per weight tile for 33..64 rows: twice the
+// workgroups, the second read of each weight tile served by the XCD's L2).
+constexpr int kNumCfgs = 11;
 constexpr CfgInfo kCfgs[kNumCfgs] = {{8, 4, 4, 64, 512, 1},   {8, 2, 4, 64, 512, 1},   {8, 1, 8, 64, 512, 1},
                                      {8, 2, 4, 128, 256, 1},  {8, 1, 4, 256, 128, 1},  {8, 2, 4, 192, 128, 2},
                                      {8, 2, 4, 160, 128, 2},  {4, 4, 4, 192, 128, 2},  {4, 4, 4, 160, 128, 2},
-                                     {8, 1, 8, 16, 512, 1}};
+                                     {8, 1, 8, 16, 512, 1},   {8, 1, 8, 32, 512, 1}};
 constexpr bool cfg_wide(int c) { return c == 7 || c == 8; }
 
 template <int NW, int RB, int PD, bool DUAL, int MT, int KC, int XB, int EH = 1>
@@ -1396,8 +1398,10 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
   // (the 16-token tile is tried first, so it wins the ties: with one K split its cost is
   // the 64-token tile's, while it stages a quarter of the activations; measured 7% faster
   // for the 8B gate/up at 1..16 rows)
+  static constexpr int kOrder[kNumCfgs] = {9, 0, 1, 2, 3, 4, 5, 6, 7, 8, 10};
   for (int ci = 0; ci < kNumCfgs; ++ci) {
-    const int c = (ci + kNumCfgs - 1) % kNumCfgs;  // 9, 0, 1, ..., 8
+    const int c = kOrder[ci];
+    if (c == 10) continue;  // (measured picks only)
     const CfgInfo& cf = kCfgs[c];
     const bool wide = cfg_wide(c);
     if (wide && (m < 192 || epi_kind == EPI_TOPK)) continue;  // never faster below a few hundred rows
@@ -1436,9 +1440,12 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
   // Shapes where the model's pick was measured well behind the best (tile configuration,
   // K split) of a sweep over all of them (the 8B- and 70B-shaped projections, rows 16..960),
   // confirmed by alternating runs of both picks: the measured best is taken for row counts
-  // within 25% of the swept one.  All in the 160..256-row range of the draft's levels: QKV
+  // within 25% of the swept one.  In the 160..256-row range of the draft's levels: QKV
   // 19-23%, O 6-20% and down 15% faster than the model's 128-row tiles with few K splits;
-  // gate/up (128-token tiles instead of 160) and the draft's feature FC 3-4%.
+  // gate/up (128-token tiles instead of 160) and the draft's feature FC 3-4%.  At 60 rows
+  // (one verified tree) the 8B QKV, O and down on 32-token tiles: 8%, 16% and 7% faster
+  // (50-60 rows; at 75 rows, three token tiles, O and down were slower, so these picks
+  // stop at two token tiles; the 70B shapes gained nothing).
   struct TunedPick {
     int n, k, dual, epi, m, cfg, splits;
   };
@@ -1446,11 +1453,14 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
       {6144, 4096, 0, EPI_QKV, 160, 1, 3},    {6144, 4096, 0, EPI_QKV, 256, 1, 2},
       {4096, 4096, 0, EPI_RESID, 256, 2, 2},  {4096, 14336, 0, EPI_RESID, 160, 1, 5},
       {10240, 8192, 0, EPI_QKV, 160, 1, 2},   {8192, 8192, 0, EPI_RESID, 160, 3, 4},
-      {14336, 4096, 1, EPI_SILU, 160, 3, 1},  {4096, 8192, 0, EPI_RESID, 160, 1, 4}};
+      {14336, 4096, 1, EPI_SILU, 160, 3, 1},  {4096, 8192, 0, EPI_RESID, 160, 1, 4},
+      {6144, 4096, 0, EPI_QKV, 60, 10, 2},    {4096, 4096, 0, EPI_RESID, 60, 10, 4},
+      {4096, 14336, 0, EPI_RESID, 60, 10, 4}};
   {
     double bestd = 0.2232;  // |ln(m / swept m)| <= ln 1.25
     for (const TunedPick& t : kTuned) {
       if (t.n != n || t.k != k || t.dual != dual || t.epi != epi_kind) continue;
+      if (kCfgs[t.cfg].mt < 64 && m > 2 * kCfgs[t.cfg].mt) continue;  // at most two narrow token tiles
       const double dd = std::fabs(std::log((double)m / t.m));
       if (dd <= bestd) {
         bestd = dd;
@@ -1544,6 +1554,7 @@ int launch_gemm(GemmDesc& d, const GemmPlan& p, hipStream_t s) {
           dual ? launch_cfg<4, 4, 4, true, 160, 128, 2, 2>(d, grid, s) : launch_cfg<4, 4, 4, false, 160, 128, 2, 2>(d, grid, s);
         break;
       case 9: dual ? launch_cfg<8, 1, 8, true, 16, 512, 2>(d, grid, s) : launch_cfg<8, 1, 8, false, 16, 512, 2>(d, grid, s); break;
+      case 10: dual ? launch_cfg<8, 1, 8, true, 32, 512, 2>(d, grid, s) : launch_cfg<8, 1, 8, false, 32, 512, 2>(d, grid, s); break;
       default: return EAGLE_ERR_UNSUPPORTED;
     }
   }
