@@ -118,6 +118,20 @@ def test_verify_mini_small_trees_four_wave_attention():
     _print(errs)
 
 
+def test_verify_few_rows_wider_layer_split_k_narrow_tiles():
+    """Twelve rows through a layer of hidden 2048 (16 query heads, FFN 2816): every GEMM runs
+    the 16-token tiles, and the down projection (K 2816 over 16 weight tiles) is split over
+    K, so the narrow tiles' split-K hand-off and partial sums are compared with the oracle."""
+    dims = mini_dims(hidden=2048, n_q_heads=16, n_kv_heads=4, ffn=2816)
+    parents = [T.chain(5), T.star(6), [-1]]
+    wl = make_workload(2, seed=44, dims=dims, batch=3, prefix=[300, 64, 0], parents=parents)
+    _print("verify few rows, hidden 2048", wl.tree_off)
+    g = GpuRun(wl).run().outputs()
+    ref = oracle_verify(wl)
+    errs = check_verify(g, ref, dims, label="few-rows-2048")
+    _print(errs)
+
+
 def test_verify_mini_random_gains_and_embedding_input():
     dims = mini_dims()
     wl = make_workload(2, seed=11, dims=dims, batch=2, prefix=[129, 400], parents=[T.static_tree_60(),
