@@ -781,7 +781,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(GemmDesc d, int grid
     }
     wstep = 32;
   }
-  auto wload = [&](int rb, int k) { return *(const bf16x8_t*)(wp[rb] + (int64_t)(k >> 5) * wstep); };
+  // Weight loads carry the non-temporal hint: each weight line is used by this launch only
+  // (and by the few token tiles of its weight tile, which run together on one XCD), so the
+  // stream should not displace what the caches hold for the activations and partials.
+  // Measured: the 60-row LM head 186 -> 165 us (1.05 GB at 6.4 TB/s), the 70B layer at 60
+  // rows 10% faster, the draft expansion 6%; neutral at 960 rows.
+  auto wload = [&](int rb, int k) {
+    return __builtin_nontemporal_load((const bf16x8_t*)(wp[rb] + (int64_t)(k >> 5) * wstep));
+  };
 
   // X rows staged by this lane: r = (wid + j * NW) * RPP + lane / LPR, 8 columns at
   // (lane % LPR) * 8 of each chunk
