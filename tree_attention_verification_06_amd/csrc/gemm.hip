@@ -1447,27 +1447,31 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
   // Shapes where the model's pick was measured well behind the best (tile configuration,
   // K split) of a sweep over all of them (the 8B- and 70B-shaped projections, rows 16..960),
   // confirmed by alternating runs of both picks: the measured best is taken for row counts
-  // within 25% of the swept one.  In the 160..256-row range of the draft's levels: QKV
-  // 19-23%, O 6-20% and down 15% faster than the model's 128-row tiles with few K splits;
-  // gate/up (128-token tiles instead of 160) and the draft's feature FC 3-4%.  At 60 rows
-  // (one verified tree) the 8B QKV, O and down on 32-token tiles: 8%, 16% and 7% faster
-  // (50-60 rows; at 75 rows, three token tiles, O and down were slower, so these picks
-  // stop at two token tiles; the 70B shapes gained nothing).
+  // within 25% of the swept one.  In the 160..256-row range of the draft's levels: QKV at
+  // 256 rows, O at 256 and down at 160 rows 6-20% faster than the model's 128-row tiles with
+  // few K splits, the draft's feature FC 3-4%; the 8B QKV at 160 rows on 32-token tiles
+  // (five token tiles per weight tile, one K split) 19% faster than the 64-token tiles the
+  // table gave it before the weight stream took the non-temporal hint.  At 60 rows (one
+  // verified tree) the 8B QKV, O and down on 32-token tiles: 8%, 16% and 7% faster (50-60
+  // rows; at 75 rows, three token tiles, O and down were slower, so those picks stop at two
+  // token tiles; the 70B shapes gained nothing).  The 8B gate/up at 160 rows now takes the
+  // model's pick (3% faster than the 128-token tiles measured best without the hint).
   struct TunedPick {
     int n, k, dual, epi, m, cfg, splits;
   };
   static constexpr TunedPick kTuned[] = {
-      {6144, 4096, 0, EPI_QKV, 160, 1, 3},    {6144, 4096, 0, EPI_QKV, 256, 1, 2},
+      {6144, 4096, 0, EPI_QKV, 160, 10, 1},   {6144, 4096, 0, EPI_QKV, 256, 1, 2},
       {4096, 4096, 0, EPI_RESID, 256, 2, 2},  {4096, 14336, 0, EPI_RESID, 160, 1, 5},
       {10240, 8192, 0, EPI_QKV, 160, 1, 2},   {8192, 8192, 0, EPI_RESID, 160, 3, 4},
-      {14336, 4096, 1, EPI_SILU, 160, 3, 1},  {4096, 8192, 0, EPI_RESID, 160, 1, 4},
+      {4096, 8192, 0, EPI_RESID, 160, 1, 4},
       {6144, 4096, 0, EPI_QKV, 60, 10, 2},    {4096, 4096, 0, EPI_RESID, 60, 10, 4},
       {4096, 14336, 0, EPI_RESID, 60, 10, 4}};
   {
     double bestd = 0.2232;  // |ln(m / swept m)| <= ln 1.25
     for (const TunedPick& t : kTuned) {
       if (t.n != n || t.k != k || t.dual != dual || t.epi != epi_kind) continue;
-      if (kCfgs[t.cfg].mt < 64 && m > 2 * kCfgs[t.cfg].mt) continue;  // at most two narrow token tiles
+      // a narrow-tile pick measured with at most two token tiles does not extend to more
+      if (kCfgs[t.cfg].mt < 64 && t.m <= 2 * kCfgs[t.cfg].mt && m > 2 * kCfgs[t.cfg].mt) continue;
       const double dd = std::fabs(std::log((double)m / t.m));
       if (dd <= bestd) {
         bestd = dd;
