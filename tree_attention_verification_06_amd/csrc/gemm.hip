@@ -1455,7 +1455,9 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
   // verified tree) the 8B QKV, O and down on 32-token tiles: 8%, 16% and 7% faster (50-60
   // rows; at 75 rows, three token tiles, O and down were slower, so those picks stop at two
   // token tiles; the 70B shapes gained nothing).  The 8B gate/up at 160 rows now takes the
-  // model's pick (3% faster than the 128-token tiles measured best without the hint).
+  // model's pick (3% faster than the 128-token tiles measured best without the hint).  For
+  // hundreds of rows: the 8B O at 362 and 960 rows on 256-row x 64-token tiles (9% and 5%
+  // faster) and the QKV at 960 rows on 512-row tiles (2%).
   struct TunedPick {
     int n, k, dual, epi, m, cfg, splits;
   };
@@ -1465,7 +1467,9 @@ GemmPlan plan_gemm(int dtype, int n, int k, int m, int dual, int epi_kind, int h
       {10240, 8192, 0, EPI_QKV, 160, 1, 2},   {8192, 8192, 0, EPI_RESID, 160, 3, 4},
       {4096, 8192, 0, EPI_RESID, 160, 1, 4},
       {6144, 4096, 0, EPI_QKV, 60, 10, 2},    {4096, 4096, 0, EPI_RESID, 60, 10, 4},
-      {4096, 14336, 0, EPI_RESID, 60, 10, 4}};
+      {4096, 14336, 0, EPI_RESID, 60, 10, 4},
+      {4096, 4096, 0, EPI_RESID, 362, 1, 2},  {4096, 4096, 0, EPI_RESID, 960, 1, 1},
+      {6144, 4096, 0, EPI_QKV, 960, 0, 1}};
   {
     double bestd = 0.2232;  // |ln(m / swept m)| <= ln 1.25
     for (const TunedPick& t : kTuned) {
