@@ -29,7 +29,7 @@ def tol(dims):
     return TOL_BF16 if dims.dtype == "bf16" else TOL_F32
 
 
-class GpuRun:
+class HipPathRun:
     """One verification of a workload on the GPU, with debug outputs."""
 
     def __init__(self, wl, *, use_embed=False, want_logits=True, max_prefix=None, layout=0):

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests._gpu import GpuRun, check_verify, oracle_verify
+from tests._gpu import HipPathRun, check_verify, oracle_verify
 from workloads import make_workload, trees as T
 
 pytestmark = pytest.mark.gpu
@@ -25,7 +25,7 @@ def _run_full(cfg, prefix=None, **kw):
     t0 = time.time()
     wl = make_workload(cfg, prefix=prefix, **kw)
     _log(f"cfg {wl.name}: {wl.n_nodes} nodes, generated in {time.time() - t0:.1f}s")
-    g = GpuRun(wl).run(accept=True)
+    g = HipPathRun(wl).run(accept=True)
     out = g.outputs()
     _log(f"  gpu done {time.time() - t0:.1f}s")
     ref = oracle_verify(wl)
@@ -46,7 +46,7 @@ def test_full_llama8b_layer_60_nodes_prefix_2048():
     """Row-major weights against the oracle, then fragment-blocked weights (the layout the
     benchmark runs): the same arithmetic in the same order, so every output is bit-identical."""
     wl, g, out, ref = _run_full(2)
-    p = GpuRun(wl, layout=1).run(accept=True).outputs()
+    p = HipPathRun(wl, layout=1).run(accept=True).outputs()
     check_verify(p, ref, wl.dims, label=wl.name + " packed")
     for k in ("k_tree", "v_tree", "h", "attn", "logits", "maxlogit", "argmax"):
         assert np.array_equal(out[k], p[k]), k
@@ -73,7 +73,7 @@ def test_full_ragged_dynamic_batch_prefix_4096():
 def test_repeated_verification_is_bitwise_identical():
     """Split-K fixups and the split-KV merge reduce in a fixed order, so two runs agree bit for bit."""
     wl = make_workload(2)
-    g = GpuRun(wl)
+    g = HipPathRun(wl)
     a = g.run().outputs()
     b = g.run().outputs()
     for k in ("k_tree", "v_tree", "h", "attn", "logits", "maxlogit", "argmax"):

@@ -4,7 +4,7 @@ the weights in either layout (the GEMM visits K in the same order for both)."""
 import numpy as np
 import pytest
 
-from tests._gpu import GpuRun, gpu_draft_outputs
+from tests._gpu import HipPathRun, gpu_draft_outputs
 from workloads import DraftParams, make_workload
 from workloads.configs import mini_dims
 from workloads.device import upload
@@ -43,8 +43,8 @@ def test_pack_fragments_matches_definition(rows, cols):
 
 
 def _verify_pair(wl, **kw):
-    a = GpuRun(wl, **kw).run(accept=True).outputs()
-    b = GpuRun(wl, layout=1, **kw).run(accept=True).outputs()
+    a = HipPathRun(wl, **kw).run(accept=True).outputs()
+    b = HipPathRun(wl, layout=1, **kw).run(accept=True).outputs()
     return a, b
 
 
@@ -66,7 +66,7 @@ def test_verify_packed_weights_bit_identical_8b_no_logits():
     for k in ("k_tree", "v_tree", "h", "attn", "maxlogit", "argmax"):
         assert np.array_equal(a[k], b[k]), k
     # and the same as a run that writes the logits (the argmax scan's other path)
-    c = GpuRun(wl, want_logits=True).run(accept=True).outputs()
+    c = HipPathRun(wl, want_logits=True).run(accept=True).outputs()
     for k in ("maxlogit", "argmax"):
         assert np.array_equal(a[k], c[k]), k
     assert np.array_equal(c["maxlogit"], c["logits"].max(axis=1))
@@ -80,8 +80,8 @@ def test_register_argmax_equals_tile_argmax_wide_lm_head(batch):
     of the logits it wrote."""
     wl = make_workload(3, batch=batch, prefix=[4096, 1500, 300, 2048, 64, 777][:batch])
     _log(f"{wl.name} batch {batch}: {wl.n_nodes} nodes")
-    a = GpuRun(wl, layout=1, want_logits=False).run(accept=True).outputs()
-    c = GpuRun(wl, layout=1, want_logits=True).run(accept=True).outputs()
+    a = HipPathRun(wl, layout=1, want_logits=False).run(accept=True).outputs()
+    c = HipPathRun(wl, layout=1, want_logits=True).run(accept=True).outputs()
     for k in ("maxlogit", "argmax"):
         assert np.array_equal(a[k], c[k]), k
     assert np.array_equal(c["maxlogit"], c["logits"].max(axis=1))

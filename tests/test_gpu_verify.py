@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests._gpu import GpuRun, check_verify, oracle_verify
+from tests._gpu import HipPathRun, check_verify, oracle_verify
 from workloads import make_workload, mini_dims, trees as T
 
 pytestmark = pytest.mark.gpu
@@ -73,7 +73,7 @@ def test_tree_build_rejects_malformed_tree():
 def test_verify_tiny_fp32_full_config():
     wl = make_workload(1)
     _print("verify cfg tiny fp32", wl.n_nodes)
-    g = GpuRun(wl).run().outputs()
+    g = HipPathRun(wl).run().outputs()
     ref = oracle_verify(wl)
     errs = check_verify(g, ref, wl.dims, label="tiny-fp32")
     _print(errs)
@@ -86,7 +86,7 @@ def test_verify_mini_bf16(seed, prefix, tree):
     par = {"static60": T.static_tree_60(), "random": T.random_tree(rng, 90), "chain": T.chain(64)}[tree]
     wl = make_workload(2, seed=seed, dims=dims, batch=1, prefix=prefix, parents=[par])
     _print("verify mini bf16", seed, prefix, tree, wl.n_nodes)
-    g = GpuRun(wl).run().outputs()
+    g = HipPathRun(wl).run().outputs()
     ref = oracle_verify(wl)
     errs = check_verify(g, ref, dims, label=f"mini-{tree}")
     _print(errs)
@@ -96,7 +96,7 @@ def test_verify_mini_ragged_batch_dynamic_trees():
     dims = mini_dims()
     wl = make_workload(3, seed=5, dims=dims, prefix=[1000, 37, 513, 2048])
     _print("verify ragged", wl.tree_off, wl.mask_words)
-    g = GpuRun(wl).run().outputs()
+    g = HipPathRun(wl).run().outputs()
     ref = oracle_verify(wl)
     errs = check_verify(g, ref, dims, label="ragged")
     _print(errs)
@@ -112,7 +112,7 @@ def test_verify_mini_small_trees_four_wave_attention():
     wl = make_workload(2, seed=41, dims=dims, batch=4, prefix=[300, 1000, 0, 513], parents=parents)
     assert max(len(p) for p in parents) * dims.n_q_heads // dims.n_kv_heads <= 64
     _print("verify small trees", wl.tree_off)
-    g = GpuRun(wl).run().outputs()
+    g = HipPathRun(wl).run().outputs()
     ref = oracle_verify(wl)
     errs = check_verify(g, ref, dims, label="small-trees")
     _print(errs)
@@ -126,7 +126,7 @@ def test_verify_few_rows_wider_layer_split_k_narrow_tiles():
     parents = [T.chain(5), T.star(6), [-1]]
     wl = make_workload(2, seed=44, dims=dims, batch=3, prefix=[300, 64, 0], parents=parents)
     _print("verify few rows, hidden 2048", wl.tree_off)
-    g = GpuRun(wl).run().outputs()
+    g = HipPathRun(wl).run().outputs()
     ref = oracle_verify(wl)
     errs = check_verify(g, ref, dims, label="few-rows-2048")
     _print(errs)
@@ -140,7 +140,7 @@ def test_verify_mini_random_gains_and_embedding_input():
     from workloads.bf16 import f32_to_bf16_bits
     wl.weights["embed"] = f32_to_bf16_bits(wl.weights["embed"])
     _print("verify embed-input", wl.tree_off)
-    g = GpuRun(wl, use_embed=True).run().outputs()
+    g = HipPathRun(wl, use_embed=True).run().outputs()
     ref = oracle_verify(wl, use_embed=True)
     errs = check_verify(g, ref, dims, label="embed")
     _print(errs)
@@ -153,7 +153,7 @@ def test_accept_commit_bit_exact(cfg):
     dims = None if cfg == 1 else mini_dims()
     wl = make_workload(cfg, seed=21, dims=dims, prefix=None if cfg == 1 else [300, 77, 1024, 5])
     # plant paths: set tokens along one root path per tree to the GPU's argmax of the parent
-    run0 = GpuRun(wl, want_logits=False).run()
+    run0 = HipPathRun(wl, want_logits=False).run()
     g0 = run0.outputs()
     rng = np.random.default_rng(9)
     tokens = wl.tokens.copy()
@@ -169,7 +169,7 @@ def test_accept_commit_bit_exact(cfg):
         for node in path[::-1][1:]:
             tokens[o + node] = g0["argmax"][o + par[node]]
     wl.tokens = tokens
-    run = GpuRun(wl, want_logits=False)
+    run = HipPathRun(wl, want_logits=False)
     pre_k = run.t["k_cache"].clone()
     pre_v = run.t["v_cache"].clone()
     run.run(accept=True)
@@ -216,7 +216,7 @@ def test_verify_and_accept_degenerate_trees():
     wl = make_workload(2, seed=31, dims=dims, batch=4, prefix=[0, 17, 0, 1000], parents=parents)
     assert wl.mask_words == 2
     _print("verify degenerate", wl.tree_off)
-    run0 = GpuRun(wl)
+    run0 = HipPathRun(wl)
     g0 = run0.run().outputs()
     ref = oracle_verify(wl)
     _print(check_verify(g0, ref, dims, label="degenerate"))
@@ -226,7 +226,7 @@ def test_verify_and_accept_degenerate_trees():
     for i in range(1, 128):
         tokens[o + i] = g0["argmax"][o + i - 1]
     wl.tokens = tokens
-    run = GpuRun(wl, want_logits=False)
+    run = HipPathRun(wl, want_logits=False)
     run.run(accept=True)
     g = run.outputs()
     v = run.v
@@ -253,7 +253,7 @@ def test_accept_reports_cache_overflow():
     cap = wl.cache_cap
     # sequence 1 starts 3 slots short of the end: committing its 6-node path cannot fit
     wl.prefix_len = np.array([10, cap - 3], dtype=np.int32)
-    run0 = GpuRun(wl, want_logits=False, max_prefix=cap)
+    run0 = HipPathRun(wl, want_logits=False, max_prefix=cap)
     g0 = run0.run().outputs()
     tokens = wl.tokens.copy()
     for b in range(2):
@@ -261,7 +261,7 @@ def test_accept_reports_cache_overflow():
         for i in range(1, 6):
             tokens[o + i] = g0["argmax"][o + i - 1]
     wl.tokens = tokens
-    run = GpuRun(wl, want_logits=False, max_prefix=cap)
+    run = HipPathRun(wl, want_logits=False, max_prefix=cap)
     pre_k = run.t["k_cache"].clone()
     t, v = run.t, run.v
     v.encode(t["tree_off"], t["parent"], t["prefix_len"], run.M)
@@ -289,7 +289,7 @@ def test_accept_refuses_malformed_or_stale_trees():
     dims = mini_dims()
     parents = [T.chain(6), T.chain(6)]
     wl = make_workload(2, seed=35, dims=dims, batch=2, prefix=[40, 40], parents=parents)
-    run0 = GpuRun(wl, want_logits=False)
+    run0 = HipPathRun(wl, want_logits=False)
     g0 = run0.run().outputs()
     tokens = wl.tokens.copy()
     for b in range(2):          # plant both chains in full: a trusted tree accepts depth 5
@@ -298,7 +298,7 @@ def test_accept_refuses_malformed_or_stale_trees():
             tokens[o + i] = g0["argmax"][o + i - 1]
     for case in ("malformed", "stale"):
         wl.tokens = tokens
-        run = GpuRun(wl, want_logits=False)
+        run = HipPathRun(wl, want_logits=False)
         t, v = run.t, run.v
         v.encode(t["tree_off"], t["parent"], t["prefix_len"], run.M)
         v.verify(t["tree_off"], t["tokens"], t["prefix_len"], run.M, x=t["x"])
@@ -339,7 +339,7 @@ def test_verify_prefix_longer_than_planned(cfg):
     parents = None if cfg == 1 else [T.static_tree_60(), T.random_tree(np.random.default_rng(8), 30)]
     wl = make_workload(cfg, seed=37, dims=dims, batch=len(prefix), prefix=prefix, parents=parents)
     _print("verify prefix beyond plan", cfg, prefix)
-    g = GpuRun(wl, max_prefix=128).run().outputs()
+    g = HipPathRun(wl, max_prefix=128).run().outputs()
     ref = oracle_verify(wl)
     assert g["status"] == 0
     _print(check_verify(g, ref, wl.dims, label=f"prefix-beyond-plan-{cfg}"))
@@ -375,7 +375,7 @@ def test_verify_fp32_ragged_batch_several_key_blocks():
     wl = make_workload(1, seed=47, dims=TINY, batch=3, prefix=[100, 250, 300], parents=parents)
     assert wl.mask_words == 2
     _print("verify fp32 ragged", wl.tree_off.tolist(), wl.prefix_len.tolist())
-    g = GpuRun(wl).run().outputs()
+    g = HipPathRun(wl).run().outputs()
     ref = oracle_verify(wl)
     _print(check_verify(g, ref, wl.dims, label="fp32-ragged"))
     tokens = wl.tokens.copy()
@@ -383,7 +383,7 @@ def test_verify_fp32_ragged_batch_several_key_blocks():
     for i in range(1, 9):
         tokens[o + i] = g["argmax"][o + i - 1]
     wl.tokens = tokens
-    run = GpuRun(wl, want_logits=False)
+    run = HipPathRun(wl, want_logits=False)
     run.run(accept=True)
     g2 = run.outputs()
     acc = run.v.accept_len.cpu().numpy()

@@ -6,7 +6,7 @@ also within the bf16 tolerance of the oracle."""
 import numpy as np
 import pytest
 
-from tests._gpu import GpuRun, check_verify, oracle_verify
+from tests._gpu import HipPathRun, check_verify, oracle_verify
 from workloads import make_workload, mini_dims, trees as T
 
 pytestmark = pytest.mark.gpu
@@ -48,7 +48,7 @@ def test_noalloc_verify_equals_workspace_verify_on_two_calls(layout):
         np.random.default_rng(5), 17)])
     for wl in (big, small):
         print("noalloc verify", layout, wl.tree_off.tolist(), wl.prefix_len.tolist(), flush=True)
-        run = GpuRun(wl, layout=layout).run()
+        run = HipPathRun(wl, layout=layout).run()
         ref_gpu = run.outputs()
         got = _noalloc_outputs(run)
         for k in ("k_tree", "v_tree"):
